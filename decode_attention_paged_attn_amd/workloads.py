@@ -1,0 +1,290 @@
+"""Seeded synthetic decode-attention workloads over a paged KV cache.
+
+This module only draws inputs: context lengths, a shuffled physical block pool
+dealt out as block tables, and N(0, 1) fp16 queries, keys and values.  It holds
+none of the attention arithmetic, so both the HIP path and the float64 checker
+can be fed from it.
+
+Shapes follow the pages' workloads:
+
+* Llama-3.1-8B attention: 32 query heads, 8 KV heads, head dim 128, fp16 KV
+  (KernelFlume paper §6.1 "Implementation and Setup"; the batch-64, ~4K-token
+  capacity example in §1 "Introduction").
+* 16-token blocks (16 tokens per block by default in "Optimising decode in
+  vLLM", section 1; B_size = 16 in "Physical Memory Block Layout" of the
+  disaggregated-inference page).
+* Agentic long-context sessions with a median of roughly 80K tokens and tails
+  above 200K (KernelFlume paper §1 and §2.1).  The trace itself is not used;
+  a clipped log-normal with that median stands in for it.
+
+Draw order for a seed: context lengths, then the pool permutation, then Q,
+then the K pool, then the V pool.  Small cases draw everything with numpy's
+PCG64; large pools draw Q/K/V with a torch generator on the target device
+(the lengths and tables still come from PCG64), so multi-GiB pools never pass
+through host memory.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+K_POISON = 6.0e4        # would dominate any softmax it leaked into
+V_POISON = float("nan")  # would turn any output it leaked into into NaN
+
+
+@dataclasses.dataclass
+class Case:
+    """One decode-attention batch: device tensors plus the host-side recipe."""
+    name: str
+    q: torch.Tensor              # [B, Hq, D] fp16
+    k_cache: torch.Tensor        # [num_blocks, bs, Hkv, D] fp16
+    v_cache: torch.Tensor        # [num_blocks, bs, Hkv, D] fp16
+    block_table: torch.Tensor    # [B, width] int32, -1 past each sequence's blocks
+    context_lens: torch.Tensor   # [B] int32
+    scale: float                 # fp32-representable 1/sqrt(D)
+    lens: np.ndarray             # host copy of context_lens (int64)
+    block_table_host: np.ndarray  # host copy of block_table (int64)
+    seed: int
+    rng_backend: str
+    partition_tokens: int = 0    # 0 = let the library choose
+    ranges: int = 0              # token ranges for the partial + merge workload
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def Hq(self):
+        return self.q.shape[1]
+
+    @property
+    def Hkv(self):
+        return self.k_cache.shape[2]
+
+    @property
+    def D(self):
+        return self.q.shape[2]
+
+    @property
+    def num_blocks(self):
+        return self.k_cache.shape[0]
+
+
+def fp32_scale(head_dim: int) -> float:
+    """1/sqrt(D) rounded to fp32, the value passed to the kernels."""
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+def _deal_blocks(lens, pool_blocks, width, perm, bs):
+    nblk = [-(-int(n) // bs) for n in lens]
+    if sum(nblk) > pool_blocks:
+        raise ValueError("pool too small for the requested lengths")
+    table = np.full((len(lens), width), -1, dtype=np.int64)
+    off = 0
+    for b, k in enumerate(nblk):
+        table[b, :k] = perm[off:off + k]
+        off += k
+    return table, off
+
+
+def build_case(lens, Hq, Hkv, *, D=HEAD_DIM, bs=BLOCK_SIZE, pool_blocks=None,
+               width=None, seed=0, device="cpu", poison=True,
+               rng_backend="numpy", name="custom", rng=None,
+               partition_tokens=0, ranges=0) -> Case:
+    """Draw Q, a shuffled K/V pool and block tables for the given lengths.
+
+    ``pool_blocks`` defaults to exactly the blocks the lengths need; extra pool
+    blocks are unused and, like the slots past each sequence's last token,
+    filled with K = +-6e4 and V = NaN when ``poison`` is set.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    B = len(lens)
+    nblk = -(-lens // bs)
+    need = int(nblk.sum())
+    pool_blocks = need if pool_blocks is None else int(pool_blocks)
+    pool_blocks = max(pool_blocks, 1)
+    width = max(int(nblk.max()) if B else 1, 1) if width is None else int(width)
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    perm = rng.permutation(pool_blocks)
+    table, used = _deal_blocks(lens, pool_blocks, width, perm, bs)
+
+    if rng_backend == "numpy":
+        q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(np.float16)
+        k = rng.standard_normal((pool_blocks, bs, Hkv, D), dtype=np.float32).astype(np.float16)
+        v = rng.standard_normal((pool_blocks, bs, Hkv, D), dtype=np.float32).astype(np.float16)
+        q_t = torch.from_numpy(q).to(device)
+        k_t = torch.from_numpy(k).to(device)
+        v_t = torch.from_numpy(v).to(device)
+    elif rng_backend == "torch":
+        gen = torch.Generator(device=device)
+        gen.manual_seed(int(seed))
+        q_t = torch.randn((B, Hq, D), generator=gen, device=device,
+                          dtype=torch.float32).to(torch.float16)
+        k_t = torch.empty((pool_blocks, bs, Hkv, D), dtype=torch.float16, device=device)
+        v_t = torch.empty_like(k_t)
+        chunk = max(1, (1 << 26) // (bs * Hkv * D))
+        for dst in (k_t, v_t):
+            for lo in range(0, pool_blocks, chunk):
+                hi = min(lo + chunk, pool_blocks)
+                dst[lo:hi] = torch.randn((hi - lo, bs, Hkv, D), generator=gen,
+                                         device=device, dtype=torch.float32)
+    else:
+        raise ValueError(rng_backend)
+
+    if poison:
+        _poison(k_t, v_t, lens, table, perm[used:], bs, rng)
+
+    return Case(name=name, q=q_t, k_cache=k_t, v_cache=v_t,
+                block_table=torch.from_numpy(table.astype(np.int32)).to(device),
+                context_lens=torch.from_numpy(lens.astype(np.int32)).to(device),
+                scale=fp32_scale(D), lens=lens, block_table_host=table, seed=seed,
+                rng_backend=rng_backend, partition_tokens=partition_tokens,
+                ranges=ranges)
+
+
+def _poison(k_t, v_t, lens, table, unused_blocks, bs, rng):
+    """Fill every slot no sequence owns: unused blocks and last-block tails."""
+    Hkv, D = k_t.shape[2], k_t.shape[3]
+    dev = k_t.device
+    if len(unused_blocks):
+        idx = torch.from_numpy(np.asarray(unused_blocks, dtype=np.int64)).to(dev)
+        sign = torch.from_numpy(rng.choice([-1.0, 1.0], size=(len(unused_blocks), bs, Hkv, D))
+                                .astype(np.float16)).to(dev)
+        k_t[idx] = sign * K_POISON
+        v_t[idx] = V_POISON
+    blk, slot = [], []
+    for b, n in enumerate(lens):
+        n = int(n)
+        if n % bs:
+            last = int(table[b, (n - 1) // bs])
+            for s in range(n % bs, bs):
+                blk.append(last)
+                slot.append(s)
+    if blk:
+        bi = torch.tensor(blk, dtype=torch.int64, device=dev)
+        si = torch.tensor(slot, dtype=torch.int64, device=dev)
+        k_t[bi, si] = K_POISON
+        v_t[bi, si] = V_POISON
+
+
+# --- the pages' workloads -----------------------------------------------------
+
+K1 = 1024   # "K" token counts are binary: 8K = 8192, 128K = 131072
+
+
+def tiny(seed=0, device="cpu", poison=True):
+    """Batch 2, 8 query / 2 KV heads, context {37, 512}, 35 of a 128-block pool."""
+    return build_case([37, 512], 8, 2, pool_blocks=128, seed=seed, device=device,
+                      poison=poison, rng_backend="numpy", name="tiny_b2_ctx37_512")
+
+
+def llama8b_4k(seed=0, device="cpu", rng_backend="torch"):
+    """Llama-3.1-8B layer: batch 64, 32/8 heads, every context 4096 tokens."""
+    return build_case([4096] * 64, 32, 8, seed=seed, device=device,
+                      rng_backend=rng_backend, name="llama8b_b64_ctx4096")
+
+
+def agentic_lengths(rng, B=16, median=80 * K1, sigma=0.42, lo=8 * K1, hi=200 * K1):
+    """Clipped log-normal context lengths with the trace's ~80K median.
+
+    sigma = 0.42 puts the expected maximum of ~610 sessions near the ~273K tail
+    quoted for the trace: ln(273/80) / Phi^-1(1 - 1/610) = 1.2275 / 2.94.
+    """
+    z = rng.standard_normal(B)
+    return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
+
+
+def agentic_80k(seed=0, device="cpu", rng_backend="torch"):
+    """Long-context agentic decode: batch 16, 32/8 heads, P = 512 partitions."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = agentic_lengths(rng)
+    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng,
+                      rng_backend=rng_backend, name="agentic_b16_median80k",
+                      partition_tokens=512)
+
+
+def ragged_lengths(rng, B=256):
+    """Uniform on [1, 32K], then 10% of sequences set to 1 and 5% to 128K."""
+    lens = rng.integers(1, 32 * K1, size=B, endpoint=True).astype(np.int64)
+    order = rng.permutation(B)
+    n_one, n_long = round(0.10 * B), round(0.05 * B)
+    lens[order[:n_one]] = 1
+    lens[order[n_one:n_one + n_long]] = 128 * K1
+    return lens
+
+
+def ragged_mixed(seed=0, device="cpu", rng_backend="torch"):
+    """Mixed ragged batch: 256 sequences, 32/8 heads."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = ragged_lengths(rng)
+    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng,
+                      rng_backend=rng_backend, name="ragged_b256_u32k")
+
+
+def disagg_merge(seed=0, device="cpu", rng_backend="torch"):
+    """Batch 32, 32/8 heads, 128K tokens each, split into 4 token ranges."""
+    return build_case([128 * K1] * 32, 32, 8, seed=seed, device=device,
+                      rng_backend=rng_backend, name="disagg_b32_ctx128k_r4", ranges=4)
+
+
+def range_views(case: Case, R: int):
+    """Block-table column slices and lengths of R equal contiguous token ranges.
+
+    Each range must be a whole number of blocks of every sequence; the slices
+    are strided views of the one table, as a node owning the range would see.
+    """
+    width = case.block_table.shape[1]
+    if width % R:
+        raise ValueError("table width must split into R equal ranges")
+    cols = width // R
+    toks = cols * BLOCK_SIZE
+    if not np.all(case.lens == case.lens[0]) or case.lens[0] != toks * R:
+        raise ValueError("range_views expects every sequence to fill the table")
+    views = []
+    for r in range(R):
+        bt = case.block_table[:, r * cols:(r + 1) * cols]
+        ln = torch.full((case.B,), toks, dtype=torch.int32, device=case.block_table.device)
+        views.append((bt, ln))
+    return views
+
+
+def host_sequences(case: Case, seq_ids):
+    """Host copies of Q and of the blocks of the chosen sequences.
+
+    Returns (q [n, Hq, D] fp16, k_pool, v_pool [sum blocks, bs, Hkv, D] fp16,
+    block_table [n, width] int64, lens [n]); the blocks are renumbered in the
+    order they are copied, so the returned table indexes the returned pools.
+    """
+    seq_ids = [int(b) for b in seq_ids]
+    lens = case.lens[seq_ids]
+    nblk = -(-lens // BLOCK_SIZE)
+    width = max(int(nblk.max()), 1)
+    table = np.full((len(seq_ids), width), -1, dtype=np.int64)
+    frames = []
+    off = 0
+    for i, b in enumerate(seq_ids):
+        k = int(nblk[i])
+        frames.extend(int(x) for x in case.block_table_host[b, :k])
+        table[i, :k] = np.arange(off, off + k)
+        off += k
+    idx = torch.tensor(frames, dtype=torch.int64, device=case.k_cache.device)
+    k_pool = case.k_cache.index_select(0, idx).cpu().numpy()
+    v_pool = case.v_cache.index_select(0, idx).cpu().numpy()
+    q = case.q[torch.tensor(seq_ids, device=case.q.device)].cpu().numpy()
+    return q, k_pool, v_pool, table, lens
+
+
+CONFIGS = {
+    "tiny": tiny,
+    "llama8b_4k": llama8b_4k,
+    "agentic_80k": agentic_80k,
+    "ragged_mixed": ragged_mixed,
+    "disagg_merge": disagg_merge,
+}
