@@ -1,0 +1,188 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+One step = one ``paged_decode_attn`` call (split-K partial kernel + merge
+kernel) over the whole batch, inputs resident in HBM.  Default workload: the
+long-context agentic batch (16 sequences, Llama-3.1-8B attention shape,
+clipped log-normal context lengths with an 80K median, 512-token partitions).
+
+Prints ONE JSON line:
+  value          KV-read GB/s of the whole job: algorithmic K+V bytes of valid
+                 tokens (sum_b ctx_b * 2 * Hkv * D * 2 B) / wall time per step
+  roofline       the same bytes / the average call time measured with HIP
+                 events on the launch stream, against the 8 TB/s HBM peak
+  cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV-read GB/s and % of HBM peak; decode-attn tokens/s at Llama-3.1-8B shape"
+SRC = os.path.join(ROOT, "decode_attention_paged_attn_amd", "csrc", "paged_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash():
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kv_bytes(lens, Hkv, D=128, elem=2):
+    return int(sum(int(n) for n in lens)) * 2 * Hkv * D * elem
+
+
+def measured_traffic(config_name):
+    """Counter-measured HBM bytes per call, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(config_name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(case, budget_s):
+    """Time the float64 oracle (gather + compute) on whole sequences until the budget."""
+    import numpy as np
+    import oracle.paged_attention as O
+    from decode_attention_paged_attn_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:                                    # threadpoolctl missing
+        threads = 1
+    rng = np.random.default_rng(1)
+    order = rng.permutation(case.B)
+    done, tokens, spent = [], 0, 0.0
+    for b in order:
+        q, k, v, table, lens = W.host_sequences(case, [int(b)])
+        t0 = time.perf_counter()
+        O.paged_decode_attention(q, k, v, table, lens, case.scale)
+        spent += time.perf_counter() - t0
+        done.append(int(b))
+        tokens += int(lens[0])
+        if spent >= budget_s:
+            break
+    gbs = kv_bytes([tokens], case.Hkv) / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {case.B} sequences ({tokens} tokens, all {case.Hq} query "
+                      f"heads), float64 numpy gather + two-pass softmax, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="agentic_80k")
+    ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU sharding of "
+                          "the path is described in the design notes, not built",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    from decode_attention_paged_attn_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pda.load_library()
+    torch.cuda.set_device(0)
+    case = W.CONFIGS[args.config](device="cuda")
+    P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    B, Hq, Hkv = case.B, case.Hq, case.Hkv
+    width = case.block_table.shape[1]
+    ws = torch.empty(max(pda.workspace_size(B, Hq, Hkv, width, P), 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    used_P = pda.workspace_layout(B, Hq, Hkv, width, P)["partition_tokens"]
+
+    def step():
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                              case.context_lens, case.scale, out=out, lse_out=lse,
+                              partition_tokens=P, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ev_mean = sum(ev_ms) / len(ev_ms)
+
+    nbytes = kv_bytes(case.lens, Hkv)
+    ms_per_step = wall / args.steps * 1e3
+    value = nbytes / (ms_per_step / 1e3) / 1e9
+    achieved = nbytes / (ev_mean / 1e3) / 1e9
+    traffic = measured_traffic(args.config)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "block_size": 16,
+            "partition_tokens": used_P, "tokens": int(case.lens.sum()),
+            "min_ctx": int(case.lens.min()), "max_ctx": int(case.lens.max()),
+            "kv_bytes_per_step": nbytes, "seed": case.seed,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_attn_tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "attn_only_tokens_per_s_32_layer_step": round(B / (32 * ms_per_step / 1e3), 1),
+        "event_ms": {"mean": round(ev_mean, 5), "p10": round(ev_ms[len(ev_ms) // 10], 5),
+                     "p50": round(ev_ms[len(ev_ms) // 2], 5),
+                     "p90": round(ev_ms[(9 * len(ev_ms)) // 10], 5)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_attn call (split_kernel + merge_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "kernel_source_sha256_16": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

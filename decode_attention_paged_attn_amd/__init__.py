@@ -1,0 +1,28 @@
+"""Paged decode attention for MI355X: thin Python binding over the HIP C ABI.
+
+Every step of the computation runs in the HIP kernels of ``libpagedattn.so``;
+this package only checks tensor shapes, takes device pointers and torch's
+current stream, and allocates the caller-side buffers.  If the library is not
+built the calls raise; there is no fallback.
+"""
+from ._binding import (  # noqa: F401
+    PdaError,
+    library_path,
+    load_library,
+    merge_partials,
+    paged_decode_attn,
+    paged_decode_attn_partial,
+    workspace_layout,
+    workspace_size,
+)
+
+__all__ = [
+    "PdaError",
+    "library_path",
+    "load_library",
+    "merge_partials",
+    "paged_decode_attn",
+    "paged_decode_attn_partial",
+    "workspace_layout",
+    "workspace_size",
+]

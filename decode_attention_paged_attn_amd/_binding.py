@@ -1,0 +1,223 @@
+"""ctypes binding of ``include/paged_attn.h``.
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+layout, then their device pointers go to the C ABI together with torch's
+current HIP stream.  Output and workspace buffers are allocated with torch
+when the caller does not pass them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpagedattn.so"
+_lock = threading.Lock()
+_lib = None
+
+HEAD_DIM = 128
+BLOCK_SIZE = 16
+
+_c_int = ctypes.c_int
+_c_i64 = ctypes.c_int64
+_c_size = ctypes.c_size_t
+_c_float = ctypes.c_float
+_vp = ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/paged_attn.h
+_SIGNATURES = {
+    "pda_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    ctypes.POINTER(_c_size)]),
+    "pda_workspace_layout": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      ctypes.POINTER(_c_size), ctypes.POINTER(_c_size),
+                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "paged_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_i64, _c_int, _c_float, _c_int, _vp, _vp,
+                                   _c_size, _vp]),
+    "paged_decode_attn_partial": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
+                                           _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                           _c_float, _c_int, _vp, _c_size, _vp]),
+    "merge_partials": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "pda_last_error": (ctypes.c_char_p, []),
+    "pda_version": (ctypes.c_char_p, []),
+}
+
+STATUS = {0: "PDA_OK", 1: "PDA_EINVAL", 2: "PDA_EUNSUPPORTED", 3: "PDA_EHIP"}
+
+
+class PdaError(RuntimeError):
+    """A non-zero status from the C ABI, with the library's message."""
+
+    def __init__(self, code, message):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+def library_path():
+    return os.environ.get("PDA_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load ``libpagedattn.so`` (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is missing: build the HIP library first "
+                    "(python -m decode_attention_paged_attn_amd.build_lib)")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+        return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        msg = load_library().pda_last_error().decode(errors="replace")
+        raise PdaError(rc, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
+                   block_size=BLOCK_SIZE):
+    n = _c_size(0)
+    _check(load_library().pda_workspace_size(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                                             partition_tokens, ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace_layout(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
+                     block_size=BLOCK_SIZE):
+    o_off, lse_off = _c_size(0), _c_size(0)
+    max_parts, P = _c_int(0), _c_int(0)
+    _check(load_library().pda_workspace_layout(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                                               partition_tokens, ctypes.byref(o_off),
+                                               ctypes.byref(lse_off), ctypes.byref(max_parts),
+                                               ctypes.byref(P)))
+    return {"o_offset": int(o_off.value), "lse_offset": int(lse_off.value),
+            "max_parts": int(max_parts.value), "partition_tokens": int(P.value)}
+
+
+def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
+    if q.dtype != torch.float16 or k_cache.dtype != torch.float16 or v_cache.dtype != torch.float16:
+        raise TypeError("q, k_cache and v_cache must be float16")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_table and context_lens must be int32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t in (k_cache, v_cache, block_table, context_lens):
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q is [B, Hq, D]; k_cache and v_cache are [num_blocks, bs, Hkv, D]")
+    if not (q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("q, k_cache, v_cache and context_lens must be contiguous")
+    B = q.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table is [B, width] and context_lens is [B]")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous (stride(1) == 1)")
+    if q.shape[2] != k_cache.shape[3]:
+        raise ValueError("head dims of q and the caches differ")
+    return dev
+
+
+def _run(partial, q, k_cache, v_cache, block_table, context_lens, scale, out, lse, need_lse,
+         partition_tokens, workspace, max_blocks_per_seq):
+    dev = _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    width = block_table.shape[1]
+    mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    if mb > width:
+        raise ValueError("max_blocks_per_seq exceeds the block table width")
+    bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
+    ws_bytes = workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace needs {ws_bytes} bytes")
+    out_dtype = torch.float32 if partial else torch.float16
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    if out.dtype != out_dtype or out.shape != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError(f"output must be contiguous {out_dtype} [B, Hq, D]")
+    if lse is None and need_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B, Hq)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [B, Hq]")
+    lib = load_library()
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), bt_stride,
+            _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb, float(scale),
+            int(partition_tokens))
+    if partial:
+        rc = lib.paged_decode_attn_partial(_ptr(out), _ptr(lse), *args, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(dev))
+    else:
+        rc = lib.paged_decode_attn(_ptr(out), *args, _ptr(lse), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc)
+    return out, lse
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale, out=None,
+                      lse_out=None, return_lse=False, partition_tokens=0, workspace=None,
+                      max_blocks_per_seq=None):
+    """fp16 decode attention over a paged KV cache; see include/paged_attn.h.
+
+    Returns ``out`` (fp16 [B, Hq, D]), or ``(out, lse)`` when ``return_lse`` or
+    ``lse_out`` is given.
+    """
+    out, lse = _run(False, q, k_cache, v_cache, block_table, context_lens, scale, out,
+                    lse_out, return_lse, partition_tokens, workspace, max_blocks_per_seq)
+    return (out, lse) if (return_lse or lse_out is not None) else out
+
+
+def paged_decode_attn_partial(q, k_cache, v_cache, block_table, context_lens, scale, o=None,
+                              lse=None, partition_tokens=0, workspace=None,
+                              max_blocks_per_seq=None):
+    """Normalised partial (o fp32 [B, Hq, D], lse fp32 [B, Hq]) of a token range."""
+    return _run(True, q, k_cache, v_cache, block_table, context_lens, scale, o, lse, True,
+                partition_tokens, workspace, max_blocks_per_seq)
+
+
+def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
+    """Log-sum-exp merge of R partials: o_parts [R, B, Hq, D], lse_parts [R, B, Hq]."""
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if o_parts.dim() != 4 or lse_parts.shape != o_parts.shape[:3]:
+        raise ValueError("o_parts is [R, B, Hq, D] and lse_parts [R, B, Hq]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    if o_parts.device.type != "cuda" or lse_parts.device != o_parts.device:
+        raise ValueError("partials must be on one GPU")
+    R, B, Hq, D = o_parts.shape
+    dev = o_parts.device
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    if out.dtype != torch.float16 or out.shape != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float16 [B, Hq, D]")
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check(load_library().merge_partials(_ptr(out), _ptr(lse_out), _ptr(o_parts),
+                                         _ptr(lse_parts), R, B, Hq, D, _stream(dev)))
+    return (out, lse_out) if return_lse else out

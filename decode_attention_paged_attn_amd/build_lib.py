@@ -1,0 +1,55 @@
+"""Compile the HIP library in-tree for gfx950.
+
+``python -m decode_attention_paged_attn_amd.build_lib`` (or ``build()``) runs
+hipcc on ``csrc/paged_attn.hip`` and writes ``libpagedattn.so`` next to this
+file.  It always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "paged_attn.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpagedattn.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # no packed-fp32 instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose=False, extra_flags=()):
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in res.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    print("built", LIB)
+    sys.exit(0)

@@ -281,6 +281,12 @@ def host_sequences(case: Case, seq_ids):
     return q, k_pool, v_pool, table, lens
 
 
+def host_full(case: Case):
+    """Host copies of the whole case (small cases only): q, pools, table, lens."""
+    return (case.q.cpu().numpy(), case.k_cache.cpu().numpy(), case.v_cache.cpu().numpy(),
+            case.block_table_host.copy(), case.lens.copy())
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama8b_4k": llama8b_4k,

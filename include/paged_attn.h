@@ -1,0 +1,191 @@
+/*
+ * paged_attn.h - single-token decode attention over a paged KV cache, for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What the library computes
+ * -------------------------
+ * For every sequence b and query head h of one decode step,
+ *
+ *     out[b,h,:] = softmax_t( scale * q[b,h,:] . K_b[t,g,:] ) V_b[t,g,:],
+ *     lse[b,h]   = ln sum_t exp( scale * q[b,h,:] . K_b[t,g,:] ),
+ *
+ * over the tokens t = 0 .. context_lens[b]-1 of that sequence, where the key
+ * and value rows are not contiguous but gathered through a block table, and
+ * g = h / (Hq / Hkv) is the KV head shared by a group of query heads.  Decode
+ * attention reads the whole accumulated KV of each sequence for one query, so
+ * it is bound by HBM bandwidth ("Why prefill and decode are opposite
+ * problems" and "How the backend reads the paged KV" on the page "The
+ * signature-dish specialist: vLLM's attention backend"; §2.2 of the
+ * KernelFlume paper, academ.us/article/2606.29207).
+ *
+ * Layouts (all row-major, the last index contiguous)
+ * --------------------------------------------------
+ *   q            fp16  [B, Hq, D]
+ *   k_cache      fp16  [num_blocks, block_size, Hkv, D]   physical pool of K
+ *   v_cache      fp16  [num_blocks, block_size, Hkv, D]   physical pool of V
+ *   block_table  int32 [B, block_table_stride]; entry [b, i] is the physical
+ *                block holding tokens i*block_size .. i*block_size+block_size-1
+ *                of sequence b.  Only entries i < ceil(context_lens[b] /
+ *                block_size) are read; the rest may hold anything.
+ *   context_lens int32 [B]; number of cached tokens of each sequence, the token
+ *                being decoded included (its K/V must already be in the cache).
+ *   out          fp16  [B, Hq, D];  lse fp32 [B, Hq] (natural log).
+ * One block of one pool holds block_size * Hkv * D fp16 values, the block
+ * stride of "Physical Memory Block Layout" on the page "Disaggregated
+ * Inference Architecture: Paged KV-Cache Tiering, Chunked Prefill, and
+ * Asynchronous Overlap"; logical block i holds tokens 16i .. 16i+15 (figure
+ * "Virtual Sequence Address Space" on that page).
+ *
+ * Supported shapes: D = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 8}.
+ * Other shapes return PDA_EUNSUPPORTED.
+ *
+ * Conventions
+ * -----------
+ * - Device pointers: q, k_cache, v_cache, block_table, context_lens, out,
+ *   lse, workspace and every partial buffer are device memory of the current
+ *   HIP device.  `stream` is a hipStream_t (NULL = the default stream).
+ * - Ownership: the caller allocates and owns every buffer, the workspace
+ *   included.  The library never allocates or frees memory on these calls,
+ *   never synchronises, and only enqueues kernels on `stream`, so the calls
+ *   may be captured into a HIP graph.  Inputs are read-only; outputs must not
+ *   alias inputs.
+ * - Errors: a non-zero pda_status is returned and pda_last_error() gives a
+ *   message for the calling thread.  Argument errors are detected on the host
+ *   before anything is enqueued.  Device-side contract violations (a block
+ *   id outside [0, num_blocks), context_lens[b] > max_blocks_per_seq *
+ *   block_size or negative) are undefined behaviour; setting the environment
+ *   variable PDA_DEBUG_VALIDATE=1 makes each call copy context_lens and the
+ *   block table to the host and check them first (this synchronises the
+ *   stream; for tests only).
+ * - Results are bitwise deterministic for a fixed partition length: no
+ *   floating-point atomics are used.
+ * - Thread safety: calls may be made from several threads; the only global
+ *   state is a per-device property cache filled on first use.
+ */
+#ifndef PAGED_ATTN_H_
+#define PAGED_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PDA_OK = 0,
+  PDA_EINVAL = 1,       /* bad argument: null pointer, Hq % Hkv != 0, ...   */
+  PDA_EUNSUPPORTED = 2, /* valid but not built: D != 128, block_size != 16  */
+  PDA_EHIP = 3          /* a HIP runtime or launch error                    */
+} pda_status;
+
+/*
+ * Bytes of device workspace paged_decode_attn and paged_decode_attn_partial
+ * need for these sizes (*bytes; 0 is possible).  partition_tokens as in
+ * paged_decode_attn (0 = automatic).  The workspace holds, per (sequence,
+ * split-K partition, query head), the fp32 partial output and log-sum-exp.
+ */
+int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size,
+                       int max_blocks_per_seq, int partition_tokens,
+                       size_t* bytes);
+
+/*
+ * Where the per-partition partials live inside the workspace after a call,
+ * for inspection by tests: lse of (b, p, h) is the float at byte offset
+ * *lse_offset + 4 * ((b * *max_parts + p) * Hq + h), and its normalised
+ * output row the D floats at *o_offset + 4 * D * ((b * *max_parts + p) * Hq
+ * + h).  *partition_tokens_out receives the partition length that is used.
+ * Only partitions p < ceil(context_lens[b] / partition length) are written.
+ */
+int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size,
+                         int max_blocks_per_seq, int partition_tokens,
+                         size_t* o_offset, size_t* lse_offset, int* max_parts,
+                         int* partition_tokens_out);
+
+/*
+ * Decode attention over a paged KV cache (see the top of this file).
+ *
+ * Each sequence's KV is cut into contiguous split-K partitions of
+ * partition_tokens tokens (a multiple of block_size, at most 1024; 0 picks a
+ * length from the batch shape and the device's CU count).  Partition p of a
+ * sequence with n tokens covers tokens [p*P, min((p+1)*P, n)).  A first kernel
+ * computes, for every (sequence, KV head, partition), the partial of all Hq /
+ * Hkv query heads that share the KV head; a second kernel merges the partials
+ * of each (sequence, query head) by log-sum-exp.  Partials over contiguous
+ * token ranges and their merge are the attention-node / weight-node split of
+ * §3.1 "Kernel-level Disaggregation" and §3.2 "Workflow of Elastic Decoding"
+ * in the KernelFlume paper, whose merge equals attention over the full range
+ * (§5.1 "Query-First Attention"; the (m, l, O) update equations of
+ * "Mathematical Formulation of Chunked Attention" on the
+ * disaggregated-inference page).
+ *
+ * out            fp16 [B, Hq, D], written.
+ * lse_out        fp32 [B, Hq] or NULL; natural-log log-sum-exp of the scaled
+ *                scores.  A sequence with context_lens[b] == 0 gets out = 0
+ *                and lse = -inf.
+ * scale          multiplies q . k before the softmax (typically 1/sqrt(D)).
+ * num_blocks     rows of k_cache / v_cache (used by PDA_DEBUG_VALIDATE).
+ * max_blocks_per_seq  largest ceil(context_lens[b] / block_size) the call may
+ *                see; sizes the workspace and the launch.
+ * block_table_stride  int32 elements between rows of block_table
+ *                (>= max_blocks_per_seq), so a column slice of a wider table
+ *                can be passed without a copy.
+ * workspace      device memory of at least pda_workspace_size() bytes, 256-byte
+ *                aligned; contents on entry are ignored.
+ */
+int paged_decode_attn(void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      int64_t block_table_stride, const int32_t* context_lens,
+                      int B, int Hq, int Hkv, int D, int block_size,
+                      int64_t num_blocks, int max_blocks_per_seq, float scale,
+                      int partition_tokens, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * The partial of a token range: same inputs as paged_decode_attn, where the
+ * block table and context_lens describe the range a caller owns (a column
+ * slice of the full table via block_table_stride, and the range's length).
+ * Writes the normalised output o fp32 [B, Hq, D] and lse fp32 [B, Hq] of
+ * attention over that range: the (o_i, m_i, l_i) partial an attention node
+ * returns in §3.2 of the KernelFlume paper, with o_i normalised and
+ * lse = m_i + ln l_i.  An empty range gives o = 0, lse = -inf.
+ */
+int paged_decode_attn_partial(float* o, float* lse, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_table,
+                              int64_t block_table_stride,
+                              const int32_t* context_lens, int B, int Hq,
+                              int Hkv, int D, int block_size,
+                              int64_t num_blocks, int max_blocks_per_seq,
+                              float scale, int partition_tokens,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Merge R partials over disjoint token ranges into attention over their
+ * union, by log-sum-exp: with L = max_r lse_r and w_r = exp(lse_r - L),
+ * lse = L + ln sum_r w_r and out = sum_r w_r o_r / sum_r w_r (the merge a
+ * weight node applies to attention-node partials, KernelFlume paper §3.2 and
+ * §5.1; "Mathematical Formulation of Chunked Attention" on the
+ * disaggregated-inference page).  Partials with lse = -inf carry no weight;
+ * if all are -inf, out = 0 and lse = -inf.
+ *
+ * o_parts   fp32 [R, B, Hq, D]    lse_parts fp32 [R, B, Hq]
+ * out       fp16 [B, Hq, D]       lse_out   fp32 [B, Hq] or NULL
+ * D must be 128.  R >= 1.
+ */
+int merge_partials(void* out, float* lse_out, const float* o_parts,
+                   const float* lse_parts, int R, int B, int Hq, int D,
+                   void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* pda_last_error(void);
+
+/* Library version string. */
+const char* pda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H_ */

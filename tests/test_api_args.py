@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_paged_attn_amd as pda
+from decode_attention_paged_attn_amd import build_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pda.library_path()):
+        build_lib.build()
+    return pda.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_api():
+    names = set(declared_functions())
+    assert {"paged_decode_attn", "paged_decode_attn_partial", "merge_partials",
+            "pda_workspace_size", "pda_workspace_layout", "pda_last_error",
+            "pda_version"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_empty_error(lib):
+    assert b"gfx950" in lib.pda_version()
+
+
+def _ws(B=2, Hq=8, Hkv=2, D=128, bs=16, mb=32, P=0):
+    n = ctypes.c_size_t(0)
+    rc = pda.load_library().pda_workspace_size(B, Hq, Hkv, D, bs, mb, P, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), 1),        # Hq % Hkv != 0
+    (dict(Hq=48, Hkv=4), 2),       # G = 12 not built
+    (dict(D=64), 2),
+    (dict(bs=32), 2),
+    (dict(P=24), 1),               # not a multiple of the block size
+    (dict(P=-16), 1),
+    (dict(P=2048), 2),             # above the block-table window
+    (dict(B=-1), 1),
+    (dict(mb=-1), 1),
+    (dict(Hkv=0), 1),
+])
+def test_workspace_size_rejects(lib, kw, code):
+    rc, _ = _ws(**kw)
+    assert rc == code
+    assert lib.pda_last_error()
+
+
+def test_workspace_size_formula(lib):
+    # explicit partition length: B * ceil(mb*16/P) * Hq slots of D floats + one lse float
+    B, Hq, Hkv, mb, P = 3, 32, 8, 100, 256
+    rc, n = _ws(B=B, Hq=Hq, Hkv=Hkv, mb=mb, P=P)
+    assert rc == 0
+    parts = -(-mb * 16 // P)
+    slots = B * parts * Hq
+    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    assert n == align(slots * 128 * 4) + align(slots * 4)
+    lay = pda.workspace_layout(B, Hq, Hkv, mb, P)
+    assert lay == {"o_offset": 0, "lse_offset": align(slots * 128 * 4), "max_parts": parts,
+                   "partition_tokens": P}
+    assert pda.workspace_size(0, Hq, Hkv, mb, P) == 0
+
+
+def _call_attn(lib, **over):
+    a = dict(out=1, q=1, k=1, v=1, bt=1, bt_stride=4, ctx=1, B=2, Hq=8, Hkv=2, D=128, bs=16,
+             nblocks=10, mb=4, scale=0.1, P=0, lse=None, ws=256, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)   # noqa: E731
+    return lib.paged_decode_attn(vp(a["out"]), vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["bt"]),
+                                 a["bt_stride"], vp(a["ctx"]), a["B"], a["Hq"], a["Hkv"], a["D"],
+                                 a["bs"], a["nblocks"], a["mb"], a["scale"], a["P"], vp(a["lse"]),
+                                 vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(bt=None), 1),
+    (dict(ctx=None), 1),
+    (dict(Hq=6, Hkv=4), 1),
+    (dict(D=96), 2),
+    (dict(bs=8), 2),
+    (dict(P=40), 1),
+    (dict(bt_stride=3), 1),        # narrower than max_blocks_per_seq
+    (dict(nblocks=0), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(ws=None), 1),
+    (dict(ws_bytes=16), 1),        # too small
+    (dict(ws=257), 1),             # misaligned
+])
+def test_paged_decode_attn_rejects_before_launch(lib, over, code):
+    assert _call_attn(lib, **over) == code
+    assert lib.pda_last_error()
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _call_attn(lib, B=0, out=None, q=None, ws=None) == 0
+
+
+def test_merge_partials_rejects(lib):
+    vp = ctypes.c_void_p
+    assert lib.merge_partials(vp(1), None, vp(1), vp(1), 0, 2, 8, 128, None) == 1
+    assert lib.merge_partials(vp(1), None, vp(1), vp(1), 2, 2, 8, 64, None) == 2
+    assert lib.merge_partials(None, None, vp(1), vp(1), 2, 2, 8, 128, None) == 1
+    assert lib.merge_partials(vp(1), None, vp(1), vp(1), 2, 0, 8, 128, None) == 0
+
+
+def test_partial_requires_lse(lib):
+    vp = ctypes.c_void_p
+    rc = lib.paged_decode_attn_partial(vp(1), None, vp(1), vp(1), vp(1), vp(1), 4, vp(1), 2, 8,
+                                       2, 128, 16, 10, 4, 0.1, 0, vp(256), 1 << 30, None)
+    assert rc == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from decode_attention_paged_attn_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setenv("PDA_LIBRARY", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.load_library()

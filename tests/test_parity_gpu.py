@@ -1,0 +1,289 @@
+"""HIP path against the float64 oracle, element by element, on seeded inputs.
+
+Every call goes through the C ABI (ctypes binding).  Small cases are checked in
+full; the full-size workloads are checked on sampled sequences, which the
+oracle computes one at a time, in the launch configuration the benchmark
+times.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_attn_amd as pda
+from decode_attention_paged_attn_amd import workloads as W
+import oracle.paged_attention as O
+from tests.parity import compare_lse, compare_out, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pda.load_library()          # raises if the HIP library is missing
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run(case, partition_tokens=0, **kw):
+    _say(f"[run] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={partition_tokens}")
+    out, lse = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                     case.context_lens, case.scale, return_lse=True,
+                                     partition_tokens=partition_tokens, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_full(case):
+    q, k, v, table, lens = W.host_full(case)
+    return O.paged_decode_attention(q, k, v, table, lens, case.scale)
+
+
+# --- small cases, checked in full ----------------------------------------------
+
+@pytest.mark.parametrize("P", [0, 16, 64, 128, 512, 1024])
+def test_tiny_workload(P):
+    case = W.tiny(device="cuda")
+    out, lse = run(case, P)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 100, 255, 256, 257, 511, 512, 513, 1000, 1537]
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("P", [0, 32, 256])
+def test_ragged_lengths_all_group_sizes(G, Hkv, P):
+    case = W.build_case(RAGGED, G * Hkv, Hkv, pool_blocks=sum(-(-n // 16) for n in RAGGED) + 7,
+                        seed=100 + G, device="cuda", name=f"ragged_G{G}")
+    out, lse = run(case, P)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_empty_contexts():
+    case = W.build_case([0, 5, 0, 17], 8, 2, seed=3, device="cuda", width=2)
+    out, lse = run(case)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(o[[0, 2]] == 0) and np.all(np.isneginf(l[[0, 2]]))
+    ref, ref_lse = oracle_full(case)
+    compare_out(o, ref)
+    compare_lse(l, ref_lse)
+
+
+def test_one_token_returns_v_exactly():
+    case = W.build_case([1] * 6, 32, 8, seed=4, device="cuda")
+    out, _ = run(case)
+    o = out.cpu().numpy()
+    v = case.v_cache.cpu().numpy()
+    for b in range(6):
+        f = int(case.block_table_host[b, 0])
+        for h in range(32):
+            assert np.array_equal(o[b, h], v[f, 0, h // 4]), (b, h)
+
+
+def test_scale_zero_gives_exact_mean():
+    lens = [1, 7, 16, 37, 300, 1025]
+    case = W.build_case(lens, 8, 2, seed=5, device="cuda")
+    v = case.v_cache.cpu().numpy()
+    t = np.arange(16)
+    for b, n in enumerate(lens):
+        for i in range(-(-n // 16)):
+            f = int(case.block_table_host[b, i])
+            tok = 16 * i + t
+            for g in range(2):
+                d = np.arange(128)
+                v[f, :, g, :] = ((tok[:, None] + 7 * d[None, :] + 13 * g) % 2048) / 2048.0
+    case.v_cache.copy_(torch.from_numpy(v))
+    case.scale = 0.0
+    out, lse = run(case)
+    o, l = to_np(out), to_np(lse)
+    for b, n in enumerate(lens):
+        for g in range(2):
+            exact = [float(sum(Fraction((tt + 7 * d + 13 * g) % 2048, 2048) for tt in range(n)) / n)
+                     for d in range(128)]
+            for h in range(4 * g, 4 * g + 4):
+                compare_out(o[b, h][None], np.array(exact)[None])
+                assert abs(l[b, h] - math.log(n)) <= 1e-5
+
+
+def test_frame_permutation_changes_nothing():
+    need = sum(-(-n // 16) for n in RAGGED)
+    case = W.build_case(RAGGED, 16, 4, seed=6, device="cuda", pool_blocks=need + 20)
+    out1, lse1 = run(case)
+    sigma = torch.randperm(case.num_blocks, generator=torch.Generator().manual_seed(1))
+    k2 = torch.empty_like(case.k_cache)
+    v2 = torch.empty_like(case.v_cache)
+    k2[sigma.cuda()] = case.k_cache
+    v2[sigma.cuda()] = case.v_cache
+    bt = case.block_table.long()
+    bt2 = torch.where(bt >= 0, sigma.cuda()[bt.clamp(min=0)], bt).int()
+    case.k_cache, case.v_cache, case.block_table = k2, v2, bt2.contiguous()
+    out2, lse2 = run(case)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_bitwise_deterministic():
+    case = W.build_case(RAGGED * 2, 32, 8, seed=7, device="cuda")
+    a, la = run(case, 64)
+    b, lb = run(case, 64)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_partition_partials_in_workspace():
+    case = W.build_case([1, 63, 64, 65, 200, 777], 8, 2, seed=8, device="cuda")
+    P = 64
+    lay = pda.workspace_layout(case.B, case.Hq, case.Hkv, case.block_table.shape[1], P)
+    ws = torch.zeros(pda.workspace_size(case.B, case.Hq, case.Hkv, case.block_table.shape[1], P),
+                     dtype=torch.uint8, device="cuda")
+    run(case, P, workspace=ws)
+    mp = lay["max_parts"]
+    raw = ws.cpu()
+    o_ws = raw[lay["o_offset"]:lay["o_offset"] + 4 * case.B * mp * case.Hq * 128].view(
+        torch.float32).reshape(case.B, mp, case.Hq, 128).numpy()
+    l_ws = raw[lay["lse_offset"]:lay["lse_offset"] + 4 * case.B * mp * case.Hq].view(
+        torch.float32).reshape(case.B, mp, case.Hq).numpy()
+    q, k, v, table, lens = W.host_full(case)
+    o_ref, l_ref = O.split_k_partials(q, k, v, table, lens, case.scale, P)
+    for b, n in enumerate(lens):
+        for p in range(-(-int(n) // P)):
+            compare_lse(l_ws[b, p], l_ref[b, :, p], what=f"lse b={b} p={p}")
+            compare_out(o_ws[b, p], o_ref[b, :, p], abs_tol=1e-4, row_rel_tol=1e-4,
+                        what=f"o b={b} p={p}")
+
+
+def test_partial_api_and_merge():
+    R, per = 4, 256
+    lens = [R * per] * 3
+    case = W.build_case(lens, 32, 8, seed=9, device="cuda")
+    cols = per // 16
+    o_parts, l_parts = [], []
+    for r in range(R):
+        bt = case.block_table[:, r * cols:(r + 1) * cols]
+        ln = torch.full((case.B,), per, dtype=torch.int32, device="cuda")
+        o, l = pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln,
+                                             case.scale)
+        o_parts.append(o)
+        l_parts.append(l)
+    merged, mlse = pda.merge_partials(torch.stack(o_parts).contiguous(),
+                                      torch.stack(l_parts).contiguous())
+    single, slse = run(case)
+    ulp = np.abs(to_np(merged) - to_np(single)) / np.maximum(
+        np.spacing(np.abs(to_np(single)).astype(np.float16)).astype(np.float64), 2.0 ** -24)
+    assert ulp.max() <= 2, ulp.max()
+    q, k, v, table, ln = W.host_full(case)
+    ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
+    compare_out(to_np(merged), ref)
+    compare_lse(to_np(mlse), ref_lse)
+    # each partial against the oracle's partial over the same range
+    for r in range(R):
+        o_ref, l_ref = O.partial_attention(q, k, v, table[:, r * cols:(r + 1) * cols],
+                                           [per] * 3, case.scale)
+        compare_out(to_np(o_parts[r]), o_ref, abs_tol=1e-4, row_rel_tol=1e-4)
+        compare_lse(to_np(l_parts[r]), l_ref)
+
+
+def test_merge_partials_edge_cases():
+    g = torch.Generator(device="cuda").manual_seed(10)
+    o = torch.randn((3, 2, 4, 128), generator=g, device="cuda")
+    lse = torch.randn((3, 2, 4), generator=g, device="cuda") * 4
+    lse[1] = -float("inf")                      # an empty range everywhere
+    lse[2, 1] = -float("inf")
+    lse[:, 0, 3] = -float("inf")                # (b=0, h=3): every range empty
+    out, mlse = pda.merge_partials(o, lse)
+    ref_o, ref_l = O.merge_partials(to_np(o), to_np(lse))
+    compare_out(to_np(out), ref_o)
+    compare_lse(to_np(mlse), ref_l)
+    assert np.all(to_np(out)[0, 3] == 0) and np.isneginf(to_np(mlse)[0, 3])
+
+
+def test_graph_capture_replays_match_eager():
+    case = W.build_case(RAGGED, 32, 8, seed=11, device="cuda")
+    ws = torch.empty(pda.workspace_size(case.B, 32, 8, case.block_table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, 32, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((case.B, 32), dtype=torch.float32, device="cuda")
+    args = (case.q, case.k_cache, case.v_cache, case.block_table, case.context_lens, case.scale)
+    pda.paged_decode_attn(*args, out=out, lse_out=lse, workspace=ws)
+    torch.cuda.synchronize()
+    eager, eager_lse = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            pda.paged_decode_attn(*args, out=out, lse_out=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager) and torch.equal(lse, eager_lse), f"replay {i}"
+        _ = (case.q.float() * 2).sum().item()    # eager work between replays
+
+
+# --- full-size workloads, sampled sequences ------------------------------------
+
+def _check_sampled(case, out, lse, seq_ids):
+    q, k, v, table, lens = W.host_sequences(case, seq_ids)
+    ref, ref_lse = O.paged_decode_attention(q, k, v, table, lens, case.scale)
+    o, l = to_np(out), to_np(lse)
+    for i, b in enumerate(seq_ids):
+        compare_out(o[b], ref[i], what=f"{case.name} seq {b} (ctx {lens[i]})")
+        compare_lse(l[b], ref_lse[i], what=f"{case.name} seq {b}")
+
+
+def _sample(lens, rng, k=2):
+    order = np.argsort(lens, kind="stable")
+    pick = {int(order[0]), int(order[-1])}
+    pick.update(int(x) for x in rng.choice(len(lens), size=k, replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["llama8b_4k", "agentic_80k", "ragged_mixed"])
+def test_full_size_workload(name):
+    case = W.CONFIGS[name](device="cuda")
+    out, lse = run(case, case.partition_tokens)
+    assert torch.isfinite(out.float()).all()
+    ids = _sample(case.lens, np.random.default_rng(0))
+    _check_sampled(case, out, lse, ids)
+    # a rerun is bitwise identical
+    out2, lse2 = run(case, case.partition_tokens)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_full_size_partial_merge():
+    case = W.disagg_merge(device="cuda")
+    views = W.range_views(case, case.ranges)
+    o_parts = torch.empty((case.ranges, case.B, case.Hq, 128), dtype=torch.float32, device="cuda")
+    l_parts = torch.empty((case.ranges, case.B, case.Hq), dtype=torch.float32, device="cuda")
+    for r, (bt, ln) in enumerate(views):
+        _say(f"[run] {case.name} range {r}")
+        pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln, case.scale,
+                                      o=o_parts[r], lse=l_parts[r])
+    merged, mlse = pda.merge_partials(o_parts, l_parts)
+    single, slse = run(case)
+    m, s = to_np(merged), to_np(single)
+    ulp = np.abs(m - s) / np.maximum(np.spacing(np.abs(s).astype(np.float16)).astype(np.float64),
+                                     2.0 ** -24)
+    assert ulp.max() <= 2, ulp.max()
+    _check_sampled(case, merged, mlse, [0, 17, 31])
+    del case
+    torch.cuda.empty_cache()
