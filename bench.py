@@ -81,6 +81,25 @@ def cpu_baseline(case, budget_s):
                       f"heads), float64 numpy gather + two-pass softmax, {spent:.1f} s"}
 
 
+def copy_calibration(mib, steps):
+    """A plain copy of known size: each launch reads and writes mib MiB."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": steps + 2, "ms_per_copy": round(dt * 1e3, 4),
+                      "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,6 +109,9 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead: time a plain device copy of MIB MiB (the reference "
+                         "kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -103,8 +125,11 @@ def main():
     from decode_attention_paged_attn_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    pda.load_library()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+    pda.load_library()
     case = W.CONFIGS[args.config](device="cuda")
     P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
     B, Hq, Hkv = case.B, case.Hq, case.Hkv
@@ -113,7 +138,7 @@ def main():
                      device="cuda")
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    used_P = pda.workspace_layout(B, Hq, Hkv, width, P)["partition_tokens"]
+    used_P = pda.workspace_layout(B, Hq, Hkv, width, P)["unit_tokens"]
 
     def step():
         pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,

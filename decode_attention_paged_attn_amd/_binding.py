@@ -27,13 +27,20 @@ _c_size = ctypes.c_size_t
 _c_float = ctypes.c_float
 _vp = ctypes.c_void_p
 
+class PdaLayout(ctypes.Structure):
+    """pda_layout of include/paged_attn.h."""
+    _fields_ = [("header_offset", ctypes.c_size_t), ("lse_offset", ctypes.c_size_t),
+                ("o_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("n_workgroups", ctypes.c_int), ("n_slots", ctypes.c_int),
+                ("unit_tokens", ctypes.c_int)]
+
+
 # name -> (restype, argtypes); mirrors include/paged_attn.h
 _SIGNATURES = {
     "pda_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.POINTER(_c_size)]),
     "pda_workspace_layout": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                      ctypes.POINTER(_c_size), ctypes.POINTER(_c_size),
-                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+                                      ctypes.POINTER(PdaLayout)]),
     "paged_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_i64, _c_int, _c_float, _c_int, _vp, _vp,
                                    _c_size, _vp]),
@@ -103,14 +110,11 @@ def workspace_size(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DI
 
 def workspace_layout(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
                      block_size=BLOCK_SIZE):
-    o_off, lse_off = _c_size(0), _c_size(0)
-    max_parts, P = _c_int(0), _c_int(0)
+    """The workspace layout as a dict (see pda_workspace_layout in the header)."""
+    lay = PdaLayout()
     _check(load_library().pda_workspace_layout(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
-                                               partition_tokens, ctypes.byref(o_off),
-                                               ctypes.byref(lse_off), ctypes.byref(max_parts),
-                                               ctypes.byref(P)))
-    return {"o_offset": int(o_off.value), "lse_offset": int(lse_off.value),
-            "max_parts": int(max_parts.value), "partition_tokens": int(P.value)}
+                                               partition_tokens, ctypes.byref(lay)))
+    return {name: int(getattr(lay, name)) for name, _ in PdaLayout._fields_}
 
 
 def _check_inputs(q, k_cache, v_cache, block_table, context_lens):

@@ -1,30 +1,40 @@
 // Single-token decode attention over a paged KV cache for MI355X (gfx950).
 //
-// Two kernels on the caller's stream:
+// The math: attention of one decode query per sequence over its whole cached
+// K/V, which is bound by HBM bandwidth ("Why prefill and decode are opposite
+// problems" on the page "The signature-dish specialist: vLLM's attention
+// backend"); K/V rows gathered through a block table ("How the backend reads
+// the paged KV", same page; "Physical Memory Block Layout" on the page
+// "Disaggregated Inference Architecture: Paged KV-Cache Tiering, Chunked
+// Prefill, and Asynchronous Overlap"); partials over contiguous token ranges
+// merged by the associative online-softmax reduction (KernelFlume paper,
+// academ.us/article/2606.29207, §3.1, §3.2 and §5.1; the (m, l, O)
+// equations of "Mathematical Formulation of Chunked Attention" on the
+// disaggregated-inference page).
 //
-//  1. split_kernel: one wavefront per (sequence, KV head, split-K partition).
-//     The wave keeps the G = Hq/Hkv query rows of its KV head in registers,
-//     walks the partition's 16-token blocks through the block table, and
-//     for each block issues 16-byte K and V loads (one 256-byte row of one
-//     token and head is read by 16 lanes; a load instruction covers 4
-//     tokens), computes the G scores of every token with packed fp16 dot
-//     products accumulated in fp32, and folds them into an fp32 online
-//     softmax (running max m, running sum l, rescaled accumulator).  Every
-//     K/V byte is read once for all G query heads.  The result per
-//     partition is a normalised partial o and its log-sum-exp.
-//  2. merge_kernel: one wavefront per (sequence, query head) combines the
-//     partials of all partitions by log-sum-exp into the fp16 output.
+// Work decomposition.  Each sequence's tokens are cut into units of P tokens
+// (P a multiple of the 16-token block).  The units of all sequences, taken in
+// order, form one stream of U units; work-group w of the persistent grid
+// takes the contiguous run [w*k, (w+1)*k) with k = ceil(U / n_wg), so every
+// work-group gets the same amount of KV whatever the mix of context lengths.
+// A run covers one or a few consecutive token ranges ("segments") of
+// sequences.  Inside a work-group, wave g handles KV head g, so the waves of
+// one group read the same 16-token blocks (all heads of a block are one
+// contiguous 32 KiB frame at Hkv = 8).
 //
-// The math: attention of one decode query over the whole cached K/V, which
-// is memory-bound ("Why prefill and decode are opposite problems" on the
-// page "The signature-dish specialist: vLLM's attention backend"); the paged
-// gather through a block table ("How the backend reads the paged KV", same
-// page; "Physical Memory Block Layout" on the page "Disaggregated Inference
-// Architecture: Paged KV-Cache Tiering, Chunked Prefill, and Asynchronous
-// Overlap"); partials over contiguous token ranges merged by the associative
-// online-softmax reduction (KernelFlume paper, academ.us/article/2606.29207,
-// §3.1, §3.2 and §5.1; the (m, l, O) equations of "Mathematical Formulation
-// of Chunked Attention" on the disaggregated-inference page).
+// Per segment, a wave keeps the G = Hq/Hkv query rows of its KV head as MFMA
+// operands and walks the blocks through the block table:
+//   * K: per block, 4 loads of 16 bytes per lane (each load instruction reads
+//     64 contiguous bytes of all 16 token rows); QK^T of the 16 tokens and G
+//     heads is 4 v_mfma_f32_16x16x32_f16 (fp16 products, fp32 sums);
+//   * softmax: fp32 online softmax with a running max per head; scores are in
+//     base-2 units (the scale is folded with log2(e)); p goes through a
+//     small LDS slot to the lanes that hold V;
+//   * V: per block, 4 loads of 16 bytes per lane (each load instruction reads
+//     4 whole 256-byte token rows); acc += p * v with fp16 -> fp32 fused FMAs.
+// A segment that is a whole sequence writes the final output; otherwise its
+// normalised partial and log-sum-exp go to workspace slot w + b, and the
+// merge kernel combines the slots of each (sequence, query head).
 
 #include <hip/hip_runtime.h>
 
@@ -42,16 +52,17 @@
 
 namespace {
 
-constexpr int kD = 128;             // head dim
-constexpr int kBS = 16;             // tokens per block
+constexpr int kD = 128;               // head dim
+constexpr int kBS = 16;               // tokens per block
 constexpr int kWave = 64;
-constexpr int kWavesPerWG = 4;
-constexpr int kThreads = kWave * kWavesPerWG;
-constexpr int kMaxPartition = 1024;  // 64 block ids: one per lane of the window
+constexpr int kMaxKvHeads = 8;        // one wave per KV head in a work-group
+constexpr int kMaxPartition = 1 << 20;
+constexpr int kHdrInts = 4;           // k, U, n_wg, P, then units_before[b]
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -62,11 +73,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
-                                         0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+// All-reduce over the 16 lanes of a DPP row.
 __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
   x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
@@ -74,26 +84,42 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<0x140>(x);  // row_mirror: other half of the row
   return x;
 }
-
-__device__ __forceinline__ float xor_lanes(float x, int m) {
-  return __shfl_xor(x, m, kWave);
-}
-
-// Sum / max over the four rows of the wave (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float across_rows_sum(float x) {
-  x += xor_lanes(x, 16);
-  x += xor_lanes(x, 32);
-  return x;
-}
-__device__ __forceinline__ float across_rows_max(float x) {
-  x = fmaxf(x, xor_lanes(x, 16));
-  x = fmaxf(x, xor_lanes(x, 32));
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, xor_lanes(x, m));
+// x[l] + x[l ^ 16] and x[l] + x[l ^ 32].  (Once per segment, so a plain
+// shuffle; the gfx950 lane-swap builtins mis-compile here when both of their
+// operands are the same value.)
+__device__ __forceinline__ float add_xor16(float x) { return x + __shfl_xor(x, 16, kWave); }
+__device__ __forceinline__ float add_xor32(float x) { return x + __shfl_xor(x, 32, kWave); }
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
   return x;
+}
+__device__ __forceinline__ int wave_inclusive_scan_i32(int x, int lane) {
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(x, o, kWave);
+    if (lane >= o) x += t;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float uniform_f32(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {  // v_exp_f32; exp2(-inf) = 0
@@ -101,7 +127,7 @@ __device__ __forceinline__ float fast_exp2(float x) {  // v_exp_f32; exp2(-inf) 
 }
 
 // ---------------------------------------------------------------------------
-// split-K partial kernel
+// split kernel
 
 struct SplitParams {
   const _Float16* q;        // [B, Hq, D]
@@ -110,183 +136,322 @@ struct SplitParams {
   const int32_t* bt;        // [B, bt_stride]
   const int32_t* ctx;       // [B]
   long long bt_stride;
-  long long n_units;        // B * max_parts * Hkv
-  long long num_blocks;     // pool rows; block ids are clamped into [0, num_blocks)
-  int max_tokens;           // max_blocks_per_seq * 16; longer contexts are clamped
+  long long num_blocks;     // block ids are clamped into [0, num_blocks)
   int B, Hq, Hkv;
-  int P;                    // partition length, tokens
-  int max_parts;
+  int max_tokens;           // max_blocks_per_seq * 16; longer contexts are clamped
+  int P;                    // unit length in tokens
+  int n_wg;                 // persistent grid size
   float qk_scale;           // scale * log2(e): scores in base-2 units
-  float* ws_o;              // [B, max_parts, Hq, D]
-  float* ws_lse;            // [B, max_parts, Hq], natural log
+  float* ws_o;              // [n_wg + B, Hq, D] normalised partials
+  float* ws_lse;            // [n_wg + B, Hq] natural-log lse of each partial
+  int32_t* ws_hdr;          // [4 + B]: k, U, n_wg, P, units before sequence b
+  void* out;                // final output of whole-sequence segments
+  float* lse_out;           // may be null
+  int out_f16;              // out is fp16 (else fp32)
 };
 
+__device__ __forceinline__ int seq_len(const SplitParams& p, int b) {
+  return min(max(p.ctx[b], 0), p.max_tokens);
+}
+
+// Per-wave state of one segment for KV head g and its G query heads.
 template <int G>
-struct WaveState {
-  float m[G];               // running max, base-2 units; uniform over the wave
-  float l[G];               // running sum over this lane's row of tokens
-  float acc[G][8];          // running output of d = 8*ds .. 8*ds+7, this row
+struct Seg {
+  float m[G];               // running max per head (base 2), uniform
+  float lp[4];              // running sum of p of this lane's token slot, heads 4c+r
+  float acc[G][8];          // output dims 8*ds .. 8*ds+7 over this lane's token row
 };
 
-// Fold one 16-token block into the running state.  Lane (tg, ds) holds, for
-// i = 0..3, token 4i+tg of the block, dims 8ds..8ds+7, of K (kr) and V (vr).
-// kMasked: only tokens < nvalid of this block exist.
 template <int G, bool kMasked>
-__device__ __forceinline__ void fold_block(WaveState<G>& st, const u32x4 (&qv)[G],
-                                           const u32x4 (&kr)[4], const u32x4 (&vr)[4],
-                                           float qk_scale, int tg, int nvalid) {
-  float s[G][4];
+__device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4], const u32x4 (&kr)[4],
+                                           const u32x4 (&vr)[4], float* lds_p, float qk_scale,
+                                           int lane, int nvalid) {
+  const int t = lane & 15;        // MFMA column: token of the block
+  const int c = lane >> 4;        // MFMA row group: heads 4c .. 4c+3
+  const int tg = lane >> 4;       // V layout: token row 4i + tg
+
+  // scores: D[head][token] = sum_d q[head][d] k[token][d]
+  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2_t* kh = reinterpret_cast<const half2_t*>(&kr[i]);
+  for (int i = 0; i < 4; ++i)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(half8_t, kr[i]), sc, 0,
+                                                0, 0);
+  constexpr int kR = G < 4 ? G : 4;   // score registers that hold real heads
+  float s[kR];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    s[r] = sc[r] * qk_scale;
+    if (kMasked && t >= nvalid) s[r] = -INFINITY;
+  }
+
+  // block max of every head, uniform over the wave
+  float mb[G];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const float x = row16_max(s[r]);
+#pragma unroll
+    for (int cc = 0; cc * 4 + r < G; ++cc) mb[cc * 4 + r] = uniform_f32(x, 16 * cc);
+  }
+  bool grow = false;
+#pragma unroll
+  for (int j = 0; j < G; ++j) grow |= mb[j] > st.m[j];
+  if (grow) {                       // uniform branch: the running max moved
+    float alpha[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const half2_t* qh = reinterpret_cast<const half2_t*>(&qv[j]);
-      float a = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) a = __builtin_amdgcn_fdot2(qh[c], kh[c], a, false);
-      s[j][i] = row16_sum(a) * qk_scale;
+      const float mn = fmaxf(st.m[j], mb[j]);
+      alpha[j] = fast_exp2(st.m[j] - mn);   // 0 on the first block (m = -inf)
+      st.m[j] = mn;
     }
-  }
-  bool valid[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) valid[i] = !kMasked || (4 * i + tg < nvalid);
-  if (kMasked) {
+    for (int r = 0; r < kR; ++r) {
+      float a = alpha[r];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int cc = 1; cc * 4 + r < G; ++cc) a = c == cc ? alpha[cc * 4 + r] : a;
+      st.lp[r] *= a;
+    }
 #pragma unroll
-      for (int j = 0; j < G; ++j) s[j][i] = valid[i] ? s[j][i] : -INFINITY;
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[j][e] *= alpha[j];
   }
 
-  // online softmax: s becomes p = exp2(s - m_new); acc and l are rescaled
+  // p = exp2(s - m); lane (c, t) owns p of heads 4c + r for token t
+  float pr[kR];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float mx = fmaxf(fmaxf(s[j][0], s[j][1]), fmaxf(s[j][2], s[j][3]));
-    mx = across_rows_max(mx);
-    const float m_new = fmaxf(st.m[j], mx);      // finite: a block has >= 1 token
-    const float alpha = fast_exp2(st.m[j] - m_new);
-    st.m[j] = m_new;
-    float psum = 0.0f;
+  for (int r = 0; r < kR; ++r) {
+    float m = st.m[r];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[j][i] = fast_exp2(s[j][i] - m_new);
-      psum += s[j][i];
-    }
-    st.l[j] = st.l[j] * alpha + psum;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[j][e] *= alpha;
+    for (int cc = 1; cc * 4 + r < G; ++cc) m = c == cc ? st.m[cc * 4 + r] : m;
+    pr[r] = fast_exp2(s[r] - m);
+    st.lp[r] += pr[r];
   }
-
-  // acc += p V; a token that does not exist contributes an exact zero row
-  // (selected, so a NaN in an unused slot cannot leak through 0 * NaN)
+  // hand p to the V layout through LDS: lds_p[token][head]
+  if (4 * c < G) {
+    if constexpr (kR == 4) {
+      *reinterpret_cast<f32x4*>(lds_p + t * G + 4 * c) = f32x4{pr[0], pr[1], pr[2], pr[3]};
+    } else if constexpr (kR == 2) {
+      *reinterpret_cast<f32x2*>(lds_p + t * G) = f32x2{pr[0], pr[1]};
+    } else {
+      lds_p[t] = pr[0];
+    }
+  }
+  float pv[4][G];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const float* src = lds_p + (4 * i + tg) * G;
+    if constexpr (G >= 4) {
+#pragma unroll
+      for (int j4 = 0; j4 < G; j4 += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + j4);
+        pv[i][j4] = x[0];
+        pv[i][j4 + 1] = x[1];
+        pv[i][j4 + 2] = x[2];
+        pv[i][j4 + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j) pv[i][j] = src[j];
+    }
+  }
+
+  // acc += p v; a token past the end contributes an exact zero row (selected,
+  // so a NaN in an unused slot cannot leak through 0 * NaN)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool valid = !kMasked || (4 * i + tg < nvalid);
     const _Float16* vh = reinterpret_cast<const _Float16*>(&vr[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = static_cast<float>(vh[e]);
-      if (kMasked) x = valid[i] ? x : 0.0f;
+      if (kMasked) x = valid ? x : 0.0f;
 #pragma unroll
-      for (int j = 0; j < G; ++j) st.acc[j][e] = fmaf(s[j][i], x, st.acc[j][e]);
+      for (int j = 0; j < G; ++j) st.acc[j][e] = fmaf(pv[i][j], x, st.acc[j][e]);
+    }
+  }
+}
+
+// One wave: KV head g of sequence b over tokens [tok_lo, tok_hi).
+template <int G>
+__device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g, int b, int tok_lo,
+                            int tok_hi, bool whole, int slot) {
+  const int c = lane >> 4, t = lane & 15;
+  const int tg = lane >> 4, ds = lane & 15;
+
+  // Q rows as the MFMA A operand: lane (c, t) holds head t, dims 32i + 8c + 0..7
+  half8_t qa[4];
+  {
+    const _Float16* qrow = p.q + ((long long)b * p.Hq + (long long)g * G + t) * kD + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (t < G)
+        qa[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(qrow + 32 * i));
+      else
+        qa[i] = __builtin_bit_cast(half8_t, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  const int row_stride = p.Hkv * kD;                  // elements between tokens of a block
+  const long long block_stride = (long long)kBS * row_stride;
+  // K: lane (c, t) reads token t, dims 32i + 8c; V: lane (tg, ds) reads token 4i + tg, dims 8ds
+  const _Float16* kbase = p.k + (long long)t * row_stride + (long long)g * kD + 8 * c;
+  const _Float16* vbase = p.v + (long long)tg * row_stride + (long long)g * kD + 8 * ds;
+  const int32_t* bt_row = p.bt + (long long)b * p.bt_stride + tok_lo / kBS;
+  const int ntok = tok_hi - tok_lo;
+  const int nblk = (ntok + kBS - 1) / kBS;
+  const int last_valid = ntok - (nblk - 1) * kBS;
+
+  Seg<G> st;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    st.m[j] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st.lp[r] = 0.0f;
+
+  // block-id window: lane i holds the id of block (window base + i)
+  int window = lane < nblk ? bt_row[lane] : 0;
+  auto block_off = [&](int kb) -> long long {
+    if ((kb & 63) == 0 && kb > 0) {                  // next window of 64 ids
+      const int idx = kb + lane;
+      window = idx < nblk ? bt_row[idx] : 0;
+    }
+    // ids outside the pool are clamped: a broken table gives wrong numbers, not a fault
+    const unsigned raw = (unsigned)__builtin_amdgcn_readlane(window, kb & 63);
+    const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
+    return blk * block_stride;
+  };
+  auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+    const _Float16* kp = kbase + off;
+    const _Float16* vp = vbase + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + 32 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + (long long)4 * i * row_stride);
+  };
+  auto fold = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4], int kb) {
+    if (kb == nblk - 1 && last_valid < kBS)
+      fold_block<G, true>(st, qa, kr, vr, lds_p, p.qk_scale, lane, last_valid);
+    else
+      fold_block<G, false>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
+  };
+
+  // two register buffers: block kb+1 is in flight while block kb is folded
+  u32x4 ka[4], va[4], kb2[4], vb2[4];
+  load(block_off(0), ka, va);
+  int kb = 0;
+  while (true) {
+    if (kb + 1 < nblk) load(block_off(kb + 1), kb2, vb2);
+    fold(ka, va, kb);
+    if (++kb == nblk) break;
+    if (kb + 1 < nblk) load(block_off(kb + 1), ka, va);
+    fold(kb2, vb2, kb);
+    if (++kb == nblk) break;
+  }
+
+  // epilogue: totals over token slots and token rows, normalise, store
+  constexpr int kR = G < 4 ? G : 4;
+  float l_tot[G];
+#pragma unroll
+  for (int r = 0; r < kR; ++r) {
+    const float x = row16_sum(st.lp[r]);
+#pragma unroll
+    for (int cc = 0; cc * 4 + r < G; ++cc) l_tot[cc * 4 + r] = uniform_f32(x, 16 * cc);
+  }
+  const int hq0 = g * G;
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = add_xor32(add_xor16(st.acc[j][e]));
+    if ((j & 3) != tg) continue;
+    const float inv = 1.0f / l_tot[j];
+    const float lse = (st.m[j] + __builtin_log2f(l_tot[j])) * kLn2;
+    if (whole) {
+      const long long dst = ((long long)b * p.Hq + hq0 + j) * kD + 8 * ds;
+      if (p.out_f16) {
+        half8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(o[e] * inv);
+        *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = h;
+      } else {
+        float* d = static_cast<float*>(p.out) + dst;
+        *reinterpret_cast<f32x4*>(d) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      }
+      if (p.lse_out && ds == 0) p.lse_out[(long long)b * p.Hq + hq0 + j] = lse;
+    } else {
+      const long long sl = (long long)slot * p.Hq + hq0 + j;
+      float* d = p.ws_o + sl * kD + 8 * ds;
+      *reinterpret_cast<f32x4*>(d) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      if (ds == 0) p.ws_lse[sl] = lse;
     }
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void split_kernel(SplitParams p) {
+__global__ __launch_bounds__(kWave * kMaxKvHeads) void split_kernel(SplitParams p) {
+  __shared__ float lds[kMaxKvHeads][kBS * G];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const long long unit = (long long)blockIdx.x * kWavesPerWG + wave;
-  if (unit >= p.n_units) return;
-  const int g = (int)(unit % p.Hkv);
-  const long long rest = unit / p.Hkv;
-  const int part = (int)(rest % p.max_parts);
-  const int b = (int)(rest / p.max_parts);
-  const int n = min(max(p.ctx[b], 0), p.max_tokens);
-  const int start = part * p.P;
-  if (start >= n) return;                        // empty partition: nothing to write
-  const int ntok = min(p.P, n - start);
-  const int nblk = (ntok + kBS - 1) / kBS;       // <= 64
-  const int tg = lane >> 4;                      // token within a group of 4
-  const int ds = lane & 15;                      // 16-byte slice of the 256-byte row
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // KV head
+  const int w = blockIdx.x;
+  const bool writer = (w == 0 && g == 0);
 
-  // Block-table window of the partition: lane i holds the id of block i.
-  const int32_t* bt_row = p.bt + (long long)b * p.bt_stride + start / kBS;
-  const int my_block = lane < nblk ? bt_row[lane] : 0;
-
-  u32x4 qv[G];
-  const _Float16* qrow = p.q + ((long long)b * p.Hq + (long long)g * G) * kD + ds * 8;
-#pragma unroll
-  for (int j = 0; j < G; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + j * kD);
-
-  const int row_stride = p.Hkv * kD;             // elements between tokens in a block
-  const long long block_stride = (long long)kBS * row_stride;
-  const int lane_off = (tg * p.Hkv + g) * kD + ds * 8;
-  const _Float16* kbase = p.k + lane_off;
-  const _Float16* vbase = p.v + lane_off;
-
-  auto load = [&](int kb, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-    // ids outside the pool are clamped: a broken table gives wrong numbers, not a fault
-    const unsigned raw = (unsigned)__builtin_amdgcn_readlane(my_block, kb);
-    const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
-    const _Float16* kp = kbase + blk * block_stride;
-    const _Float16* vp = vbase + blk * block_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + i * 4 * row_stride);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vp + i * 4 * row_stride);
-  };
-
-  WaveState<G> st;
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = -INFINITY;
-    st.l[j] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.0f;
+  // units of sequence b: ceil(len / P); U = total; k = units per work-group
+  int U = 0;
+  for (int b0 = 0; b0 < p.B; b0 += kWave) {
+    const int b = b0 + lane;
+    const int nu = b < p.B ? (seq_len(p, b) + p.P - 1) / p.P : 0;
+    U += wave_sum_i32(nu);
   }
+  const int k = U > 0 ? (U + p.n_wg - 1) / p.n_wg : 1;
+  const int u_lo = w * k;
+  const int u_hi = min(u_lo + k, U);
 
-  const int last_valid = ntok - (nblk - 1) * kBS;  // 1..16 tokens in the last block
-  auto fold_last = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4]) {
-    if (last_valid == kBS)
-      fold_block<G, false>(st, qv, kr, vr, p.qk_scale, tg, kBS);
-    else
-      fold_block<G, true>(st, qv, kr, vr, p.qk_scale, tg, last_valid);
-  };
-
-  // Two register buffers: the next block's loads are in flight while the
-  // current block is folded.
-  u32x4 ka[4], va[4], kb_[4], vb[4];
-  load(0, ka, va);
-  int blk = 0;
-  while (true) {
-    if (blk + 1 < nblk) load(blk + 1, kb_, vb);
-    if (blk == nblk - 1) { fold_last(ka, va); break; }
-    fold_block<G, false>(st, qv, ka, va, p.qk_scale, tg, kBS);
-    ++blk;
-    if (blk + 1 < nblk) load(blk + 1, ka, va);
-    if (blk == nblk - 1) { fold_last(kb_, vb); break; }
-    fold_block<G, false>(st, qv, kb_, vb, p.qk_scale, tg, kBS);
-    ++blk;
-  }
-
-  // Combine the four token rows, normalise, write the partial.
-  const long long slot = ((long long)b * p.max_parts + part) * p.Hq + (long long)g * G;
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const float l = across_rows_sum(st.l[j]);
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = across_rows_sum(st.acc[j][e]);
-    if ((j & 3) == tg) {
-      const float inv = 1.0f / l;
-      float* dst = p.ws_o + (slot + j) * kD + ds * 8;
-      f32x4 lo = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      f32x4 hi = {o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-      *reinterpret_cast<f32x4*>(dst) = lo;
-      *reinterpret_cast<f32x4*>(dst + 4) = hi;
-      if (ds == 0) p.ws_lse[slot + j] = (st.m[j] + __builtin_log2f(l)) * kLn2;
+  // locate the sequence holding unit u_lo; work-group 0 records the schedule
+  int b_start = -1, before_start = 0, carry = 0;
+  for (int b0 = 0; b0 < p.B; b0 += kWave) {
+    const int b = b0 + lane;
+    const int nu = b < p.B ? (seq_len(p, b) + p.P - 1) / p.P : 0;
+    const int incl = carry + wave_inclusive_scan_i32(nu, lane);
+    const int excl = incl - nu;
+    if (writer && b < p.B) p.ws_hdr[kHdrInts + b] = excl;
+    const unsigned long long hit = __ballot(b < p.B && excl <= u_lo && u_lo < incl);
+    if (b_start < 0 && hit) {
+      const int idx = __builtin_ctzll(hit);
+      b_start = b0 + idx;
+      before_start = __builtin_amdgcn_readlane(excl, idx);
     }
+    carry = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (b_start >= 0 && !writer) break;
+  }
+  if (writer && lane == 0) {
+    p.ws_hdr[0] = k;
+    p.ws_hdr[1] = U;
+    p.ws_hdr[2] = p.n_wg;
+    p.ws_hdr[3] = p.P;
+  }
+  if (u_lo >= u_hi || b_start < 0) return;
+
+  float* lds_p = lds[g];
+  int u = u_lo, b = b_start, before = before_start;
+  while (u < u_hi && b < p.B) {
+    const int n = seq_len(p, b);
+    const int nu = (n + p.P - 1) / p.P;
+    const int p_lo = u - before;
+    const int p_hi = min(u_hi - before, nu);
+    if (p_hi > p_lo) {
+      const int tok_lo = p_lo * p.P;
+      const int tok_hi = min(p_hi * p.P, n);
+      run_segment<G>(p, lds_p, lane, g, b, tok_lo, tok_hi, p_lo == 0 && p_hi == nu, w + b);
+      u = before + p_hi;
+    }
+    before += nu;
+    ++b;
   }
 }
 
@@ -294,57 +459,95 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitParams p) {
 // log-sum-exp merge
 
 struct MergeParams {
-  const float* o;          // partial r of (b, h): o + ((b*sb + r*sr) * Hq + h) * D
-  const float* lse;        // lse + (b*sb + r*sr) * Hq + h
-  long long sb, sr;
-  const int32_t* ctx;      // non-null: sequence b has ceil(ctx[b] / P) partials
-  int P;
-  int max_parts;           // partials per sequence at most (with ctx)
-  int R;                   // used when ctx is null
+  // partial s (0 <= s < nseg) of (b, h): o + (slot * Hq + h) * D, lse + slot * Hq + h
+  const float* o;
+  const float* lse;
+  const int32_t* hdr;      // non-null: the split kernel's schedule (slot = w0 + s + b)
+  const int32_t* ctx;      // with hdr
+  int max_tokens;
+  int R;                   // without hdr: slot = s * B + b, nseg = R
   int B, Hq;
-  void* out;               // fp16 [B, Hq, D] or fp32 [B, Hq, D]
+  void* out;               // fp16 or fp32 [B, Hq, D]
   float* lse_out;          // [B, Hq] or null
+  int out_f16;
 };
 
-template <bool kOutF16>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const long long unit = (long long)blockIdx.x * kWavesPerWG + wave;
+  const long long unit = (long long)blockIdx.x * 4 + wave;
   if (unit >= (long long)p.B * p.Hq) return;
   const int b = (int)(unit / p.Hq);
   const int h = (int)(unit % p.Hq);
-  const int nparts =
-      p.ctx ? min((max(p.ctx[b], 0) + p.P - 1) / p.P, p.max_parts) : p.R;
 
-  const float* lse_b = p.lse + (long long)b * p.sb * p.Hq + h;
-  const float* o_b = p.o + ((long long)b * p.sb * p.Hq + h) * kD + 2 * lane;
-  const long long lse_step = p.sr * p.Hq;
-  const long long o_step = p.sr * p.Hq * kD;
+  long long slot0, slot_step;
+  int nseg;
+  if (p.hdr) {
+    const int k = p.hdr[0], P = p.hdr[3];
+    const int n = min(max(p.ctx[b], 0), p.max_tokens);
+    const int nu = (n + P - 1) / P;
+    const int before = p.hdr[kHdrInts + b];
+    if (nu > 0) {
+      const int w0 = before / k, w1 = (before + nu - 1) / k;
+      nseg = w1 - w0 + 1;
+      if (nseg == 1) return;                 // written by the split kernel
+      slot0 = (long long)w0 + b;
+    } else {
+      nseg = 0;
+      slot0 = 0;
+    }
+    slot_step = 1;
+  } else {
+    nseg = p.R;
+    slot0 = b;
+    slot_step = p.B;
+  }
 
+  // pass 1: the largest lse; pass 2: weights (one partial per lane) and sums
   float L = -INFINITY;
-  for (int r = lane; r < nparts; r += kWave) L = fmaxf(L, lse_b[r * lse_step]);
-  L = wave_max(L);
-
+  for (int s = lane; s < nseg; s += kWave)
+    L = fmaxf(L, p.lse[(slot0 + s * slot_step) * p.Hq + h]);
+  L = wave_max_f32(L);
   f32x2 res = {0.0f, 0.0f};
   float lse_res = -INFINITY;
   if (L != -INFINITY) {
     float wsum = 0.0f;
     f32x2 acc = {0.0f, 0.0f};
-    for (int r = 0; r < nparts; ++r) {
-      const float w = fast_exp2((lse_b[r * lse_step] - L) * kLog2e);  // 0 for -inf
-      const f32x2 o = *reinterpret_cast<const f32x2*>(o_b + r * o_step);
-      wsum += w;
-      acc.x = fmaf(w, o.x, acc.x);
-      acc.y = fmaf(w, o.y, acc.y);
+    const long long ostep = slot_step * p.Hq * kD;
+    for (int s0 = 0; s0 < nseg; s0 += kWave) {
+      const int s = s0 + lane;
+      const float wl =
+          s < nseg ? fast_exp2((p.lse[(slot0 + s * slot_step) * p.Hq + h] - L) * kLog2e) : 0.0f;
+      wsum += wl;
+      const int cnt = min(kWave, nseg - s0);
+      const float* ob = p.o + ((slot0 + (long long)s0 * slot_step) * p.Hq + h) * kD + 2 * lane;
+      int j = 0;
+      for (; j + 8 <= cnt; j += 8) {
+        f32x2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x2*>(ob + (j + u) * ostep);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = uniform_f32(wl, j + u);
+          acc.x = fmaf(wj, v[u].x, acc.x);
+          acc.y = fmaf(wj, v[u].y, acc.y);
+        }
+      }
+      for (; j < cnt; ++j) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(ob + j * ostep);
+        const float wj = uniform_f32(wl, j);
+        acc.x = fmaf(wj, v.x, acc.x);
+        acc.y = fmaf(wj, v.y, acc.y);
+      }
     }
+    wsum = wave_sum_f32(wsum);
     const float inv = 1.0f / wsum;
     res.x = acc.x * inv;
     res.y = acc.y * inv;
     lse_res = L + __builtin_logf(wsum);
   }
   const long long dst = ((long long)b * p.Hq + h) * kD + 2 * lane;
-  if (kOutF16) {
+  if (p.out_f16) {
     half2_t hv = {static_cast<_Float16>(res.x), static_cast<_Float16>(res.y)};
     *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
   } else {
@@ -373,47 +576,61 @@ int ok() {
   return PDA_OK;
 }
 
+// Per-device launch facts, filled once: CU count and how many split-kernel
+// work-groups of each (G, Hkv) shape fit on one CU.
 constexpr int kMaxDevices = 64;
-std::once_flag g_cu_once[kMaxDevices];
-int g_cu_count[kMaxDevices];
+struct DeviceFacts {
+  std::once_flag once;
+  int cus = 0;
+  int wg_per_cu[4][kMaxKvHeads + 1] = {};   // [log2 G][Hkv]
+};
+DeviceFacts g_dev[kMaxDevices];
 
-int cu_count(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return 256;
-  std::call_once(g_cu_once[dev], [dev] {
+int log2_group(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
+
+const void* split_kernel_ptr(int G) {
+  switch (G) {
+    case 1: return reinterpret_cast<const void*>(&split_kernel<1>);
+    case 2: return reinterpret_cast<const void*>(&split_kernel<2>);
+    case 4: return reinterpret_cast<const void*>(&split_kernel<4>);
+    default: return reinterpret_cast<const void*>(&split_kernel<8>);
+  }
+}
+
+// Persistent grid size for (G, Hkv) on the current device.
+int grid_size(int G, int Hkv) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 256 * 2;                 // no device: a fixed size keeps sizing queries usable
+  DeviceFacts& f = g_dev[dev];
+  std::call_once(f.once, [&f, dev] {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    g_cu_count[dev] = cus;
+    f.cus = cus;
+    for (int lg = 0; lg < 4; ++lg)
+      for (int hkv = 1; hkv <= kMaxKvHeads; ++hkv) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg),
+                                                         hkv * kWave, 0) != hipSuccess ||
+            n <= 0)
+          n = 1;
+        f.wg_per_cu[lg][hkv] = n;
+      }
   });
-  return g_cu_count[dev];
+  return f.cus * f.wg_per_cu[log2_group(G)][Hkv];
 }
-
-int current_cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  return cu_count(dev);
-}
-
-struct Plan {
-  int P = 0;
-  int max_parts = 0;
-  int max_tokens = 0;
-  size_t o_bytes = 0, lse_bytes = 0, o_offset = 0, lse_offset = 0, total = 0;
-};
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Partition length: the requested one, or 512 tokens shrunk (down to 128)
-// until the launch has at least ~16 waves per CU of work.
-int pick_partition(int B, int Hkv, int max_blocks, int requested, int cus) {
-  if (requested > 0) return requested;
-  const long long max_tokens = (long long)max_blocks * kBS;
-  int P = 512;
-  auto units = [&](int P) { return (long long)B * Hkv * ((max_tokens + P - 1) / P); };
-  while (P > 128 && units(P) < 16LL * cus) P /= 2;
-  return P;
-}
+struct Plan {
+  int P = 0;                 // unit length in tokens
+  int n_wg = 0;
+  int max_tokens = 0;
+  int n_slots = 0;
+  size_t hdr_offset = 0, lse_offset = 0, o_offset = 0, total = 0;
+};
 
 int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, int partition_tokens) {
   if (B < 0) return fail(PDA_EINVAL, "B must be >= 0 (got %d)", B);
@@ -422,10 +639,14 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built (1, 2, 4, 8 are)", G);
+  if (Hkv > kMaxKvHeads)
+    return fail(PDA_EUNSUPPORTED, "Hkv = %d above the maximum %d", Hkv, kMaxKvHeads);
   if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
   if (block_size != kBS) return fail(PDA_EUNSUPPORTED, "block size %d not built (16 is)", block_size);
   if (max_blocks < 0 || max_blocks > (1 << 26))
     return fail(PDA_EINVAL, "max_blocks_per_seq must be in [0, 2^26] (got %d)", max_blocks);
+  if ((long long)B * max_blocks >= (1LL << 31))
+    return fail(PDA_EUNSUPPORTED, "B * max_blocks_per_seq must stay below 2^31");
   if (partition_tokens < 0 || partition_tokens % kBS != 0)
     return fail(PDA_EINVAL, "partition_tokens (%d) must be 0 or a positive multiple of %d",
                 partition_tokens, kBS);
@@ -435,18 +656,16 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
   return PDA_OK;
 }
 
-Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens, int cus) {
+Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens) {
   Plan pl;
-  pl.P = pick_partition(B, Hkv, max_blocks, partition_tokens, cus);
-  const long long max_tokens = (long long)max_blocks * kBS;
-  pl.max_tokens = (int)max_tokens;
-  pl.max_parts = (int)((max_tokens + pl.P - 1) / pl.P);
-  const size_t slots = (size_t)B * pl.max_parts * Hq;
-  pl.o_bytes = slots * kD * sizeof(float);
-  pl.lse_bytes = slots * sizeof(float);
-  pl.o_offset = 0;
-  pl.lse_offset = align256(pl.o_bytes);
-  pl.total = pl.lse_offset + align256(pl.lse_bytes);
+  pl.P = partition_tokens > 0 ? partition_tokens : kBS;
+  pl.n_wg = grid_size(Hq / Hkv, Hkv);
+  pl.max_tokens = max_blocks * kBS;
+  pl.n_slots = pl.n_wg + B;
+  pl.hdr_offset = 0;
+  pl.lse_offset = align256(sizeof(int32_t) * (kHdrInts + (size_t)B));
+  pl.o_offset = pl.lse_offset + align256(sizeof(float) * (size_t)pl.n_slots * Hq);
+  pl.total = pl.o_offset + align256(sizeof(float) * (size_t)pl.n_slots * Hq * kD);
   return pl;
 }
 
@@ -477,60 +696,6 @@ int debug_validate(const int32_t* bt, long long bt_stride, const int32_t* ctx, i
   return PDA_OK;
 }
 
-int launch_split(const void* q, const void* k_cache, const void* v_cache, const int32_t* bt,
-                 long long bt_stride, const int32_t* ctx, int B, int Hq, int Hkv,
-                 long long num_blocks, float scale,
-                 const Plan& pl, void* workspace, hipStream_t stream) {
-  SplitParams sp;
-  sp.q = static_cast<const _Float16*>(q);
-  sp.k = static_cast<const _Float16*>(k_cache);
-  sp.v = static_cast<const _Float16*>(v_cache);
-  sp.bt = bt;
-  sp.ctx = ctx;
-  sp.bt_stride = bt_stride;
-  sp.B = B;
-  sp.Hq = Hq;
-  sp.Hkv = Hkv;
-  sp.P = pl.P;
-  sp.max_parts = pl.max_parts;
-  sp.n_units = (long long)B * pl.max_parts * Hkv;
-  sp.num_blocks = num_blocks;
-  sp.max_tokens = pl.max_tokens;
-  sp.qk_scale = scale * kLog2e;
-  sp.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.o_offset);
-  sp.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lse_offset);
-  if (sp.n_units == 0) return PDA_OK;
-  const long long grid = (sp.n_units + kWavesPerWG - 1) / kWavesPerWG;
-  if (grid > 0x7fffffffLL) return fail(PDA_EUNSUPPORTED, "launch of %lld work-groups too large", grid);
-  const int G = Hq / Hkv;
-  switch (G) {
-    case 1: hipLaunchKernelGGL(split_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream, sp); break;
-    case 2: hipLaunchKernelGGL(split_kernel<2>, dim3((unsigned)grid), dim3(kThreads), 0, stream, sp); break;
-    case 4: hipLaunchKernelGGL(split_kernel<4>, dim3((unsigned)grid), dim3(kThreads), 0, stream, sp); break;
-    case 8: hipLaunchKernelGGL(split_kernel<8>, dim3((unsigned)grid), dim3(kThreads), 0, stream, sp); break;
-    default: return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built", G);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PDA_EHIP, "split kernel launch: %s", hipGetErrorString(e));
-  return PDA_OK;
-}
-
-int launch_merge(bool out_f16, void* out, float* lse_out, const MergeParams& base, hipStream_t stream) {
-  MergeParams mp = base;
-  mp.out = out;
-  mp.lse_out = lse_out;
-  const long long units = (long long)mp.B * mp.Hq;
-  if (units == 0) return PDA_OK;
-  const long long grid = (units + kWavesPerWG - 1) / kWavesPerWG;
-  if (out_f16)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, mp);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, mp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PDA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
-  return PDA_OK;
-}
-
 // Shared body of paged_decode_attn and paged_decode_attn_partial.
 int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const void* k_cache,
                   const void* v_cache, const int32_t* bt, int64_t bt_stride, const int32_t* ctx,
@@ -547,34 +712,65 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
                 (long long)bt_stride, max_blocks);
   if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
   if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale must be finite");
+  if (!workspace) return fail(PDA_EINVAL, "workspace is null");
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens);
+  if (workspace_bytes < pl.total)
+    return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                pl.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PDA_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, current_cu_count());
-  if (pl.max_parts > 0) {
-    if (!workspace) return fail(PDA_EINVAL, "workspace is null");
-    if (workspace_bytes < pl.total)
-      return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
-                  pl.total);
-    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-      return fail(PDA_EINVAL, "workspace must be 256-byte aligned");
-  }
   rc = debug_validate(bt, bt_stride, ctx, B, num_blocks, max_blocks, stream);
   if (rc != PDA_OK) return rc;
-  rc = launch_split(q, k_cache, v_cache, bt, bt_stride, ctx, B, Hq, Hkv, num_blocks, scale, pl,
-                    workspace, stream);
-  if (rc != PDA_OK) return rc;
+
+  char* ws = static_cast<char*>(workspace);
+  SplitParams sp;
+  sp.q = static_cast<const _Float16*>(q);
+  sp.k = static_cast<const _Float16*>(k_cache);
+  sp.v = static_cast<const _Float16*>(v_cache);
+  sp.bt = bt;
+  sp.ctx = ctx;
+  sp.bt_stride = bt_stride;
+  sp.num_blocks = num_blocks;
+  sp.B = B;
+  sp.Hq = Hq;
+  sp.Hkv = Hkv;
+  sp.max_tokens = pl.max_tokens;
+  sp.P = pl.P;
+  sp.n_wg = pl.n_wg;
+  sp.qk_scale = scale * kLog2e;
+  sp.ws_o = reinterpret_cast<float*>(ws + pl.o_offset);
+  sp.ws_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
+  sp.ws_hdr = reinterpret_cast<int32_t*>(ws + pl.hdr_offset);
+  sp.out = out;
+  sp.lse_out = lse_out;
+  sp.out_f16 = out_f16 ? 1 : 0;
+  const dim3 grid((unsigned)pl.n_wg), block((unsigned)(Hkv * kWave));
+  switch (Hq / Hkv) {
+    case 1: hipLaunchKernelGGL(split_kernel<1>, grid, block, 0, stream, sp); break;
+    case 2: hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, stream, sp); break;
+    case 4: hipLaunchKernelGGL(split_kernel<4>, grid, block, 0, stream, sp); break;
+    default: hipLaunchKernelGGL(split_kernel<8>, grid, block, 0, stream, sp); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PDA_EHIP, "split kernel launch: %s", hipGetErrorString(e));
+
   MergeParams mp{};
-  mp.o = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.o_offset);
-  mp.lse = reinterpret_cast<const float*>(static_cast<char*>(workspace) + pl.lse_offset);
-  mp.sb = pl.max_parts;
-  mp.sr = 1;
+  mp.o = sp.ws_o;
+  mp.lse = sp.ws_lse;
+  mp.hdr = sp.ws_hdr;
   mp.ctx = ctx;
-  mp.P = pl.P;
-  mp.max_parts = pl.max_parts;
+  mp.max_tokens = pl.max_tokens;
   mp.R = 0;
   mp.B = B;
   mp.Hq = Hq;
-  rc = launch_merge(out_f16, out, lse_out, mp, stream);
-  if (rc != PDA_OK) return rc;
+  mp.out = out;
+  mp.lse_out = lse_out;
+  mp.out_f16 = sp.out_f16;
+  const long long units = (long long)B * Hq;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, mp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PDA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -587,22 +783,23 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size, int max_bl
   if (!bytes) return fail(PDA_EINVAL, "bytes is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  *bytes = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, current_cu_count()).total;
+  *bytes = B == 0 ? 0 : make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens).total;
   return ok();
 }
 
 int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
-                         int partition_tokens, size_t* o_offset, size_t* lse_offset,
-                         int* max_parts, int* partition_tokens_out) {
-  if (!o_offset || !lse_offset || !max_parts || !partition_tokens_out)
-    return fail(PDA_EINVAL, "null output pointer");
+                         int partition_tokens, pda_layout* layout) {
+  if (!layout) return fail(PDA_EINVAL, "layout is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, current_cu_count());
-  *o_offset = pl.o_offset;
-  *lse_offset = pl.lse_offset;
-  *max_parts = pl.max_parts;
-  *partition_tokens_out = pl.P;
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens);
+  layout->header_offset = pl.hdr_offset;
+  layout->lse_offset = pl.lse_offset;
+  layout->o_offset = pl.o_offset;
+  layout->total_bytes = pl.total;
+  layout->n_workgroups = pl.n_wg;
+  layout->n_slots = pl.n_slots;
+  layout->unit_tokens = pl.P;
   return ok();
 }
 
@@ -639,20 +836,24 @@ int merge_partials(void* out, float* lse_out, const float* o_parts, const float*
   MergeParams mp{};
   mp.o = o_parts;
   mp.lse = lse_parts;
-  mp.sb = 1;
-  mp.sr = B;
+  mp.hdr = nullptr;
   mp.ctx = nullptr;
-  mp.P = 1;
   mp.R = R;
   mp.B = B;
   mp.Hq = Hq;
-  int rc = launch_merge(true, out, lse_out, mp, static_cast<hipStream_t>(stream));
-  if (rc != PDA_OK) return rc;
+  mp.out = out;
+  mp.lse_out = lse_out;
+  mp.out_f16 = 1;
+  const long long units = (long long)B * Hq;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), mp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PDA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 
 const char* pda_last_error(void) { return t_last_error.c_str(); }
 
-const char* pda_version(void) { return "paged-decode-attn gfx950 0.1"; }
+const char* pda_version(void) { return "paged-decode-attn gfx950 0.2"; }
 
 }  // extern "C"

@@ -36,8 +36,8 @@
  * Asynchronous Overlap"; logical block i holds tokens 16i .. 16i+15 (figure
  * "Virtual Sequence Address Space" on that page).
  *
- * Supported shapes: D = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 8}.
- * Other shapes return PDA_EUNSUPPORTED.
+ * Supported shapes: D = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 8},
+ * Hkv <= 8.  Other shapes return PDA_EUNSUPPORTED.
  *
  * Conventions
  * -----------
@@ -81,40 +81,57 @@ typedef enum {
 
 /*
  * Bytes of device workspace paged_decode_attn and paged_decode_attn_partial
- * need for these sizes (*bytes; 0 is possible).  partition_tokens as in
- * paged_decode_attn (0 = automatic).  The workspace holds, per (sequence,
- * split-K partition, query head), the fp32 partial output and log-sum-exp.
+ * need for these sizes (*bytes; 0 when B == 0).  partition_tokens as in
+ * paged_decode_attn.  The size depends on the device (its CU count sets the
+ * number of work-groups), so query it on the device that will run the call.
  */
 int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size,
                        int max_blocks_per_seq, int partition_tokens,
                        size_t* bytes);
 
+/* Workspace layout of one call shape; see pda_workspace_layout. */
+typedef struct {
+  size_t header_offset; /* int32 [4 + B]: k, U, n_workgroups, unit_tokens,
+                           then the number of units before sequence b     */
+  size_t lse_offset;    /* fp32 [n_slots, Hq]: lse of each stored partial  */
+  size_t o_offset;      /* fp32 [n_slots, Hq, D]: normalised partials      */
+  size_t total_bytes;   /* == pda_workspace_size                           */
+  int n_workgroups;     /* persistent grid of the split kernel             */
+  int n_slots;          /* n_workgroups + B                                */
+  int unit_tokens;      /* P: tokens per unit of the schedule              */
+} pda_layout;
+
 /*
- * Where the per-partition partials live inside the workspace after a call,
- * for inspection by tests: lse of (b, p, h) is the float at byte offset
- * *lse_offset + 4 * ((b * *max_parts + p) * Hq + h), and its normalised
- * output row the D floats at *o_offset + 4 * D * ((b * *max_parts + p) * Hq
- * + h).  *partition_tokens_out receives the partition length that is used.
- * Only partitions p < ceil(context_lens[b] / partition length) are written.
+ * Where the split-K partials live inside the workspace after a call, for
+ * tests and debugging.  The schedule: each sequence's tokens are cut into
+ * units of P = unit_tokens tokens (the last one shorter); the units of all
+ * sequences in order form one stream of U units, and work-group w takes
+ * units [w*k, (w+1)*k), k = ceil(U / n_workgroups).  The tokens of sequence b
+ * that work-group w takes form one contiguous range; unless that range is
+ * the whole sequence (then the final output is written directly), its
+ * partial (o, lse) for query head h is stored in slot w + b at
+ * lse_offset + 4 * ((w + b) * Hq + h) and o_offset + 4 * D * ((w + b) * Hq
+ * + h).  The header records k, U and the units before each sequence.
  */
 int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size,
                          int max_blocks_per_seq, int partition_tokens,
-                         size_t* o_offset, size_t* lse_offset, int* max_parts,
-                         int* partition_tokens_out);
+                         pda_layout* layout);
 
 /*
  * Decode attention over a paged KV cache (see the top of this file).
  *
- * Each sequence's KV is cut into contiguous split-K partitions of
- * partition_tokens tokens (a multiple of block_size, at most 1024; 0 picks a
- * length from the batch shape and the device's CU count).  Partition p of a
- * sequence with n tokens covers tokens [p*P, min((p+1)*P, n)).  A first kernel
- * computes, for every (sequence, KV head, partition), the partial of all Hq /
- * Hkv query heads that share the KV head; a second kernel merges the partials
- * of each (sequence, query head) by log-sum-exp.  Partials over contiguous
- * token ranges and their merge are the attention-node / weight-node split of
- * §3.1 "Kernel-level Disaggregation" and §3.2 "Workflow of Elastic Decoding"
- * in the KernelFlume paper, whose merge equals attention over the full range
+ * Split-K: each sequence's tokens are cut into contiguous units of
+ * partition_tokens tokens (a multiple of block_size; 0 means 16, one block,
+ * the finest balance).  The unit stream of the whole batch is dealt to a
+ * persistent grid sized to the device's CUs in equal contiguous runs, so
+ * every work-group reads the same number of KV bytes whatever the mix of
+ * context lengths.  Within a work-group, one wavefront per KV head computes
+ * the partial of all Hq / Hkv query heads that share that head over each
+ * token range of its run; a sequence split over several work-groups is then
+ * merged by log-sum-exp in a second kernel.  Partials over contiguous token
+ * ranges and their merge are the attention-node / weight-node split of §3.1
+ * "Kernel-level Disaggregation" and §3.2 "Workflow of Elastic Decoding" in
+ * the KernelFlume paper, whose merge equals attention over the full range
  * (§5.1 "Query-First Attention"; the (m, l, O) update equations of
  * "Mathematical Formulation of Chunked Attention" on the
  * disaggregated-inference page).

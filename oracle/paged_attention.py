@@ -61,6 +61,7 @@ __all__ = [
     "merge_partials",
     "partition_ranges",
     "split_k_partials",
+    "balanced_segments",
     "kv_cache_bytes",
     "kv_read_bytes",
 ]
@@ -224,6 +225,40 @@ def partition_ranges(n_tokens, partition_tokens):
     n = int(n_tokens)
     P = int(partition_tokens)
     return [(p * P, min((p + 1) * P, n)) for p in range(-(-n // P))]
+
+
+def balanced_segments(context_lens, unit_tokens, n_workgroups):
+    """The token ranges each work-group of a persistent grid takes.
+
+    Each sequence's tokens are cut into units of ``unit_tokens`` tokens (the
+    last one shorter); the units of all sequences in order form one stream of
+    U units, and work-group w takes units [w*k, (w+1)*k) with
+    k = ceil(U / n_workgroups).  Returns, in stream order, one
+    (w, b, tok_lo, tok_hi) per sequence b that work-group w touches: a
+    contiguous range of that sequence's tokens.
+
+    This is a reading, not a page's formula: the pages only fix that the KV of
+    a sequence is cut into contiguous token ranges computed independently and
+    merged afterwards (KernelFlume paper §3.1, §3.2); sizing the cut so every
+    work-group gets the same number of units is the plainest way to keep a
+    whole GPU busy for any mix of lengths.
+    """
+    P = int(unit_tokens)
+    nu = [-(-int(n) // P) for n in context_lens]
+    U = sum(nu)
+    if U == 0:
+        return []
+    k = -(-U // int(n_workgroups))
+    before = [sum(nu[:b]) for b in range(len(nu))]
+    out = []
+    for w in range(int(n_workgroups)):
+        u_lo, u_hi = w * k, min((w + 1) * k, U)
+        for b, n in enumerate(context_lens):
+            lo = max(u_lo, before[b]) - before[b]
+            hi = min(u_hi, before[b] + nu[b]) - before[b]
+            if hi > lo:
+                out.append((w, b, lo * P, min(hi * P, int(n))))
+    return out
 
 
 def split_k_partials(q, k_pool, v_pool, block_table, context_lens, scale,

@@ -56,7 +56,8 @@ def _ws(B=2, Hq=8, Hkv=2, D=128, bs=16, mb=32, P=0):
     (dict(bs=32), 2),
     (dict(P=24), 1),               # not a multiple of the block size
     (dict(P=-16), 1),
-    (dict(P=2048), 2),             # above the block-table window
+    (dict(P=1 << 21), 2),          # above the largest unit
+    (dict(Hq=32, Hkv=16), 2),      # more KV heads than waves in a work-group
     (dict(B=-1), 1),
     (dict(mb=-1), 1),
     (dict(Hkv=0), 1),
@@ -68,17 +69,19 @@ def test_workspace_size_rejects(lib, kw, code):
 
 
 def test_workspace_size_formula(lib):
-    # explicit partition length: B * ceil(mb*16/P) * Hq slots of D floats + one lse float
+    # header int32[4 + B], lse fp32[n_slots, Hq], o fp32[n_slots, Hq, D], each 256-aligned
     B, Hq, Hkv, mb, P = 3, 32, 8, 100, 256
     rc, n = _ws(B=B, Hq=Hq, Hkv=Hkv, mb=mb, P=P)
     assert rc == 0
-    parts = -(-mb * 16 // P)
-    slots = B * parts * Hq
-    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
-    assert n == align(slots * 128 * 4) + align(slots * 4)
     lay = pda.workspace_layout(B, Hq, Hkv, mb, P)
-    assert lay == {"o_offset": 0, "lse_offset": align(slots * 128 * 4), "max_parts": parts,
-                   "partition_tokens": P}
+    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    slots = lay["n_workgroups"] + B
+    assert lay["n_slots"] == slots and lay["unit_tokens"] == P
+    assert lay["header_offset"] == 0
+    assert lay["lse_offset"] == align(4 * (4 + B))
+    assert lay["o_offset"] == lay["lse_offset"] + align(4 * slots * Hq)
+    assert n == lay["total_bytes"] == lay["o_offset"] + align(4 * slots * Hq * 128)
+    assert pda.workspace_layout(B, Hq, Hkv, mb, 0)["unit_tokens"] == 16
     assert pda.workspace_size(0, Hq, Hkv, mb, P) == 0
 
 

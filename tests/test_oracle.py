@@ -22,6 +22,7 @@ _gather_blocks = O._gather_sequence_blocks
 _merge = O.merge_partials
 _ranges = O.partition_ranges
 _token_location = O.token_location
+_segments = O.balanced_segments
 
 
 def _attend_lse_without_max(q_rows, K, V, scale):
@@ -60,6 +61,9 @@ MUTANTS = {
                            if K.shape[0] > 1 else _attend(q, K, V, scale)),
     "merge_wrong_sign": ("merge_partials", _merge_wrong_sign),
     "merge_unnormalised": ("merge_partials", _merge_unnormalised),
+    "segments_skip_last_unit": ("balanced_segments",
+                                lambda lens, P, n: [(w, b, lo, hi - P if hi - lo > P else hi)
+                                                    for w, b, lo, hi in _segments(lens, P, n)]),
     "partition_end_short": ("partition_ranges",
                             lambda n, P: [(lo, max(lo, hi - 1)) if hi - lo > 1 else (lo, hi)
                                           for lo, hi in _ranges(n, P)]),

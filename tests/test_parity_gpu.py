@@ -51,7 +51,7 @@ def oracle_full(case):
 
 # --- small cases, checked in full ----------------------------------------------
 
-@pytest.mark.parametrize("P", [0, 16, 64, 128, 512, 1024])
+@pytest.mark.parametrize("P", [0, 16, 64, 128, 512, 1024, 4096])
 def test_tiny_workload(P):
     case = W.tiny(device="cuda")
     out, lse = run(case, P)
@@ -143,26 +143,47 @@ def test_bitwise_deterministic():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
-def test_partition_partials_in_workspace():
-    case = W.build_case([1, 63, 64, 65, 200, 777], 8, 2, seed=8, device="cuda")
-    P = 64
-    lay = pda.workspace_layout(case.B, case.Hq, case.Hkv, case.block_table.shape[1], P)
-    ws = torch.zeros(pda.workspace_size(case.B, case.Hq, case.Hkv, case.block_table.shape[1], P),
-                     dtype=torch.uint8, device="cuda")
-    run(case, P, workspace=ws)
-    mp = lay["max_parts"]
+@pytest.mark.parametrize("P", [0, 64, 2048])
+def test_split_partials_in_workspace(P):
+    """Every stored partial equals the oracle's attention over the same token range."""
+    lens = [1, 63, 64, 65, 200, 777, 5000, 9000, 3000]
+    case = W.build_case(lens, 8, 2, seed=8, device="cuda")
+    width = case.block_table.shape[1]
+    lay = pda.workspace_layout(case.B, case.Hq, case.Hkv, width, P)
+    ws = torch.zeros(lay["total_bytes"], dtype=torch.uint8, device="cuda")
+    out, lse = run(case, P, workspace=ws)
     raw = ws.cpu()
-    o_ws = raw[lay["o_offset"]:lay["o_offset"] + 4 * case.B * mp * case.Hq * 128].view(
-        torch.float32).reshape(case.B, mp, case.Hq, 128).numpy()
-    l_ws = raw[lay["lse_offset"]:lay["lse_offset"] + 4 * case.B * mp * case.Hq].view(
-        torch.float32).reshape(case.B, mp, case.Hq).numpy()
-    q, k, v, table, lens = W.host_full(case)
-    o_ref, l_ref = O.split_k_partials(q, k, v, table, lens, case.scale, P)
-    for b, n in enumerate(lens):
-        for p in range(-(-int(n) // P)):
-            compare_lse(l_ws[b, p], l_ref[b, :, p], what=f"lse b={b} p={p}")
-            compare_out(o_ws[b, p], o_ref[b, :, p], abs_tol=1e-4, row_rel_tol=1e-4,
-                        what=f"o b={b} p={p}")
+    nsl, Hq = lay["n_slots"], case.Hq
+    hdr = raw[:4 * (4 + case.B)].view(torch.int32).numpy()
+    l_ws = raw[lay["lse_offset"]:lay["lse_offset"] + 4 * nsl * Hq].view(torch.float32)
+    o_ws = raw[lay["o_offset"]:lay["o_offset"] + 4 * nsl * Hq * 128].view(torch.float32)
+    l_ws = l_ws.reshape(nsl, Hq).numpy()
+    o_ws = o_ws.reshape(nsl, Hq, 128).numpy()
+    segs = O.balanced_segments(lens, lay["unit_tokens"], lay["n_workgroups"])
+    nu = [-(-n // lay["unit_tokens"]) for n in lens]
+    assert hdr[1] == sum(nu) and hdr[2] == lay["n_workgroups"] and hdr[3] == lay["unit_tokens"]
+    assert list(hdr[4:]) == [sum(nu[:b]) for b in range(case.B)]
+    q, k, v, table, ln = W.host_full(case)
+    kv = {}
+    split = 0
+    for w, b, lo, hi in segs:
+        if lo == 0 and hi == lens[b]:
+            continue                               # whole sequence: written to out directly
+        split += 1
+        for g in range(case.Hkv):
+            if (b, g) not in kv:
+                kv[b, g] = (O._gather_sequence_blocks(k, table[b], lens[b], g, 16),
+                            O._gather_sequence_blocks(v, table[b], lens[b], g, 16))
+            K, V = kv[b, g][0][lo:hi], kv[b, g][1][lo:hi]
+            heads = slice(g * 4, g * 4 + 4)
+            o_ref, l_ref = O.attend(q[b, heads], K, V, case.scale)
+            compare_lse(l_ws[w + b, heads], l_ref, what=f"lse w={w} b={b} [{lo},{hi})")
+            compare_out(o_ws[w + b, heads], o_ref, abs_tol=1e-4, row_rel_tol=1e-4,
+                        what=f"o w={w} b={b} [{lo},{hi})")
+    assert split > 0, "the case should split at least one sequence"
+    ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
 
 
 def test_partial_api_and_merge():
@@ -255,15 +276,16 @@ def _sample(lens, rng, k=2):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name", ["llama8b_4k", "agentic_80k", "ragged_mixed"])
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,P", [("llama8b_4k", 0), ("agentic_80k", 512), ("agentic_80k", 0),
+                                    ("ragged_mixed", 0)])
+def test_full_size_workload(name, P):
     case = W.CONFIGS[name](device="cuda")
-    out, lse = run(case, case.partition_tokens)
+    out, lse = run(case, P)
     assert torch.isfinite(out.float()).all()
     ids = _sample(case.lens, np.random.default_rng(0))
     _check_sampled(case, out, lse, ids)
     # a rerun is bitwise identical
-    out2, lse2 = run(case, case.partition_tokens)
+    out2, lse2 = run(case, P)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
     del case
     torch.cuda.empty_cache()
