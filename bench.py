@@ -82,22 +82,29 @@ def cpu_baseline(case, budget_s):
 
 
 def copy_calibration(mib, steps):
-    """A plain copy of known size: each launch reads and writes mib MiB."""
+    """Plain copies of known size, the reference kernels for HBM byte counters.
+
+    Each launch reads and writes ``mib`` MiB: first hipMemcpy's blit kernel
+    (dst.copy_(src)), then an elementwise fp16 kernel (torch.neg into dst).
+    """
     import torch
     n = mib << 20
-    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
-                      "launches": steps + 2, "ms_per_copy": round(dt * 1e3, 4),
-                      "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+    res = {"bytes_read_per_launch": n, "bytes_written_per_launch": n}
+    for name, fn in (("blit_copy", lambda: dst.copy_(src)),
+                     ("elementwise_neg", lambda: torch.neg(src, out=dst))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        res[name] = {"launches": steps + 2, "ms": round(dt * 1e3, 4),
+                     "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}
+    print(json.dumps(res), flush=True)
 
 
 def main():

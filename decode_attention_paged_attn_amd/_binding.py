@@ -31,7 +31,7 @@ class PdaLayout(ctypes.Structure):
     """pda_layout of include/paged_attn.h."""
     _fields_ = [("header_offset", ctypes.c_size_t), ("lse_offset", ctypes.c_size_t),
                 ("o_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
-                ("n_workgroups", ctypes.c_int), ("n_slots", ctypes.c_int),
+                ("n_runs", ctypes.c_int), ("n_slots", ctypes.c_int),
                 ("unit_tokens", ctypes.c_int)]
 
 

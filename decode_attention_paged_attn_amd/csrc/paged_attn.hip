@@ -14,13 +14,15 @@
 //
 // Work decomposition.  Each sequence's tokens are cut into units of P tokens
 // (P a multiple of the 16-token block).  The units of all sequences, taken in
-// order, form one stream of U units; work-group w of the persistent grid
-// takes the contiguous run [w*k, (w+1)*k) with k = ceil(U / n_wg), so every
-// work-group gets the same amount of KV whatever the mix of context lengths.
-// A run covers one or a few consecutive token ranges ("segments") of
-// sequences.  Inside a work-group, wave g handles KV head g, so the waves of
-// one group read the same 16-token blocks (all heads of a block are one
-// contiguous 32 KiB frame at Hkv = 8).
+// order, form one stream of U units, cut into n_runs equal contiguous runs
+// [w*k, (w+1)*k) with k = ceil(U / n_runs), so every run holds the same
+// amount of KV whatever the mix of context lengths.  A run covers one or a
+// few consecutive token ranges ("segments") of sequences.  The persistent
+// grid has one work-group per (run, head group): a work-group of hg waves
+// handles KV heads [h*hg, (h+1)*hg) of its run, one wave per head, and the
+// work-groups of one run are adjacent in dispatch order, so the waves that
+// read one 16-token block (all KV heads of a block are one contiguous frame)
+// run at about the same time.
 //
 // Per segment, a wave keeps the G = Hq/Hkv query rows of its KV head as MFMA
 // operands and walks the blocks through the block table:
@@ -44,6 +46,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -55,9 +58,14 @@ namespace {
 constexpr int kD = 128;               // head dim
 constexpr int kBS = 16;               // tokens per block
 constexpr int kWave = 64;
-constexpr int kMaxKvHeads = 8;        // one wave per KV head in a work-group
+constexpr int kMaxKvHeads = 8;        // one wave per KV head
+constexpr int kMaxWavesPerWG = 4;     // KV heads of one work-group
+// occupancy target of the split kernel: 2 waves per SIMD with two blocks of
+// K/V in flight per wave measured faster than 3 waves per SIMD squeezed into
+// 168 VGPRs
+constexpr int waves_per_eu(int) { return 2; }
 constexpr int kMaxPartition = 1 << 20;
-constexpr int kHdrInts = 4;           // k, U, n_wg, P, then units_before[b]
+constexpr int kHdrInts = 4;           // k, U, n_runs, P, then units_before[b]
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -140,11 +148,12 @@ struct SplitParams {
   int B, Hq, Hkv;
   int max_tokens;           // max_blocks_per_seq * 16; longer contexts are clamped
   int P;                    // unit length in tokens
-  int n_wg;                 // persistent grid size
+  int n_runs;               // runs of the unit stream (one per work-group and head group)
+  int hg;                   // KV heads (waves) per work-group; Hkv / hg head groups
   float qk_scale;           // scale * log2(e): scores in base-2 units
-  float* ws_o;              // [n_wg + B, Hq, D] normalised partials
-  float* ws_lse;            // [n_wg + B, Hq] natural-log lse of each partial
-  int32_t* ws_hdr;          // [4 + B]: k, U, n_wg, P, units before sequence b
+  float* ws_o;              // [n_runs + B, Hq, D] normalised partials
+  float* ws_lse;            // [n_runs + B, Hq] natural-log lse of each partial
+  int32_t* ws_hdr;          // [4 + B]: k, U, n_runs, P, units before sequence b
   void* out;                // final output of whole-sequence segments
   float* lse_out;           // may be null
   int out_f16;              // out is fp16 (else fp32)
@@ -323,14 +332,18 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
     const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
     return blk * block_stride;
   };
+  // K/V are read once per call: non-temporal loads keep them from displacing
+  // the block table, q and the partials in the caches
   auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
     const _Float16* kp = kbase + off;
     const _Float16* vp = vbase + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + 32 * i);
+    for (int i = 0; i < 4; ++i)
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vp + (long long)4 * i * row_stride);
+      vr[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vp + (long long)4 * i * row_stride));
   };
   auto fold = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
@@ -394,12 +407,16 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
 }
 
 template <int G>
-__global__ __launch_bounds__(kWave * kMaxKvHeads) void split_kernel(SplitParams p) {
-  __shared__ float lds[kMaxKvHeads][kBS * G];
+__global__ __launch_bounds__(kWave * kMaxWavesPerWG)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu(G))))
+void split_kernel(SplitParams p) {
+  __shared__ float lds[kMaxWavesPerWG][kBS * G];
   const int lane = threadIdx.x & (kWave - 1);
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // KV head
-  const int w = blockIdx.x;
-  const bool writer = (w == 0 && g == 0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n_hgroups = p.Hkv / p.hg;
+  const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
+  const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
+  const bool writer = (blockIdx.x == 0 && wave == 0);
 
   // units of sequence b: ceil(len / P); U = total; k = units per work-group
   int U = 0;
@@ -408,7 +425,7 @@ __global__ __launch_bounds__(kWave * kMaxKvHeads) void split_kernel(SplitParams 
     const int nu = b < p.B ? (seq_len(p, b) + p.P - 1) / p.P : 0;
     U += wave_sum_i32(nu);
   }
-  const int k = U > 0 ? (U + p.n_wg - 1) / p.n_wg : 1;
+  const int k = U > 0 ? (U + p.n_runs - 1) / p.n_runs : 1;
   const int u_lo = w * k;
   const int u_hi = min(u_lo + k, U);
 
@@ -432,12 +449,12 @@ __global__ __launch_bounds__(kWave * kMaxKvHeads) void split_kernel(SplitParams 
   if (writer && lane == 0) {
     p.ws_hdr[0] = k;
     p.ws_hdr[1] = U;
-    p.ws_hdr[2] = p.n_wg;
+    p.ws_hdr[2] = p.n_runs;
     p.ws_hdr[3] = p.P;
   }
   if (u_lo >= u_hi || b_start < 0) return;
 
-  float* lds_p = lds[g];
+  float* lds_p = lds[wave];
   int u = u_lo, b = b_start, before = before_start;
   while (u < u_hi && b < p.B) {
     const int n = seq_len(p, b);
@@ -577,12 +594,12 @@ int ok() {
 }
 
 // Per-device launch facts, filled once: CU count and how many split-kernel
-// work-groups of each (G, Hkv) shape fit on one CU.
+// work-groups of each (G, waves per work-group) shape fit on one CU.
 constexpr int kMaxDevices = 64;
 struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMaxKvHeads + 1] = {};   // [log2 G][Hkv]
+  int wg_per_cu[4][kMaxWavesPerWG + 1] = {};   // [log2 G][waves per work-group]
 };
 DeviceFacts g_dev[kMaxDevices];
 
@@ -597,11 +614,21 @@ const void* split_kernel_ptr(int G) {
   }
 }
 
-// Persistent grid size for (G, Hkv) on the current device.
-int grid_size(int G, int Hkv) {
+// KV heads (waves) per work-group: the largest divisor of Hkv up to 4.
+int head_group(int Hkv) {
+  for (int hg = kMaxWavesPerWG; hg > 1; --hg)
+    if (Hkv % hg == 0) return hg;
+  return 1;
+}
+
+// Runs of the unit stream for (G, Hkv) on the current device: as many
+// work-groups as fit on all CUs at once, divided by the head groups per run.
+int run_count(int G, int Hkv) {
+  const int hg = head_group(Hkv);
+  const int n_hgroups = Hkv / hg;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return 256 * 2;                 // no device: a fixed size keeps sizing queries usable
+    return 1024 / n_hgroups;        // no device: a fixed size keeps sizing queries usable
   DeviceFacts& f = g_dev[dev];
   std::call_once(f.once, [&f, dev] {
     int cus = 0;
@@ -610,23 +637,24 @@ int grid_size(int G, int Hkv) {
       cus = 256;
     f.cus = cus;
     for (int lg = 0; lg < 4; ++lg)
-      for (int hkv = 1; hkv <= kMaxKvHeads; ++hkv) {
+      for (int w = 1; w <= kMaxWavesPerWG; ++w) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg),
-                                                         hkv * kWave, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg), w * kWave,
+                                                         0) != hipSuccess ||
             n <= 0)
           n = 1;
-        f.wg_per_cu[lg][hkv] = n;
+        f.wg_per_cu[lg][w] = n;
       }
   });
-  return f.cus * f.wg_per_cu[log2_group(G)][Hkv];
+  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][hg] / n_hgroups);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plan {
   int P = 0;                 // unit length in tokens
-  int n_wg = 0;
+  int n_runs = 0;
+  int hg = 0;                // waves (KV heads) per work-group
   int max_tokens = 0;
   int n_slots = 0;
   size_t hdr_offset = 0, lse_offset = 0, o_offset = 0, total = 0;
@@ -659,9 +687,10 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
 Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens) {
   Plan pl;
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_wg = grid_size(Hq / Hkv, Hkv);
+  pl.n_runs = run_count(Hq / Hkv, Hkv);
+  pl.hg = head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
-  pl.n_slots = pl.n_wg + B;
+  pl.n_slots = pl.n_runs + B;
   pl.hdr_offset = 0;
   pl.lse_offset = align256(sizeof(int32_t) * (kHdrInts + (size_t)B));
   pl.o_offset = pl.lse_offset + align256(sizeof(float) * (size_t)pl.n_slots * Hq);
@@ -737,7 +766,8 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.Hkv = Hkv;
   sp.max_tokens = pl.max_tokens;
   sp.P = pl.P;
-  sp.n_wg = pl.n_wg;
+  sp.n_runs = pl.n_runs;
+  sp.hg = pl.hg;
   sp.qk_scale = scale * kLog2e;
   sp.ws_o = reinterpret_cast<float*>(ws + pl.o_offset);
   sp.ws_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
@@ -745,7 +775,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.out = out;
   sp.lse_out = lse_out;
   sp.out_f16 = out_f16 ? 1 : 0;
-  const dim3 grid((unsigned)pl.n_wg), block((unsigned)(Hkv * kWave));
+  const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
   switch (Hq / Hkv) {
     case 1: hipLaunchKernelGGL(split_kernel<1>, grid, block, 0, stream, sp); break;
     case 2: hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, stream, sp); break;
@@ -797,7 +827,7 @@ int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size, int max_
   layout->lse_offset = pl.lse_offset;
   layout->o_offset = pl.o_offset;
   layout->total_bytes = pl.total;
-  layout->n_workgroups = pl.n_wg;
+  layout->n_runs = pl.n_runs;
   layout->n_slots = pl.n_slots;
   layout->unit_tokens = pl.P;
   return ok();

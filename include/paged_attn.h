@@ -91,13 +91,13 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size,
 
 /* Workspace layout of one call shape; see pda_workspace_layout. */
 typedef struct {
-  size_t header_offset; /* int32 [4 + B]: k, U, n_workgroups, unit_tokens,
+  size_t header_offset; /* int32 [4 + B]: k, U, n_runs, unit_tokens,
                            then the number of units before sequence b     */
   size_t lse_offset;    /* fp32 [n_slots, Hq]: lse of each stored partial  */
   size_t o_offset;      /* fp32 [n_slots, Hq, D]: normalised partials      */
   size_t total_bytes;   /* == pda_workspace_size                           */
-  int n_workgroups;     /* persistent grid of the split kernel             */
-  int n_slots;          /* n_workgroups + B                                */
+  int n_runs;           /* runs the unit stream is cut into                */
+  int n_slots;          /* n_runs + B                                      */
   int unit_tokens;      /* P: tokens per unit of the schedule              */
 } pda_layout;
 
@@ -105,11 +105,12 @@ typedef struct {
  * Where the split-K partials live inside the workspace after a call, for
  * tests and debugging.  The schedule: each sequence's tokens are cut into
  * units of P = unit_tokens tokens (the last one shorter); the units of all
- * sequences in order form one stream of U units, and work-group w takes
- * units [w*k, (w+1)*k), k = ceil(U / n_workgroups).  The tokens of sequence b
- * that work-group w takes form one contiguous range; unless that range is
- * the whole sequence (then the final output is written directly), its
- * partial (o, lse) for query head h is stored in slot w + b at
+ * sequences in order form one stream of U units, and run w is units
+ * [w*k, (w+1)*k), k = ceil(U / n_runs) (each run is computed by one
+ * work-group per group of up to 4 KV heads).  The tokens of sequence b in
+ * run w form one contiguous range; unless that range is the whole sequence
+ * (then the final output is written directly), its partial (o, lse) for
+ * query head h is stored in slot w + b at
  * lse_offset + 4 * ((w + b) * Hq + h) and o_offset + 4 * D * ((w + b) * Hq
  * + h).  The header records k, U and the units before each sequence.
  */

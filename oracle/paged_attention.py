@@ -227,14 +227,14 @@ def partition_ranges(n_tokens, partition_tokens):
     return [(p * P, min((p + 1) * P, n)) for p in range(-(-n // P))]
 
 
-def balanced_segments(context_lens, unit_tokens, n_workgroups):
-    """The token ranges each work-group of a persistent grid takes.
+def balanced_segments(context_lens, unit_tokens, n_runs):
+    """The token ranges of each run of the unit stream.
 
     Each sequence's tokens are cut into units of ``unit_tokens`` tokens (the
     last one shorter); the units of all sequences in order form one stream of
-    U units, and work-group w takes units [w*k, (w+1)*k) with
-    k = ceil(U / n_workgroups).  Returns, in stream order, one
-    (w, b, tok_lo, tok_hi) per sequence b that work-group w touches: a
+    U units, and run w is units [w*k, (w+1)*k) with
+    k = ceil(U / n_runs).  Returns, in stream order, one
+    (w, b, tok_lo, tok_hi) per sequence b that run w touches: a
     contiguous range of that sequence's tokens.
 
     This is a reading, not a page's formula: the pages only fix that the KV of
@@ -248,10 +248,10 @@ def balanced_segments(context_lens, unit_tokens, n_workgroups):
     U = sum(nu)
     if U == 0:
         return []
-    k = -(-U // int(n_workgroups))
+    k = -(-U // int(n_runs))
     before = [sum(nu[:b]) for b in range(len(nu))]
     out = []
-    for w in range(int(n_workgroups)):
+    for w in range(int(n_runs)):
         u_lo, u_hi = w * k, min((w + 1) * k, U)
         for b, n in enumerate(context_lens):
             lo = max(u_lo, before[b]) - before[b]

@@ -75,7 +75,7 @@ def test_workspace_size_formula(lib):
     assert rc == 0
     lay = pda.workspace_layout(B, Hq, Hkv, mb, P)
     align = lambda x: (x + 255) // 256 * 256   # noqa: E731
-    slots = lay["n_workgroups"] + B
+    slots = lay["n_runs"] + B
     assert lay["n_slots"] == slots and lay["unit_tokens"] == P
     assert lay["header_offset"] == 0
     assert lay["lse_offset"] == align(4 * (4 + B))

@@ -159,9 +159,9 @@ def test_split_partials_in_workspace(P):
     o_ws = raw[lay["o_offset"]:lay["o_offset"] + 4 * nsl * Hq * 128].view(torch.float32)
     l_ws = l_ws.reshape(nsl, Hq).numpy()
     o_ws = o_ws.reshape(nsl, Hq, 128).numpy()
-    segs = O.balanced_segments(lens, lay["unit_tokens"], lay["n_workgroups"])
+    segs = O.balanced_segments(lens, lay["unit_tokens"], lay["n_runs"])
     nu = [-(-n // lay["unit_tokens"]) for n in lens]
-    assert hdr[1] == sum(nu) and hdr[2] == lay["n_workgroups"] and hdr[3] == lay["unit_tokens"]
+    assert hdr[1] == sum(nu) and hdr[2] == lay["n_runs"] and hdr[3] == lay["unit_tokens"]
     assert list(hdr[4:]) == [sum(nu[:b]) for b in range(case.B)]
     q, k, v, table, ln = W.host_full(case)
     kv = {}
