@@ -107,6 +107,90 @@ def copy_calibration(mib, steps):
     print(json.dumps(res), flush=True)
 
 
+def measure(case, P, steps, warmup, flush_mib=0):
+    """Time ``steps`` calls after ``warmup``; wall clock and HIP events on the stream."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    B, Hq, Hkv = case.B, case.Hq, case.Hkv
+    width = case.block_table.shape[1]
+    ws = torch.empty(max(pda.workspace_size(B, Hq, Hkv, width, P), 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    unit = pda.workspace_layout(B, Hq, Hkv, width, P)["unit_tokens"]
+    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda") if flush_mib else None
+
+    def step():
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                              case.context_lens, case.scale, out=out, lse_out=lse,
+                              partition_tokens=P, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)      # evicts K/V from the last-level cache between calls
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ev_mean = sum(ev_ms) / len(ev_ms)
+    nbytes = kv_bytes(case.lens, Hkv)
+    ms_per_step = wall / steps * 1e3
+    return {
+        "kv_bytes": nbytes,
+        "unit_tokens": unit,
+        "ms_per_step": round(ms_per_step, 5),
+        "value": round(nbytes / (ms_per_step / 1e3) / 1e9, 2),
+        "achieved": round(nbytes / (ev_mean / 1e3) / 1e9, 2),
+        "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "event_ms": {"mean": round(ev_mean, 5), "p10": round(ev_ms[len(ev_ms) // 10], 5),
+                     "p50": round(ev_ms[len(ev_ms) // 2], 5),
+                     "p90": round(ev_ms[(9 * len(ev_ms)) // 10], 5)},
+    }
+
+
+def bench_append(case, steps, warmup):
+    """Time paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16)."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    g = torch.Generator(device="cuda").manual_seed(1)
+    kn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
+    vn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
+
+    def step():
+        pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table,
+                            case.context_lens)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / steps * 1e3
+    ev_ms = e0.elapsed_time(e1) / steps
+    nbytes = 2 * 2 * case.B * case.Hkv * 128 * 2          # K and V rows, read + write
+    print(json.dumps({"metric": "KV append GB/s", "op": "paged_kv_append", "unit": "GB/s",
+                      "value": round(nbytes / (wall_ms / 1e3) / 1e9, 2),
+                      "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+                      "us_per_call_events": round(ev_ms * 1e3, 3), "bytes_per_call": nbytes,
+                      "steps": steps, "config": {"workload": case.name, "batch": case.B,
+                                                 "kv_heads": case.Hkv}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +200,14 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also", default="llama8b_4k",
+                    help="comma-separated extra workloads reported under 'also'")
+    ap.add_argument("--op", default="attention", choices=["attention", "append"],
+                    help="attention (default): paged_decode_attn; append: paged_kv_append of "
+                         "one token per sequence")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB of scratch between timed calls (outside the "
+                         "event pair; the wall clock includes it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: time a plain device copy of MIB MiB (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -138,50 +230,22 @@ def main():
         return
     pda.load_library()
     case = W.CONFIGS[args.config](device="cuda")
+    if args.op == "append":
+        bench_append(case, args.steps, args.warmup)
+        return
     P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    m = measure(case, P, args.steps, args.warmup, args.flush_mib)
+    nbytes = m["kv_bytes"]
     B, Hq, Hkv = case.B, case.Hq, case.Hkv
-    width = case.block_table.shape[1]
-    ws = torch.empty(max(pda.workspace_size(B, Hq, Hkv, width, P), 1), dtype=torch.uint8,
-                     device="cuda")
-    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    used_P = pda.workspace_layout(B, Hq, Hkv, width, P)["unit_tokens"]
-
-    def step():
-        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
-                              case.context_lens, case.scale, out=out, lse_out=lse,
-                              partition_tokens=P, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    ev_mean = sum(ev_ms) / len(ev_ms)
-
-    nbytes = kv_bytes(case.lens, Hkv)
-    ms_per_step = wall / args.steps * 1e3
-    value = nbytes / (ms_per_step / 1e3) / 1e9
-    achieved = nbytes / (ev_mean / 1e3) / 1e9
     traffic = measured_traffic(args.config)
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": m["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -190,27 +254,43 @@ def main():
         "config": {
             "workload": case.name,
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "block_size": 16,
-            "partition_tokens": used_P, "tokens": int(case.lens.sum()),
+            "partition_tokens": m["unit_tokens"], "tokens": int(case.lens.sum()),
             "min_ctx": int(case.lens.min()), "max_ctx": int(case.lens.max()),
             "kv_bytes_per_step": nbytes, "seed": case.seed,
         },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "decode_attn_tokens_per_s": round(B / (ms_per_step / 1e3), 1),
-        "attn_only_tokens_per_s_32_layer_step": round(B / (32 * ms_per_step / 1e3), 1),
-        "event_ms": {"mean": round(ev_mean, 5), "p10": round(ev_ms[len(ev_ms) // 10], 5),
-                     "p50": round(ev_ms[len(ev_ms) // 2], 5),
-                     "p90": round(ev_ms[(9 * len(ev_ms)) // 10], 5)},
+        "pct_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBS, 2),
+        "decode_attn_tokens_per_s": m["tokens_per_s"],
+        "attn_only_tokens_per_s_32_layer_step": round(m["tokens_per_s"] / 32, 1),
+        "event_ms": m["event_ms"],
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_attn call (split_kernel + merge_kernel)",
-            "achieved": round(achieved, 2),
+            "achieved": m["achieved"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(m["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
         },
         "kernel_source_sha256_16": source_hash(),
     }
+    if args.flush_mib:
+        rec["flush_mib_between_steps"] = args.flush_mib
+    also = {}
+    for name in [x for x in args.also.split(",") if x and x != args.config]:
+        del case
+        torch.cuda.empty_cache()
+        case = W.CONFIGS[name](device="cuda")
+        mm = measure(case, case.partition_tokens, args.steps, args.warmup, args.flush_mib)
+        also[case.name] = {"value": mm["value"], "unit": "GB/s",
+                           "pct_hbm_peak": round(100.0 * mm["value"] / HBM_PEAK_GBS, 2),
+                           "event_GBps": mm["achieved"], "ms_per_step": mm["ms_per_step"],
+                           "decode_attn_tokens_per_s": mm["tokens_per_s"],
+                           "kv_bytes_per_step": mm["kv_bytes"]}
+    if also:
+        rec["also"] = also
+        del case
+        torch.cuda.empty_cache()
+        case = W.CONFIGS[args.config](device="cuda")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     merge_partials,
     paged_decode_attn,
     paged_decode_attn_partial,
+    paged_kv_append,
     workspace_layout,
     workspace_size,
 )
@@ -23,6 +24,7 @@ __all__ = [
     "merge_partials",
     "paged_decode_attn",
     "paged_decode_attn_partial",
+    "paged_kv_append",
     "workspace_layout",
     "workspace_size",
 ]

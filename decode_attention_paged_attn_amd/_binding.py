@@ -48,6 +48,8 @@ _SIGNATURES = {
                                            _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                                            _c_float, _c_int, _vp, _c_size, _vp]),
     "merge_partials": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "paged_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
+                                 _c_int, _c_i64, _c_int, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -100,12 +102,21 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+_ws_cache = {}
+
+
 def workspace_size(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
-                   block_size=BLOCK_SIZE):
-    n = _c_size(0)
-    _check(load_library().pda_workspace_size(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
-                                             partition_tokens, ctypes.byref(n)))
-    return int(n.value)
+                   block_size=BLOCK_SIZE, device=None):
+    """Bytes of workspace for this call shape on the current (or given) device."""
+    dev = torch.cuda.current_device() if device is None and torch.cuda.is_available() else device
+    key = (B, Hq, Hkv, max_blocks_per_seq, partition_tokens, D, block_size, dev)
+    n = _ws_cache.get(key)
+    if n is None:
+        c = _c_size(0)
+        _check(load_library().pda_workspace_size(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
+                                                 partition_tokens, ctypes.byref(c)))
+        n = _ws_cache[key] = int(c.value)
+    return n
 
 
 def workspace_layout(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
@@ -153,7 +164,7 @@ def _run(partial, q, k_cache, v_cache, block_table, context_lens, scale, out, ls
     if mb > width:
         raise ValueError("max_blocks_per_seq exceeds the block table width")
     bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
-    ws_bytes = workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs)
+    ws_bytes = workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs, dev.index)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < ws_bytes:
@@ -225,3 +236,23 @@ def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
     _check(load_library().merge_partials(_ptr(out), _ptr(lse_out), _ptr(o_parts),
                                          _ptr(lse_parts), R, B, Hq, D, _stream(dev)))
     return (out, lse_out) if return_lse else out
+
+
+def paged_kv_append(k_cache, v_cache, k_new, v_new, block_table, context_lens,
+                    max_blocks_per_seq=None):
+    """Write token ctx_b - 1 of every sequence (k_new, v_new: fp16 [B, Hkv, D]) in place."""
+    dev = _check_inputs(k_new, k_cache, v_cache, block_table, context_lens)
+    B = k_new.shape[0]
+    num_blocks, bs, Hkv, D = k_cache.shape
+    if (k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or k_new.dtype != torch.float16
+            or v_new.dtype != torch.float16 or not k_new.is_contiguous()
+            or not v_new.is_contiguous() or k_new.device != dev or v_new.device != dev):
+        raise ValueError("k_new and v_new must be contiguous fp16 [B, Hkv, D] on the caches' GPU")
+    width = block_table.shape[1]
+    mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    if mb > width:
+        raise ValueError("max_blocks_per_seq exceeds the block table width")
+    bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
+    _check(load_library().paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                          _ptr(block_table), bt_stride, _ptr(context_lens), B,
+                                          Hkv, D, bs, num_blocks, mb, _stream(dev)))

@@ -574,6 +574,40 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// KV append: the newest token of each sequence into its tail slot
+
+struct AppendParams {
+  _Float16* k;              // [num_blocks, 16, Hkv, D], written in place
+  _Float16* v;
+  const _Float16* kn;       // [B, Hkv, D]
+  const _Float16* vn;
+  const int32_t* bt;
+  const int32_t* ctx;       // counts the new token
+  long long bt_stride;
+  long long num_blocks;
+  int B, Hkv;
+  int max_tokens;
+};
+
+// One thread per 16-byte chunk of the Hkv * D row of K and of V.
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int chunks = p.Hkv * (kD / 8);
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)p.B * chunks) return;
+  const int b = (int)(i / chunks);
+  const int c = (int)(i % chunks);
+  const int n = p.ctx[b];
+  if (n <= 0 || n > p.max_tokens) return;           // nothing to append / outside the table
+  const int t = n - 1;
+  const unsigned frame = (unsigned)p.bt[(long long)b * p.bt_stride + t / kBS];
+  if (frame >= (unsigned long long)p.num_blocks) return;
+  const long long dst = ((long long)frame * kBS + t % kBS) * p.Hkv * kD + (long long)c * 8;
+  const long long src = (long long)b * p.Hkv * kD + (long long)c * 8;
+  *reinterpret_cast<u32x4*>(p.k + dst) = *reinterpret_cast<const u32x4*>(p.kn + src);
+  *reinterpret_cast<u32x4*>(p.v + dst) = *reinterpret_cast<const u32x4*>(p.vn + src);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 
 thread_local std::string t_last_error;
@@ -879,6 +913,42 @@ int merge_partials(void* out, float* lse_out, const float* o_parts, const float*
                      static_cast<hipStream_t>(stream), mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PDA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* context_lens, int B, int Hkv, int D, int block_size,
+                    int64_t num_blocks, int max_blocks_per_seq, void* stream) {
+  if (B < 0 || Hkv <= 0) return fail(PDA_EINVAL, "B must be >= 0 and Hkv > 0");
+  if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
+  if (block_size != kBS) return fail(PDA_EUNSUPPORTED, "block size %d not built (16 is)", block_size);
+  if (max_blocks_per_seq < 0 || max_blocks_per_seq > (1 << 26))
+    return fail(PDA_EINVAL, "max_blocks_per_seq must be in [0, 2^26]");
+  if (B == 0 || max_blocks_per_seq == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_table || !context_lens)
+    return fail(PDA_EINVAL, "null pointer");
+  if (block_table_stride < max_blocks_per_seq)
+    return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
+                (long long)block_table_stride, max_blocks_per_seq);
+  if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
+  AppendParams ap;
+  ap.k = static_cast<_Float16*>(k_cache);
+  ap.v = static_cast<_Float16*>(v_cache);
+  ap.kn = static_cast<const _Float16*>(k_new);
+  ap.vn = static_cast<const _Float16*>(v_new);
+  ap.bt = block_table;
+  ap.ctx = context_lens;
+  ap.bt_stride = block_table_stride;
+  ap.num_blocks = num_blocks;
+  ap.B = B;
+  ap.Hkv = Hkv;
+  ap.max_tokens = max_blocks_per_seq * kBS;
+  const long long threads = (long long)B * Hkv * (kD / 8);
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), ap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PDA_EHIP, "append kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -196,6 +196,28 @@ int merge_partials(void* out, float* lse_out, const float* o_parts,
                    const float* lse_parts, int R, int B, int Hq, int D,
                    void* stream);
 
+/*
+ * KV append: write the newest token's key and value of every sequence into
+ * its paged cache, in place, before attending.  The tail node appends
+ * (K_new, V_new) and then attends over the updated range (KernelFlume paper
+ * §3.2 "Workflow of Elastic Decoding", §5.1 "Query-First Attention").
+ *
+ * k_new, v_new   fp16 [B, Hkv, D].
+ * context_lens   counts the new token: sequence b writes token t = ctx_b - 1,
+ *                i.e. row (frame = block_table[b, t / block_size],
+ *                slot = t % block_size) of both pools, all Hkv heads.
+ *                ctx_b <= 0 writes nothing; the block holding token t must
+ *                already be in the table (allocating blocks is the caller's).
+ * Sequences must own distinct tail slots (each sequence's own last block).
+ * A block id outside [0, num_blocks) or ctx_b > max_blocks_per_seq *
+ * block_size skips that sequence.  D must be 128 and block_size 16.
+ */
+int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
+                    const void* v_new, const int32_t* block_table,
+                    int64_t block_table_stride, const int32_t* context_lens,
+                    int B, int Hkv, int D, int block_size, int64_t num_blocks,
+                    int max_blocks_per_seq, void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pda_last_error(void);
 

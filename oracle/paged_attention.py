@@ -62,6 +62,7 @@ __all__ = [
     "partition_ranges",
     "split_k_partials",
     "balanced_segments",
+    "kv_append",
     "kv_cache_bytes",
     "kv_read_bytes",
 ]
@@ -287,6 +288,29 @@ def split_k_partials(q, k_pool, v_pool, block_table, context_lens, scale,
                 op, lp = attend(q[b, h:h + 1], K[lo:hi], V[lo:hi], scale)
                 o[b, h, p], lse[b, h, p] = op[0], lp[0]
     return o, lse
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, block_table, context_lens, block_size=16):
+    """Write each sequence's newest token into its paged K/V cache.
+
+    ``context_lens[b]`` already counts the new token, so it is token
+    t = ctx_b - 1, stored in frame ``block_table[b, t // bs]`` at slot
+    ``t % bs``: the tail node appends (K_new, V_new) before attending
+    (KernelFlume paper §3.2, §5.1; logical block -> frame mapping of
+    "Distributed Paged KV-Cache Tiering and Memory Layout" on the
+    disaggregated-inference page).  k_new, v_new: ``[B, H_kv, D]``.
+    Sequences with ctx_b = 0 are left alone.  Returns new pools (copies).
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    for b, n in enumerate(context_lens):
+        n = int(n)
+        if n <= 0:
+            continue
+        frame, slot = token_location(block_table[b], n - 1, block_size)
+        k_out[frame, slot] = k_new[b]
+        v_out[frame, slot] = v_new[b]
+    return k_out, v_out
 
 
 def kv_cache_bytes(seq_lens, n_kv_heads, head_dim, n_layers, bytes_per_elem=2):

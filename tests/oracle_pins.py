@@ -370,6 +370,40 @@ def pin_balanced_segments(O):
     assert O.balanced_segments([40, 8], 16, 2) == [(0, 0, 0, 32), (1, 0, 32, 40), (1, 1, 0, 8)]
 
 
+def pin_kv_append(O):
+    ex = _golden("paged_layout_example.json")
+    row = [blk["physical_frame"] for blk in ex["logical_blocks"]]
+    # the figure's request: token 47 is the last slot of logical block 2 (frame 88),
+    # token 16 the first slot of logical block 1 (frame 9)
+    for ctx, frame, slot in ((48, 88, 15), (17, 9, 0), (1, 42, 0)):
+        k = np.zeros((100, 16, 1, 2))
+        v = np.zeros((100, 16, 1, 2))
+        kn = np.array([[[1.0, 2.0]]])
+        k2, v2 = O.kv_append(k, v, kn, -kn, [row], [ctx])
+        changed = np.argwhere(np.any(k2 != k, axis=(2, 3)))
+        assert changed.tolist() == [[frame, slot]], (ctx, changed.tolist())
+        assert np.array_equal(k2[frame, slot], kn[0]) and np.array_equal(v2[frame, slot], -kn[0])
+    # append then attend == attention over the old rows plus the new one, contiguous
+    rng = np.random.default_rng(23)
+    lens_old = [0, 15, 16, 40]
+    lens = [n + 1 for n in lens_old]
+    q, k, v, table, _ = small_paged(rng, lens, 4, 2, 8)
+    kn = rng.standard_normal((4, 2, 8)).astype(np.float16)
+    vn = rng.standard_normal((4, 2, 8)).astype(np.float16)
+    k2, v2 = O.kv_append(k, v, kn, vn, table, lens)
+    out, lse = O.paged_decode_attention(q, k2, v2, table, lens, 0.3)
+    for b, n in enumerate(lens_old):
+        for h in range(4):
+            g = h // 2
+            K = np.concatenate([O.gather_sequence(k, table[b], n, g), kn[b, g][None].astype(np.float64)])
+            V = np.concatenate([O.gather_sequence(v, table[b], n, g), vn[b, g][None].astype(np.float64)])
+            o, l = O.attend(q[b, h:h + 1], K, V, 0.3)
+            assert np.array_equal(out[b, h], o[0]) and np.array_equal(lse[b, h], l[0])
+    # ctx = 0 appends nothing
+    k3, _ = O.kv_append(k, v, kn, vn, table, [0, 0, 0, 0])
+    assert np.array_equal(k3, k)
+
+
 ALL_PINS = [
     pin_page_layout_example,
     pin_block_stride,
@@ -386,4 +420,5 @@ ALL_PINS = [
     pin_partitions,
     pin_balanced_segments,
     pin_poison_not_read,
+    pin_kv_append,
 ]

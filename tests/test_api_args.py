@@ -142,3 +142,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("PDA_LIBRARY", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.load_library()
+
+
+def test_kv_append_rejects(lib):
+    vp = ctypes.c_void_p
+    args = [vp(1), vp(1), vp(1), vp(1), vp(1), 4, vp(1), 2, 8, 128, 16, 10, 4, None]
+    bad_d = list(args)
+    bad_d[9] = 64
+    assert lib.paged_kv_append(*bad_d) == 2
+    bad_ptr = list(args)
+    bad_ptr[0] = None
+    assert lib.paged_kv_append(*bad_ptr) == 1
+    bad_stride = list(args)
+    bad_stride[5] = 3
+    assert lib.paged_kv_append(*bad_stride) == 1
+    empty = list(args)
+    empty[7] = 0
+    assert lib.paged_kv_append(*empty) == 0

@@ -23,6 +23,7 @@ _merge = O.merge_partials
 _ranges = O.partition_ranges
 _token_location = O.token_location
 _segments = O.balanced_segments
+_append = O.kv_append
 
 
 def _attend_lse_without_max(q_rows, K, V, scale):
@@ -64,6 +65,10 @@ MUTANTS = {
     "segments_skip_last_unit": ("balanced_segments",
                                 lambda lens, P, n: [(w, b, lo, hi - P if hi - lo > P else hi)
                                                     for w, b, lo, hi in _segments(lens, P, n)]),
+    "append_one_slot_late": ("kv_append",
+                             lambda k, v, kn, vn, bt, lens, bs=16: _append(
+                                 k, v, kn, vn, bt, [n + 1 if 0 < n and n % bs else n for n in lens],
+                                 bs)),
     "partition_end_short": ("partition_ranges",
                             lambda n, P: [(lo, max(lo, hi - 1)) if hi - lo > 1 else (lo, hi)
                                           for lo, hi in _ranges(n, P)]),

@@ -309,3 +309,49 @@ def test_full_size_partial_merge():
     _check_sampled(case, merged, mlse, [0, 17, 31])
     del case
     torch.cuda.empty_cache()
+
+
+# --- KV append of the decoded token --------------------------------------------
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 2)])
+def test_kv_append_then_attend(Hq, Hkv):
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257]   # counts the appended token
+    case = W.build_case(lens, Hq, Hkv, seed=12, device="cuda",
+                        pool_blocks=sum(-(-n // 16) for n in lens) + 5)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    kn = torch.randn((case.B, Hkv, 128), generator=g, device="cuda").half()
+    vn = torch.randn((case.B, Hkv, 128), generator=g, device="cuda").half()
+    q, k, v, table, ln = W.host_full(case)
+    k_ref, v_ref = O.kv_append(k, v, kn.cpu().numpy(), vn.cpu().numpy(), table, ln)
+    _say(f"[append] B={case.B} Hkv={Hkv}")
+    pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table, case.context_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(case.k_cache.cpu().numpy()), _bits(k_ref))
+    assert np.array_equal(_bits(case.v_cache.cpu().numpy()), _bits(v_ref))
+    out, lse = run(case)
+    ref, ref_lse = O.paged_decode_attention(q, k_ref, v_ref, table, ln, case.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_kv_append_full_size():
+    case = W.llama8b_4k(device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(14)
+    kn = torch.randn((case.B, 8, 128), generator=g, device="cuda").half()
+    vn = torch.randn((case.B, 8, 128), generator=g, device="cuda").half()
+    before = case.k_cache[::97].clone()
+    pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table, case.context_lens)
+    torch.cuda.synchronize()
+    last = torch.from_numpy(case.block_table_host[:, 255]).cuda()
+    assert torch.equal(case.k_cache[last, 15], kn) and torch.equal(case.v_cache[last, 15], vn)
+    touched = set(case.block_table_host[:, 255].tolist())
+    rows = [i for i in range(0, case.num_blocks, 97) if i not in touched]
+    assert torch.equal(case.k_cache[rows], before[[r // 97 for r in rows]])
+    out, lse = run(case)
+    _check_sampled(case, out, lse, [0, 31, 63])
+    del case
+    torch.cuda.empty_cache()
