@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code never relies on NaN propagation (tails are masked by select),
+    # so max reductions fuse into single DPP instructions
+    "-Xarch_device", "-fno-honor-nans",
     "-Wall",
 ]
 

@@ -150,7 +150,8 @@ struct SplitParams {
   int P;                    // unit length in tokens
   int n_runs;               // runs of the unit stream (one per work-group and head group)
   int hg;                   // KV heads (waves) per work-group; Hkv / hg head groups
-  float qk_scale;           // scale * log2(e): scores in base-2 units
+  float qk_scale;           // |scale| * log2(e): scores in base-2 units
+  unsigned q_sign;          // 0x80008000 to negate q (scale < 0), else 0
   float* ws_o;              // [n_runs + B, Hq, D] normalised partials
   float* ws_lse;            // [n_runs + B, Hq] natural-log lse of each partial
   int32_t* ws_hdr;          // [4 + B]: k, U, n_runs, P, units before sequence b
@@ -186,20 +187,18 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4], c
     sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(half8_t, kr[i]), sc, 0,
                                                 0, 0);
   constexpr int kR = G < 4 ? G : 4;   // score registers that hold real heads
-  float s[kR];
+  const bool tok_valid = !kMasked || t < nvalid;
+  float s[kR];                        // raw q.k; the scale is applied inside the exponent
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    s[r] = sc[r] * qk_scale;
-    if (kMasked && t >= nvalid) s[r] = -INFINITY;
-  }
+  for (int r = 0; r < kR; ++r) s[r] = tok_valid ? sc[r] : -INFINITY;
 
-  // block max of every head, uniform over the wave
+  // block max of every head (base-2 units), uniform over the wave
   float mb[G];
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     const float x = row16_max(s[r]);
 #pragma unroll
-    for (int cc = 0; cc * 4 + r < G; ++cc) mb[cc * 4 + r] = uniform_f32(x, 16 * cc);
+    for (int cc = 0; cc * 4 + r < G; ++cc) mb[cc * 4 + r] = uniform_f32(x, 16 * cc) * qk_scale;
   }
   bool grow = false;
 #pragma unroll
@@ -225,14 +224,17 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4], c
       for (int e = 0; e < 8; ++e) st.acc[j][e] *= alpha[j];
   }
 
-  // p = exp2(s - m); lane (c, t) owns p of heads 4c + r for token t
+  // p = exp2(scale' * s - m); lane (c, t) owns p of heads 4c + r for token t.
+  // A token past the end gets p = 0 by select (scale' may be 0, and -inf * 0
+  // would be NaN).
   float pr[kR];
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
     float m = st.m[r];
 #pragma unroll
     for (int cc = 1; cc * 4 + r < G; ++cc) m = c == cc ? st.m[cc * 4 + r] : m;
-    pr[r] = fast_exp2(s[r] - m);
+    pr[r] = fast_exp2(fmaf(s[r], qk_scale, -m));
+    if (kMasked) pr[r] = tok_valid ? pr[r] : 0.0f;
     st.lp[r] += pr[r];
   }
   // hand p to the V layout through LDS: lds_p[token][head]
@@ -294,17 +296,22 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (t < G)
-        qa[i] = __builtin_bit_cast(half8_t, *reinterpret_cast<const u32x4*>(qrow + 32 * i));
+        qa[i] = __builtin_bit_cast(half8_t,
+                                   *reinterpret_cast<const u32x4*>(qrow + 32 * i) ^ p.q_sign);
       else
         qa[i] = __builtin_bit_cast(half8_t, u32x4{0u, 0u, 0u, 0u});
     }
   }
 
   const int row_stride = p.Hkv * kD;                  // elements between tokens of a block
-  const long long block_stride = (long long)kBS * row_stride;
-  // K: lane (c, t) reads token t, dims 32i + 8c; V: lane (tg, ds) reads token 4i + tg, dims 8ds
-  const _Float16* kbase = p.k + (long long)t * row_stride + (long long)g * kD + 8 * c;
-  const _Float16* vbase = p.v + (long long)tg * row_stride + (long long)g * kD + 8 * ds;
+  const long long block_bytes = (long long)kBS * row_stride * 2;
+  // byte offsets inside a block: K lane (c, t) reads token t, dims 32i + 8c;
+  // V lane (tg, ds) reads token 4i + tg, dims 8ds (the block base is uniform)
+  const unsigned k_lane = (unsigned)(((t * p.Hkv + g) * kD + 8 * c) * 2);
+  const unsigned v_lane = (unsigned)(((tg * p.Hkv + g) * kD + 8 * ds) * 2);
+  const unsigned row_bytes = (unsigned)row_stride * 2;
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int32_t* bt_row = p.bt + (long long)b * p.bt_stride + tok_lo / kBS;
   const int ntok = tok_hi - tok_lo;
   const int nblk = (ntok + kBS - 1) / kBS;
@@ -330,20 +337,20 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
     // ids outside the pool are clamped: a broken table gives wrong numbers, not a fault
     const unsigned raw = (unsigned)__builtin_amdgcn_readlane(window, kb & 63);
     const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
-    return blk * block_stride;
+    return blk * block_bytes;
   };
   // K/V are read once per call: non-temporal loads keep them from displacing
   // the block table, q and the partials in the caches
   auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-    const _Float16* kp = kbase + off;
-    const _Float16* vp = vbase + off;
+    const char* kb = kbytes + off;
+    const char* vb = vbytes + off;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * i));
+      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + k_lane + 64 * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       vr[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(vp + (long long)4 * i * row_stride));
+          reinterpret_cast<const u32x4*>(vb + v_lane + 4 * i * row_bytes));
   };
   auto fold = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
@@ -774,7 +781,9 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
     return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
                 (long long)bt_stride, max_blocks);
   if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
-  if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale must be finite");
+  uint32_t scale_bits;
+  std::memcpy(&scale_bits, &scale, sizeof(scale_bits));
+  if ((scale_bits & 0x7F800000u) == 0x7F800000u) return fail(PDA_EINVAL, "scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
   const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens);
   if (workspace_bytes < pl.total)
@@ -802,7 +811,8 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.P = pl.P;
   sp.n_runs = pl.n_runs;
   sp.hg = pl.hg;
-  sp.qk_scale = scale * kLog2e;
+  sp.qk_scale = std::fabs(scale) * kLog2e;
+  sp.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
   sp.ws_o = reinterpret_cast<float*>(ws + pl.o_offset);
   sp.ws_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   sp.ws_hdr = reinterpret_cast<int32_t*>(ws + pl.hdr_offset);

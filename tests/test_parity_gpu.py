@@ -355,3 +355,13 @@ def test_kv_append_full_size():
     _check_sampled(case, out, lse, [0, 31, 63])
     del case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("scale", [-0.0883883476, 0.5, 1e-3])
+def test_scale_sign_and_size(scale):
+    case = W.build_case(RAGGED, 32, 8, seed=15, device="cuda")
+    case.scale = float(np.float32(scale))
+    out, lse = run(case)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
