@@ -63,6 +63,9 @@ __all__ = [
     "split_k_partials",
     "balanced_segments",
     "kv_append",
+    "fp8_e4m3_value",
+    "fp8_e4m3_decode",
+    "paged_decode_attention_fp8",
     "kv_cache_bytes",
     "kv_read_bytes",
 ]
@@ -311,6 +314,62 @@ def kv_append(k_pool, v_pool, k_new, v_new, block_table, context_lens, block_siz
         k_out[frame, slot] = k_new[b]
         v_out[frame, slot] = v_new[b]
     return k_out, v_out
+
+
+def fp8_e4m3_value(code):
+    """Value of one FP8 E4M3 code (the OCP 8-bit format: 1 sign bit, 4
+    exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal,
+    m * 2^-9; the codes S.1111.111 are NaN; there are no infinities).
+
+    The FP8 KV cache of "4. Quantised KV cache" in "Optimising decode in vLLM"
+    (and the kv_cache_dtype knob of the vLLM attention-backend page) stores
+    one such code per element next to a per-tensor scale.
+    """
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3_decode(codes):
+    """Element-wise fp8_e4m3_value of a uint8 array, as float64."""
+    table = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def paged_decode_attention_fp8(q, k_codes, v_codes, block_table, context_lens, scale, k_scale,
+                               v_scale, block_size=16):
+    """Decode attention over an FP8 E4M3 paged cache with per-tensor scales.
+
+    Stored code c of K means k_scale * value(c), of V v_scale * value(c).  Each
+    sequence's rows are gathered through the block table, decoded and scaled in
+    float64, then attended exactly as in paged_decode_attention.
+    """
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    Hkv = k_codes.shape[2]
+    assert Hq % Hkv == 0
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(context_lens[b])
+        kv = {}
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            if g not in kv:
+                kc = _gather_sequence_blocks(k_codes, block_table[b], n, g, block_size)
+                vc = _gather_sequence_blocks(v_codes, block_table[b], n, g, block_size)
+                kv[g] = (float(k_scale) * fp8_e4m3_decode(kc.astype(np.uint8)),
+                         float(v_scale) * fp8_e4m3_decode(vc.astype(np.uint8)))
+            K, V = kv[g]
+            o, l = attend(q[b, h:h + 1], K, V, scale)
+            out[b, h], lse[b, h] = o[0], l[0]
+    return out, lse
 
 
 def kv_cache_bytes(seq_lens, n_kv_heads, head_dim, n_layers, bytes_per_elem=2):

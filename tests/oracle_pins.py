@@ -404,6 +404,63 @@ def pin_kv_append(O):
     assert np.array_equal(k3, k)
 
 
+def pin_fp8_decode(O):
+    g = _golden("fp8_e4m3_codes.json")
+    for code, want in g["codes"].items():
+        got = O.fp8_e4m3_value(int(code, 16))
+        if want == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got)
+    # an independent decoder of the same format: torch's float8_e4m3fn, all 256 codes
+    import torch
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    got = O.fp8_e4m3_decode(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def pin_fp8_attention(O):
+    rng = np.random.default_rng(24)
+    Hq, Hkv, D = 4, 2, 8
+    lens = [1, 9, 40]
+    _, _, _, table, _ = small_paged(rng, lens, Hq, Hkv, D)
+    pool = table.max() + 1
+    codes = rng.integers(0, 256, size=(pool, 16, Hkv, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                     # no NaN codes in owned slots
+    vcodes = rng.integers(0, 256, size=(pool, 16, Hkv, D)).astype(np.uint8)
+    vcodes[(vcodes & 0x7F) == 0x7F] = 0x3C
+    q = rng.standard_normal((len(lens), Hq, D)).astype(np.float16)
+    ks, vs = 0.0125, 0.5
+    out, lse = O.paged_decode_attention_fp8(q, codes, vcodes, table, lens, 0.3, ks, vs)
+    # one token: out = v_scale * value(code), exactly
+    f, sl = int(table[0, 0]), 0
+    for h in range(Hq):
+        want = vs * np.array([O.fp8_e4m3_value(c) for c in vcodes[f, sl, h // 2]])
+        assert np.array_equal(out[0, h], want)
+    # paged fp8 == attention on the decoded contiguous rows, bitwise
+    for b, n in enumerate(lens):
+        for h in range(Hq):
+            g = h // 2
+            rows = [(int(table[b][t // 16]), t % 16) for t in range(n)]
+            K = np.array([[ks * O.fp8_e4m3_value(c) for c in codes[fr, s_, g]] for fr, s_ in rows])
+            V = np.array([[vs * O.fp8_e4m3_value(c) for c in vcodes[fr, s_, g]] for fr, s_ in rows])
+            o, l = O.attend(q[b, h:h + 1], K, V, 0.3)
+            assert np.array_equal(out[b, h], o[0]) and np.array_equal(lse[b, h], l[0])
+    # scale 0: the mean of the decoded, scaled V rows
+    out0, lse0 = O.paged_decode_attention_fp8(q, codes, vcodes, table, lens, 0.0, ks, vs)
+    b, n = 2, lens[2]
+    for h in range(Hq):
+        vals = [[Fraction(O.fp8_e4m3_value(c)) for c in vcodes[int(table[b][t // 16]), t % 16, h // 2]]
+                for t in range(n)]
+        for d in range(D):
+            exact = Fraction(vs) * sum(v[d] for v in vals) / n
+            assert abs(Fraction(out0[b, h, d]) - exact) <= Fraction(1, 2 ** 50)
+        assert abs(lse0[b, h] - math.log(n)) <= 1e-15 * math.log(n)
+
+
 ALL_PINS = [
     pin_page_layout_example,
     pin_block_stride,
@@ -421,4 +478,6 @@ ALL_PINS = [
     pin_balanced_segments,
     pin_poison_not_read,
     pin_kv_append,
+    pin_fp8_decode,
+    pin_fp8_attention,
 ]

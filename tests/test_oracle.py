@@ -24,6 +24,7 @@ _ranges = O.partition_ranges
 _token_location = O.token_location
 _segments = O.balanced_segments
 _append = O.kv_append
+_fp8 = O.fp8_e4m3_value
 
 
 def _attend_lse_without_max(q_rows, K, V, scale):
@@ -69,6 +70,8 @@ MUTANTS = {
                              lambda k, v, kn, vn, bt, lens, bs=16: _append(
                                  k, v, kn, vn, bt, [n + 1 if 0 < n and n % bs else n for n in lens],
                                  bs)),
+    "fp8_bias_8": ("fp8_e4m3_value",
+                   lambda code: _fp8(code) / 2.0 if (int(code) >> 3) & 0xF else _fp8(code)),
     "partition_end_short": ("partition_ranges",
                             lambda n, P: [(lo, max(lo, hi - 1)) if hi - lo > 1 else (lo, hi)
                                           for lo, hi in _ranges(n, P)]),
