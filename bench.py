@@ -38,6 +38,7 @@ def source_hash():
 
 
 def kv_bytes(lens, Hkv, D=128, elem=2):
+    """Algorithmic K+V bytes of one call: valid tokens only."""
     return int(sum(int(n) for n in lens)) * 2 * Hkv * D * elem
 
 
@@ -69,13 +70,17 @@ def cpu_baseline(case, budget_s):
     for b in order:
         q, k, v, table, lens = W.host_sequences(case, [int(b)])
         t0 = time.perf_counter()
-        O.paged_decode_attention(q, k, v, table, lens, case.scale)
+        if case.kv_dtype == "fp8":
+            O.paged_decode_attention_fp8(q, k, v, table, lens, case.scale, case.k_scale,
+                                         case.v_scale)
+        else:
+            O.paged_decode_attention(q, k, v, table, lens, case.scale)
         spent += time.perf_counter() - t0
         done.append(int(b))
         tokens += int(lens[0])
         if spent >= budget_s:
             break
-    gbs = kv_bytes([tokens], case.Hkv) / spent / 1e9
+    gbs = kv_bytes([tokens], case.Hkv, elem=case.kv_bytes_per_elem) / spent / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} of {case.B} sequences ({tokens} tokens, all {case.Hq} query "
                       f"heads), float64 numpy gather + two-pass softmax, {spent:.1f} s"}
@@ -117,13 +122,16 @@ def measure(case, P, steps, warmup, flush_mib=0):
                      device="cuda")
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    unit = pda.workspace_layout(B, Hq, Hkv, width, P)["unit_tokens"]
+    unit = pda.workspace_layout(B, Hq, Hkv, width, P,
+                                kv_fp8=case.kv_dtype == "fp8")["unit_tokens"]
     scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda") if flush_mib else None
+
+    kw = case.attn_kwargs()
 
     def step():
         pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                               case.context_lens, case.scale, out=out, lse_out=lse,
-                              partition_tokens=P, workspace=ws)
+                              partition_tokens=P, workspace=ws, **kw)
 
     for _ in range(warmup):
         step()
@@ -143,7 +151,7 @@ def measure(case, P, steps, warmup, flush_mib=0):
     wall = time.perf_counter() - t0
     ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     ev_mean = sum(ev_ms) / len(ev_ms)
-    nbytes = kv_bytes(case.lens, Hkv)
+    nbytes = kv_bytes(case.lens, Hkv, elem=case.kv_bytes_per_elem)
     ms_per_step = wall / steps * 1e3
     return {
         "kv_bytes": nbytes,
@@ -205,6 +213,8 @@ def main():
     ap.add_argument("--op", default="attention", choices=["attention", "append"],
                     help="attention (default): paged_decode_attn; append: paged_kv_append of "
                          "one token per sequence")
+    ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
+                    help="element type of the K/V cache (fp8: E4M3 codes with per-tensor scales)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch between timed calls (outside the "
                          "event pair; the wall clock includes it)")
@@ -229,7 +239,7 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     pda.load_library()
-    case = W.CONFIGS[args.config](device="cuda")
+    case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if args.op == "append":
         bench_append(case, args.steps, args.warmup)
         return
@@ -249,11 +259,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": case.kv_dtype,
         "data": "synthetic",
         "config": {
             "workload": case.name,
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128, "block_size": 16,
+            "kv_dtype": case.kv_dtype,
             "partition_tokens": m["unit_tokens"], "tokens": int(case.lens.sum()),
             "min_ctx": int(case.lens.min()), "max_ctx": int(case.lens.max()),
             "kv_bytes_per_step": nbytes, "seed": case.seed,
@@ -279,7 +290,7 @@ def main():
     for name in [x for x in args.also.split(",") if x and x != args.config]:
         del case
         torch.cuda.empty_cache()
-        case = W.CONFIGS[name](device="cuda")
+        case = W.CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)
         mm = measure(case, case.partition_tokens, args.steps, args.warmup, args.flush_mib)
         also[case.name] = {"value": mm["value"], "unit": "GB/s",
                            "pct_hbm_peak": round(100.0 * mm["value"] / HBM_PEAK_GBS, 2),
@@ -290,7 +301,7 @@ def main():
         rec["also"] = also
         del case
         torch.cuda.empty_cache()
-        case = W.CONFIGS[args.config](device="cuda")
+        case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -40,13 +40,20 @@ _SIGNATURES = {
     "pda_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.POINTER(_c_size)]),
     "pda_workspace_layout": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                      ctypes.POINTER(PdaLayout)]),
+                                      _c_int, ctypes.POINTER(PdaLayout)]),
     "paged_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_i64, _c_int, _c_float, _c_int, _vp, _vp,
                                    _c_size, _vp]),
     "paged_decode_attn_partial": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
                                            _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                                            _c_float, _c_int, _vp, _c_size, _vp]),
+    "paged_decode_attn_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int,
+                                       _c_int, _c_int, _c_int, _c_i64, _c_int, _c_float,
+                                       _c_float, _c_float, _c_int, _vp, _vp, _c_size, _vp]),
+    "paged_decode_attn_partial_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
+                                               _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                               _c_float, _c_float, _c_float, _c_int, _vp, _c_size,
+                                               _vp]),
     "merge_partials": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "paged_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
                                  _c_int, _c_i64, _c_int, _vp]),
@@ -120,17 +127,30 @@ def workspace_size(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DI
 
 
 def workspace_layout(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
-                     block_size=BLOCK_SIZE):
+                     block_size=BLOCK_SIZE, kv_fp8=False):
     """The workspace layout as a dict (see pda_workspace_layout in the header)."""
     lay = PdaLayout()
     _check(load_library().pda_workspace_layout(B, Hq, Hkv, D, block_size, max_blocks_per_seq,
-                                               partition_tokens, ctypes.byref(lay)))
+                                               partition_tokens, int(bool(kv_fp8)),
+                                               ctypes.byref(lay)))
     return {name: int(getattr(lay, name)) for name, _ in PdaLayout._fields_}
 
 
+FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def is_fp8_cache(k_cache):
+    """True for a cache of FP8 E4M3 codes (uint8 or float8_e4m3fn storage)."""
+    return k_cache.dtype in FP8_DTYPES
+
+
 def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
-    if q.dtype != torch.float16 or k_cache.dtype != torch.float16 or v_cache.dtype != torch.float16:
-        raise TypeError("q, k_cache and v_cache must be float16")
+    if q.dtype != torch.float16:
+        raise TypeError("q must be float16")
+    if not (k_cache.dtype == v_cache.dtype and
+            (k_cache.dtype == torch.float16 or k_cache.dtype in FP8_DTYPES)):
+        raise TypeError("k_cache and v_cache must both be float16, or both FP8 E4M3 codes "
+                        "(uint8 or float8_e4m3fn)")
     if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_table and context_lens must be int32")
     dev = q.device
@@ -155,7 +175,7 @@ def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
 
 
 def _run(partial, q, k_cache, v_cache, block_table, context_lens, scale, out, lse, need_lse,
-         partition_tokens, workspace, max_blocks_per_seq):
+         partition_tokens, workspace, max_blocks_per_seq, k_scale=None, v_scale=None):
     dev = _check_inputs(q, k_cache, v_cache, block_table, context_lens)
     B, Hq, D = q.shape
     num_blocks, bs, Hkv, _ = k_cache.shape
@@ -180,39 +200,54 @@ def _run(partial, q, k_cache, v_cache, block_table, context_lens, scale, out, ls
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [B, Hq]")
     lib = load_library()
-    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), bt_stride,
-            _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb, float(scale),
-            int(partition_tokens))
-    if partial:
-        rc = lib.paged_decode_attn_partial(_ptr(out), _ptr(lse), *args, _ptr(workspace),
-                                           workspace.numel() * workspace.element_size(),
+    ws_n = workspace.numel() * workspace.element_size()
+    if is_fp8_cache(k_cache):
+        if k_scale is None or v_scale is None:
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), bt_stride,
+                _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb, float(scale),
+                float(k_scale), float(v_scale), int(partition_tokens))
+        if partial:
+            rc = lib.paged_decode_attn_partial_fp8(_ptr(out), _ptr(lse), *args, _ptr(workspace),
+                                                   ws_n, _stream(dev))
+        else:
+            rc = lib.paged_decode_attn_fp8(_ptr(out), *args, _ptr(lse), _ptr(workspace), ws_n,
                                            _stream(dev))
     else:
-        rc = lib.paged_decode_attn(_ptr(out), *args, _ptr(lse), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(dev))
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), bt_stride,
+                _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb, float(scale),
+                int(partition_tokens))
+        if partial:
+            rc = lib.paged_decode_attn_partial(_ptr(out), _ptr(lse), *args, _ptr(workspace), ws_n,
+                                               _stream(dev))
+        else:
+            rc = lib.paged_decode_attn(_ptr(out), *args, _ptr(lse), _ptr(workspace), ws_n,
+                                       _stream(dev))
     _check(rc)
     return out, lse
 
 
 def paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale, out=None,
                       lse_out=None, return_lse=False, partition_tokens=0, workspace=None,
-                      max_blocks_per_seq=None):
-    """fp16 decode attention over a paged KV cache; see include/paged_attn.h.
+                      max_blocks_per_seq=None, k_scale=None, v_scale=None):
+    """Decode attention over a paged KV cache; see include/paged_attn.h.
 
-    Returns ``out`` (fp16 [B, Hq, D]), or ``(out, lse)`` when ``return_lse`` or
-    ``lse_out`` is given.
+    fp16 caches, or FP8 E4M3 caches (uint8 / float8_e4m3fn) with per-tensor
+    ``k_scale`` and ``v_scale``.  Returns ``out`` (fp16 [B, Hq, D]), or
+    ``(out, lse)`` when ``return_lse`` or ``lse_out`` is given.
     """
     out, lse = _run(False, q, k_cache, v_cache, block_table, context_lens, scale, out,
-                    lse_out, return_lse, partition_tokens, workspace, max_blocks_per_seq)
+                    lse_out, return_lse, partition_tokens, workspace, max_blocks_per_seq,
+                    k_scale, v_scale)
     return (out, lse) if (return_lse or lse_out is not None) else out
 
 
 def paged_decode_attn_partial(q, k_cache, v_cache, block_table, context_lens, scale, o=None,
                               lse=None, partition_tokens=0, workspace=None,
-                              max_blocks_per_seq=None):
+                              max_blocks_per_seq=None, k_scale=None, v_scale=None):
     """Normalised partial (o fp32 [B, Hq, D], lse fp32 [B, Hq]) of a token range."""
     return _run(True, q, k_cache, v_cache, block_table, context_lens, scale, o, lse, True,
-                partition_tokens, workspace, max_blocks_per_seq)
+                partition_tokens, workspace, max_blocks_per_seq, k_scale, v_scale)
 
 
 def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
@@ -242,6 +277,8 @@ def paged_kv_append(k_cache, v_cache, k_new, v_new, block_table, context_lens,
                     max_blocks_per_seq=None):
     """Write token ctx_b - 1 of every sequence (k_new, v_new: fp16 [B, Hkv, D]) in place."""
     dev = _check_inputs(k_new, k_cache, v_cache, block_table, context_lens)
+    if k_cache.dtype != torch.float16:
+        raise TypeError("paged_kv_append writes fp16 caches")
     B = k_new.shape[0]
     num_blocks, bs, Hkv, D = k_cache.shape
     if (k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or k_new.dtype != torch.float16

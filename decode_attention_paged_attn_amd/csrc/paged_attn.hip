@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "paged_attn.h"
@@ -63,7 +64,16 @@ constexpr int kMaxWavesPerWG = 4;     // KV heads of one work-group
 // occupancy target of the split kernel: 2 waves per SIMD with two blocks of
 // K/V in flight per wave measured faster than 3 waves per SIMD squeezed into
 // 168 VGPRs
-constexpr int waves_per_eu(int) { return 2; }
+#ifndef PDA_WAVES_PER_EU_FP8
+#define PDA_WAVES_PER_EU_FP8 2
+#endif
+#ifndef PDA_RING_FP16
+#define PDA_RING_FP16 2
+#endif
+#ifndef PDA_RING_FP8
+#define PDA_RING_FP8 3
+#endif
+constexpr int waves_per_eu(int G, bool fp8) { return fp8 && G <= 4 ? PDA_WAVES_PER_EU_FP8 : 2; }
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kHdrInts = 4;           // k, U, n_runs, P, then units_before[b]
 constexpr float kLog2e = 1.4426950408889634f;
@@ -139,8 +149,8 @@ __device__ __forceinline__ float fast_exp2(float x) {  // v_exp_f32; exp2(-inf) 
 
 struct SplitParams {
   const _Float16* q;        // [B, Hq, D]
-  const _Float16* k;        // [num_blocks, 16, Hkv, D]
-  const _Float16* v;
+  const void* k;            // [num_blocks, 16, Hkv, D] fp16, or FP8 E4M3 codes
+  const void* v;
   const int32_t* bt;        // [B, bt_stride]
   const int32_t* ctx;       // [B]
   long long bt_stride;
@@ -152,6 +162,7 @@ struct SplitParams {
   int hg;                   // KV heads (waves) per work-group; Hkv / hg head groups
   float qk_scale;           // |scale| * log2(e): scores in base-2 units
   unsigned q_sign;          // 0x80008000 to negate q (scale < 0), else 0
+  float v_scale;            // multiplies the output (FP8 V scale; 1 for fp16)
   float* ws_o;              // [n_runs + B, Hq, D] normalised partials
   float* ws_lse;            // [n_runs + B, Hq] natural-log lse of each partial
   int32_t* ws_hdr;          // [4 + B]: k, U, n_runs, P, units before sequence b
@@ -164,6 +175,22 @@ __device__ __forceinline__ int seq_len(const SplitParams& p, int b) {
   return min(max(p.ctx[b], 0), p.max_tokens);
 }
 
+// K/V element storage.  fp16 elements are used as stored.  FP8 elements are
+// E4M3 codes, decoded exactly (every E4M3 value is an fp16 value) to fp16 for
+// the MFMA operands of K and to fp32 for V; the per-tensor scales are folded
+// into the softmax scale and the output normalisation.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <bool kFp8>
+struct KvFmt {
+  static constexpr int kElemBytes = kFp8 ? 1 : 2;
+  static constexpr int kKLoads = kFp8 ? 2 : 4;     // 16-byte K loads per lane per block
+  using VRow = typename std::conditional<kFp8, u32x2, u32x4>::type;   // 8 V elements
+  // MFMA k-chunk i (8 dims), lane group c: first head dimension it covers
+  __device__ static constexpr int q_dim(int i, int c) {
+    return kFp8 ? 64 * (i / 2) + 16 * c + 8 * (i % 2) : 32 * i + 8 * c;
+  }
+};
+
 // Per-wave state of one segment for KV head g and its G query heads.
 template <int G>
 struct Seg {
@@ -172,20 +199,40 @@ struct Seg {
   float acc[G][8];          // output dims 8*ds .. 8*ds+7 over this lane's token row
 };
 
-template <int G, bool kMasked>
-__device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4], const u32x4 (&kr)[4],
-                                           const u32x4 (&vr)[4], float* lds_p, float qk_scale,
-                                           int lane, int nvalid) {
+template <int G, bool kMasked, bool kFp8>
+__device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
+                                           const u32x4 (&kr)[KvFmt<kFp8>::kKLoads],
+                                           const typename KvFmt<kFp8>::VRow (&vr)[4], float* lds_p,
+                                           float qk_scale, int lane, int nvalid) {
   const int t = lane & 15;        // MFMA column: token of the block
   const int c = lane >> 4;        // MFMA row group: heads 4c .. 4c+3
   const int tg = lane >> 4;       // V layout: token row 4i + tg
+
+  // K as MFMA B operands: lane (c, t) holds token t, dims KvFmt::q_dim(i, c) + 0..7
+  half8_t kop[4];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kr[j][w], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kr[j][w], 1.0f, true);
+        half8_t& dst = kop[2 * j + w / 2];
+        dst[4 * (w % 2) + 0] = lo[0];
+        dst[4 * (w % 2) + 1] = lo[1];
+        dst[4 * (w % 2) + 2] = hi[0];
+        dst[4 * (w % 2) + 3] = hi[1];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kop[i] = __builtin_bit_cast(half8_t, kr[i]);
+  }
 
   // scores: D[head][token] = sum_d q[head][d] k[token][d]
   f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], __builtin_bit_cast(half8_t, kr[i]), sc, 0,
-                                                0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], kop[i], sc, 0, 0, 0);
   constexpr int kR = G < 4 ? G : 4;   // score registers that hold real heads
   const bool tok_valid = !kMasked || t < nvalid;
   float s[kR];                        // raw q.k; the scale is applied inside the exponent
@@ -268,48 +315,84 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4], c
 
   // acc += p v; a token past the end contributes an exact zero row (selected,
   // so a NaN in an unused slot cannot leak through 0 * NaN)
+  if constexpr (kFp8) {
+    // FP8: packed fp16 dot products over the token pairs (4i + tg, 4(i+1) + tg),
+    // i = 0, 2: the codes of the two tokens are interleaved byte by byte, so
+    // one exact E4M3 -> fp16 conversion yields (v[t0][d], v[t1][d]), and p of
+    // the two tokens is rounded to fp16 for the product (sums stay fp32).
+    u32x2 vv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool valid = !kMasked || (4 * i + tg < nvalid);
-    const _Float16* vh = reinterpret_cast<const _Float16*>(&vr[i]);
+    for (int i = 0; i < 4; ++i)
+      vv[i] = (!kMasked || 4 * i + tg < nvalid) ? vr[i] : u32x2{0u, 0u};   // code 0 = +0
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = static_cast<float>(vh[e]);
-      if (kMasked) x = valid ? x : 0.0f;
+    for (int i0 = 0; i0 < 4; i0 += 2) {
+      half2_t pp[G];
 #pragma unroll
-      for (int j = 0; j < G; ++j) st.acc[j][e] = fmaf(pv[i][j], x, st.acc[j][e]);
+      for (int j = 0; j < G; ++j)
+        pp[j] = half2_t{static_cast<_Float16>(pv[i0][j]), static_cast<_Float16>(pv[i0 + 1][j])};
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {                  // dims 4w .. 4w+3 of this lane's 8
+        const unsigned a = vv[i0][w], b = vv[i0 + 1][w];
+        const unsigned lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+        const unsigned hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+        const half2_t v2[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false),
+                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+            st.acc[j][4 * w + e] = __builtin_amdgcn_fdot2(pp[j], v2[e], st.acc[j][4 * w + e],
+                                                          false);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = !kMasked || (4 * i + tg < nvalid);
+      const _Float16* vh = reinterpret_cast<const _Float16*>(&vr[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = static_cast<float>(vh[e]);
+        if (kMasked) x = valid ? x : 0.0f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) st.acc[j][e] = fmaf(pv[i][j], x, st.acc[j][e]);
+      }
     }
   }
 }
 
 // One wave: KV head g of sequence b over tokens [tok_lo, tok_hi).
-template <int G>
+template <int G, bool kFp8>
 __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g, int b, int tok_lo,
                             int tok_hi, bool whole, int slot) {
   const int c = lane >> 4, t = lane & 15;
   const int tg = lane >> 4, ds = lane & 15;
 
-  // Q rows as the MFMA A operand: lane (c, t) holds head t, dims 32i + 8c + 0..7
+  using Fmt = KvFmt<kFp8>;
+  // Q rows as the MFMA A operand: lane (c, t) holds head t, dims Fmt::q_dim(i, c) + 0..7
   half8_t qa[4];
   {
-    const _Float16* qrow = p.q + ((long long)b * p.Hq + (long long)g * G + t) * kD + 8 * c;
+    const _Float16* qrow = p.q + ((long long)b * p.Hq + (long long)g * G + t) * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (t < G)
-        qa[i] = __builtin_bit_cast(half8_t,
-                                   *reinterpret_cast<const u32x4*>(qrow + 32 * i) ^ p.q_sign);
+        qa[i] = __builtin_bit_cast(
+            half8_t, *reinterpret_cast<const u32x4*>(qrow + Fmt::q_dim(i, c)) ^ p.q_sign);
       else
         qa[i] = __builtin_bit_cast(half8_t, u32x4{0u, 0u, 0u, 0u});
     }
   }
 
-  const int row_stride = p.Hkv * kD;                  // elements between tokens of a block
-  const long long block_bytes = (long long)kBS * row_stride * 2;
-  // byte offsets inside a block: K lane (c, t) reads token t, dims 32i + 8c;
-  // V lane (tg, ds) reads token 4i + tg, dims 8ds (the block base is uniform)
-  const unsigned k_lane = (unsigned)(((t * p.Hkv + g) * kD + 8 * c) * 2);
-  const unsigned v_lane = (unsigned)(((tg * p.Hkv + g) * kD + 8 * ds) * 2);
-  const unsigned row_bytes = (unsigned)row_stride * 2;
+  constexpr int E = Fmt::kElemBytes;
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);   // between tokens of a block
+  const long long block_bytes = (long long)kBS * row_bytes;
+  // byte offsets inside a block (the block base is uniform): K lane (c, t)
+  // reads token t, 16 bytes at 16c + 64i; V lane (tg, ds) reads token 4i + tg,
+  // dims 8ds .. 8ds+7
+  const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * E + 16 * c);
+  const unsigned v_lane = (unsigned)((tg * p.Hkv + g) * kD * E + 8 * E * ds);
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int32_t* bt_row = p.bt + (long long)b * p.bt_stride + tok_lo / kBS;
@@ -341,35 +424,43 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   };
   // K/V are read once per call: non-temporal loads keep them from displacing
   // the block table, q and the partials in the caches
-  auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+  using VRow = typename Fmt::VRow;
+  constexpr int KL = Fmt::kKLoads;
+  auto load = [&](long long off, u32x4 (&kr)[KL], VRow (&vr)[4]) {
     const char* kb = kbytes + off;
     const char* vb = vbytes + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < KL; ++i)
       kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + k_lane + 64 * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       vr[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(vb + v_lane + 4 * i * row_bytes));
+          reinterpret_cast<const VRow*>(vb + v_lane + 4 * i * row_bytes));
   };
-  auto fold = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4], int kb) {
+  auto fold = [&](const u32x4 (&kr)[KL], const VRow (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
-      fold_block<G, true>(st, qa, kr, vr, lds_p, p.qk_scale, lane, last_valid);
+      fold_block<G, true, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, last_valid);
     else
-      fold_block<G, false>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
+      fold_block<G, false, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
   };
 
-  // two register buffers: block kb+1 is in flight while block kb is folded
-  u32x4 ka[4], va[4], kb2[4], vb2[4];
-  load(block_off(0), ka, va);
-  int kb = 0;
-  while (true) {
-    if (kb + 1 < nblk) load(block_off(kb + 1), kb2, vb2);
-    fold(ka, va, kb);
-    if (++kb == nblk) break;
-    if (kb + 1 < nblk) load(block_off(kb + 1), ka, va);
-    fold(kb2, vb2, kb);
-    if (++kb == nblk) break;
+  // a ring of NB register buffers: blocks kb+1 .. kb+NB-1 are in flight while
+  // block kb is folded (FP8 blocks are half the bytes, so they keep one more)
+  constexpr int NB = kFp8 ? PDA_RING_FP8 : PDA_RING_FP16;
+  u32x4 kbuf[NB][KL];
+  VRow vbuf[NB][4];
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (i < nblk) load(block_off(i), kbuf[i], vbuf[i]);
+  for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      const int cur = kb0 + s;
+      if (cur >= nblk) break;
+      const int nxt = cur + NB - 1;
+      if (nxt < nblk) load(block_off(nxt), kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
+      fold(kbuf[s], vbuf[s], cur);
+    }
   }
 
   // epilogue: totals over token slots and token rows, normalise, store
@@ -388,7 +479,7 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = add_xor32(add_xor16(st.acc[j][e]));
     if ((j & 3) != tg) continue;
-    const float inv = 1.0f / l_tot[j];
+    const float inv = p.v_scale / l_tot[j];
     const float lse = (st.m[j] + __builtin_log2f(l_tot[j])) * kLn2;
     if (whole) {
       const long long dst = ((long long)b * p.Hq + hq0 + j) * kD + 8 * ds;
@@ -413,9 +504,9 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   }
 }
 
-template <int G>
+template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMaxWavesPerWG)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu(G))))
+__attribute__((amdgpu_waves_per_eu(waves_per_eu(G, kFp8))))
 void split_kernel(SplitParams p) {
   __shared__ float lds[kMaxWavesPerWG][kBS * G];
   const int lane = threadIdx.x & (kWave - 1);
@@ -471,7 +562,8 @@ void split_kernel(SplitParams p) {
     if (p_hi > p_lo) {
       const int tok_lo = p_lo * p.P;
       const int tok_hi = min(p_hi * p.P, n);
-      run_segment<G>(p, lds_p, lane, g, b, tok_lo, tok_hi, p_lo == 0 && p_hi == nu, w + b);
+      run_segment<G, kFp8>(p, lds_p, lane, g, b, tok_lo, tok_hi, p_lo == 0 && p_hi == nu,
+                           w + b);
       u = before + p_hi;
     }
     before += nu;
@@ -635,23 +727,31 @@ int ok() {
 }
 
 // Per-device launch facts, filled once: CU count and how many split-kernel
-// work-groups of each (G, waves per work-group) shape fit on one CU.
+// work-groups of each (G, KV format, waves per work-group) shape fit on a CU.
 constexpr int kMaxDevices = 64;
 struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMaxWavesPerWG + 1] = {};   // [log2 G][waves per work-group]
+  int wg_per_cu[4][2][kMaxWavesPerWG + 1] = {};   // [log2 G][fp8][waves per work-group]
 };
 DeviceFacts g_dev[kMaxDevices];
 
 int log2_group(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
-const void* split_kernel_ptr(int G) {
+const void* split_kernel_ptr(int G, bool fp8) {
+  if (fp8) {
+    switch (G) {
+      case 1: return reinterpret_cast<const void*>(&split_kernel<1, true>);
+      case 2: return reinterpret_cast<const void*>(&split_kernel<2, true>);
+      case 4: return reinterpret_cast<const void*>(&split_kernel<4, true>);
+      default: return reinterpret_cast<const void*>(&split_kernel<8, true>);
+    }
+  }
   switch (G) {
-    case 1: return reinterpret_cast<const void*>(&split_kernel<1>);
-    case 2: return reinterpret_cast<const void*>(&split_kernel<2>);
-    case 4: return reinterpret_cast<const void*>(&split_kernel<4>);
-    default: return reinterpret_cast<const void*>(&split_kernel<8>);
+    case 1: return reinterpret_cast<const void*>(&split_kernel<1, false>);
+    case 2: return reinterpret_cast<const void*>(&split_kernel<2, false>);
+    case 4: return reinterpret_cast<const void*>(&split_kernel<4, false>);
+    default: return reinterpret_cast<const void*>(&split_kernel<8, false>);
   }
 }
 
@@ -662,9 +762,9 @@ int head_group(int Hkv) {
   return 1;
 }
 
-// Runs of the unit stream for (G, Hkv) on the current device: as many
-// work-groups as fit on all CUs at once, divided by the head groups per run.
-int run_count(int G, int Hkv) {
+// Runs of the unit stream for (G, Hkv, KV format) on the current device: as
+// many work-groups as fit on all CUs at once, divided by the head groups.
+int run_count(int G, int Hkv, bool fp8) {
   const int hg = head_group(Hkv);
   const int n_hgroups = Hkv / hg;
   int dev = 0;
@@ -678,16 +778,17 @@ int run_count(int G, int Hkv) {
       cus = 256;
     f.cus = cus;
     for (int lg = 0; lg < 4; ++lg)
-      for (int w = 1; w <= kMaxWavesPerWG; ++w) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg), w * kWave,
-                                                         0) != hipSuccess ||
-            n <= 0)
-          n = 1;
-        f.wg_per_cu[lg][w] = n;
-      }
+      for (int f8 = 0; f8 < 2; ++f8)
+        for (int w = 1; w <= kMaxWavesPerWG; ++w) {
+          int n = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg, f8 != 0),
+                                                           w * kWave, 0) != hipSuccess ||
+              n <= 0)
+            n = 1;
+          f.wg_per_cu[lg][f8][w] = n;
+        }
   });
-  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][hg] / n_hgroups);
+  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][fp8 ? 1 : 0][hg] / n_hgroups);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -725,10 +826,10 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
   return PDA_OK;
 }
 
-Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens) {
+Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens, bool fp8) {
   Plan pl;
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_runs = run_count(Hq / Hkv, Hkv);
+  pl.n_runs = run_count(Hq / Hkv, Hkv, fp8);
   pl.hg = head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
   pl.n_slots = pl.n_runs + B;
@@ -767,11 +868,18 @@ int debug_validate(const int32_t* bt, long long bt_stride, const int32_t* ctx, i
 }
 
 // Shared body of paged_decode_attn and paged_decode_attn_partial.
+bool finite(float x) {
+  uint32_t bits;
+  std::memcpy(&bits, &x, sizeof(bits));
+  return (bits & 0x7F800000u) != 0x7F800000u;
+}
+
 int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const void* k_cache,
                   const void* v_cache, const int32_t* bt, int64_t bt_stride, const int32_t* ctx,
                   int B, int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
-                  int max_blocks, float scale, int partition_tokens, void* workspace,
-                  size_t workspace_bytes, void* stream_ptr) {
+                  int max_blocks, float scale, bool fp8, float k_scale, float v_scale,
+                  int partition_tokens, void* workspace, size_t workspace_bytes,
+                  void* stream_ptr) {
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks, partition_tokens);
   if (rc != PDA_OK) return rc;
   if (B == 0) return ok();
@@ -781,11 +889,10 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
     return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
                 (long long)bt_stride, max_blocks);
   if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
-  uint32_t scale_bits;
-  std::memcpy(&scale_bits, &scale, sizeof(scale_bits));
-  if ((scale_bits & 0x7F800000u) == 0x7F800000u) return fail(PDA_EINVAL, "scale must be finite");
+  if (!finite(scale) || !finite(k_scale) || !finite(v_scale))
+    return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens);
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, fp8);
   if (workspace_bytes < pl.total)
     return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
                 pl.total);
@@ -798,8 +905,8 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   char* ws = static_cast<char*>(workspace);
   SplitParams sp;
   sp.q = static_cast<const _Float16*>(q);
-  sp.k = static_cast<const _Float16*>(k_cache);
-  sp.v = static_cast<const _Float16*>(v_cache);
+  sp.k = k_cache;
+  sp.v = v_cache;
   sp.bt = bt;
   sp.ctx = ctx;
   sp.bt_stride = bt_stride;
@@ -811,8 +918,10 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.P = pl.P;
   sp.n_runs = pl.n_runs;
   sp.hg = pl.hg;
-  sp.qk_scale = std::fabs(scale) * kLog2e;
-  sp.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
+  const float score_scale = scale * k_scale;      // k = k_scale * decoded code for FP8
+  sp.qk_scale = std::fabs(score_scale) * kLog2e;
+  sp.q_sign = std::signbit(score_scale) ? 0x80008000u : 0u;
+  sp.v_scale = v_scale;
   sp.ws_o = reinterpret_cast<float*>(ws + pl.o_offset);
   sp.ws_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   sp.ws_hdr = reinterpret_cast<int32_t*>(ws + pl.hdr_offset);
@@ -820,11 +929,20 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.lse_out = lse_out;
   sp.out_f16 = out_f16 ? 1 : 0;
   const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
-  switch (Hq / Hkv) {
-    case 1: hipLaunchKernelGGL(split_kernel<1>, grid, block, 0, stream, sp); break;
-    case 2: hipLaunchKernelGGL(split_kernel<2>, grid, block, 0, stream, sp); break;
-    case 4: hipLaunchKernelGGL(split_kernel<4>, grid, block, 0, stream, sp); break;
-    default: hipLaunchKernelGGL(split_kernel<8>, grid, block, 0, stream, sp); break;
+  if (fp8) {
+    switch (Hq / Hkv) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, true>), grid, block, 0, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, 0, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, true>), grid, block, 0, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, true>), grid, block, 0, stream, sp); break;
+    }
+  } else {
+    switch (Hq / Hkv) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, false>), grid, block, 0, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, false>), grid, block, 0, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, false>), grid, block, 0, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, false>), grid, block, 0, stream, sp); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PDA_EHIP, "split kernel launch: %s", hipGetErrorString(e));
@@ -857,16 +975,18 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size, int max_bl
   if (!bytes) return fail(PDA_EINVAL, "bytes is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  *bytes = B == 0 ? 0 : make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens).total;
+  *bytes = B == 0 ? 0
+                  : std::max(make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, false).total,
+                             make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, true).total);
   return ok();
 }
 
 int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
-                         int partition_tokens, pda_layout* layout) {
+                         int partition_tokens, int kv_fp8, pda_layout* layout) {
   if (!layout) return fail(PDA_EINVAL, "layout is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens);
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, kv_fp8 != 0);
   layout->header_offset = pl.hdr_offset;
   layout->lse_offset = pl.lse_offset;
   layout->o_offset = pl.o_offset;
@@ -885,7 +1005,20 @@ int paged_decode_attn(void* out, const void* q, const void* k_cache, const void*
                       size_t workspace_bytes, void* stream) {
   return run_attention(true, out, lse_out, q, k_cache, v_cache, block_table, block_table_stride,
                        context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
-                       scale, partition_tokens, workspace, workspace_bytes, stream);
+                       scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
+                       stream);
+}
+
+int paged_decode_attn_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int64_t block_table_stride,
+                          const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                          int block_size, int64_t num_blocks, int max_blocks_per_seq, float scale,
+                          float k_scale, float v_scale, int partition_tokens, float* lse_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(true, out, lse_out, q, k_cache, v_cache, block_table, block_table_stride,
+                       context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                       scale, true, k_scale, v_scale, partition_tokens, workspace,
+                       workspace_bytes, stream);
 }
 
 int paged_decode_attn_partial(float* o, float* lse, const void* q, const void* k_cache,
@@ -897,7 +1030,22 @@ int paged_decode_attn_partial(float* o, float* lse, const void* q, const void* k
   if (B > 0 && !lse) return fail(PDA_EINVAL, "lse is null");
   return run_attention(false, o, lse, q, k_cache, v_cache, block_table, block_table_stride,
                        context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
-                       scale, partition_tokens, workspace, workspace_bytes, stream);
+                       scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
+                       stream);
+}
+
+int paged_decode_attn_partial_fp8(float* o, float* lse, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  int64_t block_table_stride, const int32_t* context_lens, int B,
+                                  int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
+                                  int max_blocks_per_seq, float scale, float k_scale,
+                                  float v_scale, int partition_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (B > 0 && !lse) return fail(PDA_EINVAL, "lse is null");
+  return run_attention(false, o, lse, q, k_cache, v_cache, block_table, block_table_stride,
+                       context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                       scale, true, k_scale, v_scale, partition_tokens, workspace,
+                       workspace_bytes, stream);
 }
 
 int merge_partials(void* out, float* lse_out, const float* o_parts, const float* lse_parts, int R,

@@ -36,6 +36,8 @@ BLOCK_SIZE = 16
 HEAD_DIM = 128
 K_POISON = 6.0e4        # would dominate any softmax it leaked into
 V_POISON = float("nan")  # would turn any output it leaked into into NaN
+FP8_POISON = 0x7F        # the E4M3 NaN code, for both FP8 pools
+FP8_MAX = 448.0          # largest finite E4M3 value
 
 
 @dataclasses.dataclass
@@ -54,6 +56,17 @@ class Case:
     rng_backend: str
     partition_tokens: int = 0    # 0 = let the library choose
     ranges: int = 0              # token ranges for the partial + merge workload
+    kv_dtype: str = "fp16"       # "fp16", or "fp8": E4M3 codes (uint8) with per-tensor scales
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def kv_bytes_per_elem(self):
+        return 1 if self.kv_dtype == "fp8" else 2
+
+    def attn_kwargs(self):
+        """The scale arguments paged_decode_attn needs for this cache."""
+        return {"k_scale": self.k_scale, "v_scale": self.v_scale} if self.kv_dtype == "fp8" else {}
 
     @property
     def B(self):
@@ -96,12 +109,17 @@ def _deal_blocks(lens, pool_blocks, width, perm, bs):
 def build_case(lens, Hq, Hkv, *, D=HEAD_DIM, bs=BLOCK_SIZE, pool_blocks=None,
                width=None, seed=0, device="cpu", poison=True,
                rng_backend="numpy", name="custom", rng=None,
-               partition_tokens=0, ranges=0) -> Case:
+               partition_tokens=0, ranges=0, kv_dtype="fp16") -> Case:
     """Draw Q, a shuffled K/V pool and block tables for the given lengths.
 
     ``pool_blocks`` defaults to exactly the blocks the lengths need; extra pool
     blocks are unused and, like the slots past each sequence's last token,
     filled with K = +-6e4 and V = NaN when ``poison`` is set.
+
+    ``kv_dtype="fp8"``: the N(0, 1) pools are quantised to E4M3 codes with one
+    scale per pool, amax / 448 (the per-tensor scales of an FP8 KV cache), by
+    torch's float8_e4m3fn conversion (round to nearest even); unowned slots
+    then hold the NaN code in both pools.
     """
     lens = np.asarray(lens, dtype=np.int64)
     B = len(lens)
@@ -138,10 +156,18 @@ def build_case(lens, Hq, Hkv, *, D=HEAD_DIM, bs=BLOCK_SIZE, pool_blocks=None,
     else:
         raise ValueError(rng_backend)
 
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8":
+        k_t, k_scale = _to_fp8(k_t)
+        v_t, v_scale = _to_fp8(v_t)
+    elif kv_dtype != "fp16":
+        raise ValueError(kv_dtype)
+
     if poison:
         _poison(k_t, v_t, lens, table, perm[used:], bs, rng)
 
-    return Case(name=name, q=q_t, k_cache=k_t, v_cache=v_t,
+    return Case(name=name, q=q_t, k_cache=k_t, v_cache=v_t, kv_dtype=kv_dtype,
+                k_scale=k_scale, v_scale=v_scale,
                 block_table=torch.from_numpy(table.astype(np.int32)).to(device),
                 context_lens=torch.from_numpy(lens.astype(np.int32)).to(device),
                 scale=fp32_scale(D), lens=lens, block_table_host=table, seed=seed,
@@ -149,16 +175,50 @@ def build_case(lens, Hq, Hkv, *, D=HEAD_DIM, bs=BLOCK_SIZE, pool_blocks=None,
                 ranges=ranges)
 
 
+def _to_fp8(pool):
+    """E4M3 codes (uint8) of pool / s and the per-tensor scale s = amax / 448."""
+    amax = max(float(pool.abs().max()), 1e-12)
+    scale = float(np.float32(amax / FP8_MAX))
+    codes = torch.empty(pool.shape, dtype=torch.uint8, device=pool.device)
+    chunk = max(1, (1 << 26) // max(1, pool[0].numel()))
+    for lo in range(0, pool.shape[0], chunk):
+        x = pool[lo:lo + chunk].float() / scale
+        codes[lo:lo + chunk] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
 def _poison(k_t, v_t, lens, table, unused_blocks, bs, rng):
     """Fill every slot no sequence owns: unused blocks and last-block tails."""
     Hkv, D = k_t.shape[2], k_t.shape[3]
     dev = k_t.device
+    if k_t.dtype == torch.uint8:                   # FP8 codes: the NaN code everywhere
+        blk, slot = _unowned_slots(lens, table, bs)
+        if len(unused_blocks):
+            idx = torch.from_numpy(np.asarray(unused_blocks, dtype=np.int64)).to(dev)
+            k_t[idx] = FP8_POISON
+            v_t[idx] = FP8_POISON
+        if blk:
+            bi = torch.tensor(blk, dtype=torch.int64, device=dev)
+            si = torch.tensor(slot, dtype=torch.int64, device=dev)
+            k_t[bi, si] = FP8_POISON
+            v_t[bi, si] = FP8_POISON
+        return
     if len(unused_blocks):
         idx = torch.from_numpy(np.asarray(unused_blocks, dtype=np.int64)).to(dev)
         sign = torch.from_numpy(rng.choice([-1.0, 1.0], size=(len(unused_blocks), bs, Hkv, D))
                                 .astype(np.float16)).to(dev)
         k_t[idx] = sign * K_POISON
         v_t[idx] = V_POISON
+    blk, slot = _unowned_slots(lens, table, bs)
+    if blk:
+        bi = torch.tensor(blk, dtype=torch.int64, device=dev)
+        si = torch.tensor(slot, dtype=torch.int64, device=dev)
+        k_t[bi, si] = K_POISON
+        v_t[bi, si] = V_POISON
+
+
+def _unowned_slots(lens, table, bs):
+    """(frame, slot) lists of the slots past each sequence's last token."""
     blk, slot = [], []
     for b, n in enumerate(lens):
         n = int(n)
@@ -167,11 +227,7 @@ def _poison(k_t, v_t, lens, table, unused_blocks, bs, rng):
             for s in range(n % bs, bs):
                 blk.append(last)
                 slot.append(s)
-    if blk:
-        bi = torch.tensor(blk, dtype=torch.int64, device=dev)
-        si = torch.tensor(slot, dtype=torch.int64, device=dev)
-        k_t[bi, si] = K_POISON
-        v_t[bi, si] = V_POISON
+    return blk, slot
 
 
 # --- the pages' workloads -----------------------------------------------------
@@ -179,16 +235,21 @@ def _poison(k_t, v_t, lens, table, unused_blocks, bs, rng):
 K1 = 1024   # "K" token counts are binary: 8K = 8192, 128K = 131072
 
 
-def tiny(seed=0, device="cpu", poison=True):
+def _suffix(kv_dtype):
+    return "" if kv_dtype == "fp16" else "_" + kv_dtype
+
+
+def tiny(seed=0, device="cpu", poison=True, kv_dtype="fp16"):
     """Batch 2, 8 query / 2 KV heads, context {37, 512}, 35 of a 128-block pool."""
     return build_case([37, 512], 8, 2, pool_blocks=128, seed=seed, device=device,
-                      poison=poison, rng_backend="numpy", name="tiny_b2_ctx37_512")
+                      poison=poison, rng_backend="numpy", kv_dtype=kv_dtype,
+                      name="tiny_b2_ctx37_512" + _suffix(kv_dtype))
 
 
-def llama8b_4k(seed=0, device="cpu", rng_backend="torch"):
+def llama8b_4k(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Llama-3.1-8B layer: batch 64, 32/8 heads, every context 4096 tokens."""
-    return build_case([4096] * 64, 32, 8, seed=seed, device=device,
-                      rng_backend=rng_backend, name="llama8b_b64_ctx4096")
+    return build_case([4096] * 64, 32, 8, seed=seed, device=device, kv_dtype=kv_dtype,
+                      rng_backend=rng_backend, name="llama8b_b64_ctx4096" + _suffix(kv_dtype))
 
 
 def agentic_lengths(rng, B=16, median=80 * K1, sigma=0.42, lo=8 * K1, hi=200 * K1):
@@ -201,12 +262,12 @@ def agentic_lengths(rng, B=16, median=80 * K1, sigma=0.42, lo=8 * K1, hi=200 * K
     return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
 
 
-def agentic_80k(seed=0, device="cpu", rng_backend="torch"):
+def agentic_80k(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Long-context agentic decode: batch 16, 32/8 heads, P = 512 partitions."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = agentic_lengths(rng)
-    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng,
-                      rng_backend=rng_backend, name="agentic_b16_median80k",
+    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng, kv_dtype=kv_dtype,
+                      rng_backend=rng_backend, name="agentic_b16_median80k" + _suffix(kv_dtype),
                       partition_tokens=512)
 
 
@@ -220,18 +281,19 @@ def ragged_lengths(rng, B=256):
     return lens
 
 
-def ragged_mixed(seed=0, device="cpu", rng_backend="torch"):
+def ragged_mixed(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Mixed ragged batch: 256 sequences, 32/8 heads."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = ragged_lengths(rng)
-    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng,
-                      rng_backend=rng_backend, name="ragged_b256_u32k")
+    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng, kv_dtype=kv_dtype,
+                      rng_backend=rng_backend, name="ragged_b256_u32k" + _suffix(kv_dtype))
 
 
-def disagg_merge(seed=0, device="cpu", rng_backend="torch"):
+def disagg_merge(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Batch 32, 32/8 heads, 128K tokens each, split into 4 token ranges."""
-    return build_case([128 * K1] * 32, 32, 8, seed=seed, device=device,
-                      rng_backend=rng_backend, name="disagg_b32_ctx128k_r4", ranges=4)
+    return build_case([128 * K1] * 32, 32, 8, seed=seed, device=device, kv_dtype=kv_dtype,
+                      rng_backend=rng_backend, name="disagg_b32_ctx128k_r4" + _suffix(kv_dtype),
+                      ranges=4)
 
 
 def range_views(case: Case, R: int):

@@ -81,9 +81,10 @@ typedef enum {
 
 /*
  * Bytes of device workspace paged_decode_attn and paged_decode_attn_partial
- * need for these sizes (*bytes; 0 when B == 0).  partition_tokens as in
- * paged_decode_attn.  The size depends on the device (its CU count sets the
- * number of work-groups), so query it on the device that will run the call.
+ * need for these sizes (*bytes; 0 when B == 0), enough for both the fp16 and
+ * the FP8 entry points.  partition_tokens as in paged_decode_attn.  The size
+ * depends on the device (its CU count sets the number of work-groups), so
+ * query it on the device that will run the call.
  */
 int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size,
                        int max_blocks_per_seq, int partition_tokens,
@@ -103,7 +104,8 @@ typedef struct {
 
 /*
  * Where the split-K partials live inside the workspace after a call, for
- * tests and debugging.  The schedule: each sequence's tokens are cut into
+ * tests and debugging (kv_fp8: 1 for the *_fp8 entry points, else 0; the
+ * number of runs depends on it).  The schedule: each sequence's tokens are cut into
  * units of P = unit_tokens tokens (the last one shorter); the units of all
  * sequences in order form one stream of U units, and run w is units
  * [w*k, (w+1)*k), k = ceil(U / n_runs) (each run is computed by one
@@ -116,7 +118,7 @@ typedef struct {
  */
 int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size,
                          int max_blocks_per_seq, int partition_tokens,
-                         pda_layout* layout);
+                         int kv_fp8, pda_layout* layout);
 
 /*
  * Decode attention over a paged KV cache (see the top of this file).
@@ -178,6 +180,39 @@ int paged_decode_attn_partial(float* o, float* lse, const void* q,
                               float scale, int partition_tokens,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * FP8 KV cache: as paged_decode_attn / paged_decode_attn_partial, with
+ * k_cache and v_cache holding one FP8 E4M3 code per element (1 byte; the OCP
+ * 8-bit format: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN) in the same [num_blocks, block_size, Hkv, D]
+ * layout, and per-tensor scales: a stored K code c stands for
+ * k_scale * value(c), a V code for v_scale * value(c).  This is the quantised
+ * KV cache of "4. Quantised KV cache" on the page "Optimising decode in vLLM:
+ * squeezing every token out of small hardware" (kv_cache_dtype fp8 with
+ * per-tensor scales); it halves the bytes read per token.  Codes are decoded
+ * exactly; arithmetic is as in the fp16 entry points.  NaN codes in valid
+ * tokens give undefined results.
+ */
+int paged_decode_attn_fp8(void* out, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          int64_t block_table_stride,
+                          const int32_t* context_lens, int B, int Hq, int Hkv,
+                          int D, int block_size, int64_t num_blocks,
+                          int max_blocks_per_seq, float scale, float k_scale,
+                          float v_scale, int partition_tokens, float* lse_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+int paged_decode_attn_partial_fp8(float* o, float* lse, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table,
+                                  int64_t block_table_stride,
+                                  const int32_t* context_lens, int B, int Hq,
+                                  int Hkv, int D, int block_size,
+                                  int64_t num_blocks, int max_blocks_per_seq,
+                                  float scale, float k_scale, float v_scale,
+                                  int partition_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Merge R partials over disjoint token ranges into attention over their

@@ -52,3 +52,14 @@ def compare_lse(lse, ref, tol=LSE_TOL, what="lse"):
     worst = float(d.max()) if d.size else 0.0
     assert worst <= tol, f"{what}: max |lse error| {worst:.3e} > {tol:.1e}"
     return worst
+
+
+def compare_ulps(a, b, ulps=2, rowwise=False, what="merge"):
+    """|a - b| <= ulps fp16 ulps, element by element, or of each row's largest |b| (rowwise)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    ref = np.abs(b).max(axis=-1, keepdims=True) if rowwise else np.abs(b)
+    unit = np.maximum(np.spacing(ref.astype(np.float16)).astype(np.float64), 2.0 ** -24)
+    worst = float((np.abs(a - b) / unit).max())
+    assert worst <= ulps, f"{what}: {worst:.1f} fp16 ulps > {ulps}"
+    return worst

@@ -16,7 +16,7 @@ import torch
 import decode_attention_paged_attn_amd as pda
 from decode_attention_paged_attn_amd import workloads as W
 import oracle.paged_attention as O
-from tests.parity import compare_lse, compare_out, to_np
+from tests.parity import compare_lse, compare_out, compare_ulps, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -36,17 +36,26 @@ def _say(msg):
 
 
 def run(case, partition_tokens=0, **kw):
-    _say(f"[run] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={partition_tokens}")
+    _say(f"[run] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={partition_tokens} "
+         f"kv={case.kv_dtype}")
     out, lse = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                      case.context_lens, case.scale, return_lse=True,
-                                     partition_tokens=partition_tokens, **kw)
+                                     partition_tokens=partition_tokens, **case.attn_kwargs(),
+                                     **kw)
     torch.cuda.synchronize()
     return out, lse
 
 
-def oracle_full(case):
-    q, k, v, table, lens = W.host_full(case)
+def oracle_of(case, q, k, v, table, lens):
+    """The oracle's attention for this case's cache format on host copies."""
+    if case.kv_dtype == "fp8":
+        return O.paged_decode_attention_fp8(q, k, v, table, lens, case.scale, case.k_scale,
+                                            case.v_scale)
     return O.paged_decode_attention(q, k, v, table, lens, case.scale)
+
+
+def oracle_full(case):
+    return oracle_of(case, *W.host_full(case))
 
 
 # --- small cases, checked in full ----------------------------------------------
@@ -149,8 +158,10 @@ def test_split_partials_in_workspace(P):
     lens = [1, 63, 64, 65, 200, 777, 5000, 9000, 3000]
     case = W.build_case(lens, 8, 2, seed=8, device="cuda")
     width = case.block_table.shape[1]
-    lay = pda.workspace_layout(case.B, case.Hq, case.Hkv, width, P)
-    ws = torch.zeros(lay["total_bytes"], dtype=torch.uint8, device="cuda")
+    lay = pda.workspace_layout(case.B, case.Hq, case.Hkv, width, P, kv_fp8=False)
+    ws = torch.zeros(pda.workspace_size(case.B, case.Hq, case.Hkv, width, P), dtype=torch.uint8,
+                     device="cuda")
+    assert ws.numel() >= lay["total_bytes"]
     out, lse = run(case, P, workspace=ws)
     raw = ws.cpu()
     nsl, Hq = lay["n_slots"], case.Hq
@@ -262,7 +273,7 @@ def test_graph_capture_replays_match_eager():
 
 def _check_sampled(case, out, lse, seq_ids):
     q, k, v, table, lens = W.host_sequences(case, seq_ids)
-    ref, ref_lse = O.paged_decode_attention(q, k, v, table, lens, case.scale)
+    ref, ref_lse = oracle_of(case, q, k, v, table, lens)
     o, l = to_np(out), to_np(lse)
     for i, b in enumerate(seq_ids):
         compare_out(o[b], ref[i], what=f"{case.name} seq {b} (ctx {lens[i]})")
@@ -365,3 +376,74 @@ def test_scale_sign_and_size(scale):
     ref, ref_lse = oracle_full(case)
     compare_out(to_np(out), ref)
     compare_lse(to_np(lse), ref_lse)
+
+
+# --- FP8 (E4M3) KV cache --------------------------------------------------------
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_fp8_tiny_workload(P):
+    case = W.tiny(device="cuda", kv_dtype="fp8")
+    out, lse = run(case, P)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+def test_fp8_ragged_lengths(G, Hkv):
+    case = W.build_case(RAGGED, G * Hkv, Hkv, pool_blocks=sum(-(-n // 16) for n in RAGGED) + 7,
+                        seed=200 + G, device="cuda", name=f"ragged_fp8_G{G}", kv_dtype="fp8")
+    out, lse = run(case)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_fp8_every_code_decodes_exactly():
+    """One token per sequence: out = v_scale * value(code), for every finite code."""
+    case = W.build_case([1] * 4, 32, 8, seed=16, device="cuda", kv_dtype="fp8")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    v = case.v_cache.cpu().numpy()
+    allc = np.resize(codes, 4 * 8 * 128).reshape(4, 8, 128)
+    for b in range(4):
+        v[int(case.block_table_host[b, 0]), 0] = allc[b]
+    case.v_cache.copy_(torch.from_numpy(v))
+    case.v_scale = 0.5                                   # a power of two keeps fp16 exact
+    out, _ = run(case)
+    want = (0.5 * O.fp8_e4m3_decode(allc)).astype(np.float16)
+    for b in range(4):
+        for h in range(32):
+            assert np.array_equal(out[b, h].cpu().numpy(), want[b, h // 4]), (b, h)
+
+
+@pytest.mark.parametrize("name,P", [("llama8b_4k", 0), ("agentic_80k", 512), ("ragged_mixed", 0)])
+def test_fp8_full_size_workload(name, P):
+    case = W.CONFIGS[name](device="cuda", kv_dtype="fp8")
+    out, lse = run(case, P)
+    assert torch.isfinite(out.float()).all()
+    _check_sampled(case, out, lse, _sample(case.lens, np.random.default_rng(1)))
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_fp8_partial_api_and_merge():
+    R, per = 4, 512
+    case = W.build_case([R * per] * 3, 32, 8, seed=17, device="cuda", kv_dtype="fp8")
+    cols = per // 16
+    o_parts, l_parts = [], []
+    for r in range(R):
+        bt = case.block_table[:, r * cols:(r + 1) * cols]
+        ln = torch.full((case.B,), per, dtype=torch.int32, device="cuda")
+        o, l = pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln,
+                                             case.scale, **case.attn_kwargs())
+        o_parts.append(o)
+        l_parts.append(l)
+    merged, mlse = pda.merge_partials(torch.stack(o_parts).contiguous(),
+                                      torch.stack(l_parts).contiguous())
+    single, _ = run(case)
+    # p enters the FP8 PV products rounded to fp16, so the two schedules agree to
+    # fp16 ulps of each row's scale (element-wise near zero they may differ more)
+    compare_ulps(to_np(merged), to_np(single), ulps=2, rowwise=True)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(merged), ref)
+    compare_lse(to_np(mlse), ref_lse)
