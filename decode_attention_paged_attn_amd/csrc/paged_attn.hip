@@ -81,6 +81,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -196,7 +197,7 @@ template <int G>
 struct Seg {
   float m[G];               // running max per head (base 2), uniform
   float lp[4];              // running sum of p of this lane's token slot, heads 4c+r
-  float acc[G][8];          // output dims 8*ds .. 8*ds+7 over this lane's token row
+  f32x4 acc[8];             // PV MFMA tiles: lane (c, n), tile u, reg r = head 4c+r, dim 8n+u
 };
 
 template <int G, bool kMasked, bool kFp8>
@@ -266,9 +267,13 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
       st.lp[r] *= a;
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+    for (int r = 0; r < kR; ++r) {
+      float a = alpha[r];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[j][e] *= alpha[j];
+      for (int cc = 1; cc * 4 + r < G; ++cc) a = c == cc ? alpha[cc * 4 + r] : a;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) st.acc[u][r] *= a;
+    }
   }
 
   // p = exp2(scale' * s - m); lane (c, t) owns p of heads 4c + r for token t.
@@ -284,81 +289,63 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
     if (kMasked) pr[r] = tok_valid ? pr[r] : 0.0f;
     st.lp[r] += pr[r];
   }
-  // hand p to the V layout through LDS: lds_p[token][head]
-  if (4 * c < G) {
-    if constexpr (kR == 4) {
-      *reinterpret_cast<f32x4*>(lds_p + t * G + 4 * c) = f32x4{pr[0], pr[1], pr[2], pr[3]};
-    } else if constexpr (kR == 2) {
-      *reinterpret_cast<f32x2*>(lds_p + t * G) = f32x2{pr[0], pr[1]};
-    } else {
-      lds_p[t] = pr[0];
+  // P as the A operand of the PV MFMAs (16x16x16, fp16): lane (c, m) holds
+  // p[head m][tokens c, 4+c, 8+c, 12+c].  It goes through a 16x16 fp16 LDS tile
+  // laid out [head][c][i] = p[head][4i + c]; p is rounded to fp16 for the product.
+  {
+    _Float16* tile = reinterpret_cast<_Float16*>(lds_p);
+    if (4 * c < G) {
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+        tile[(4 * c + r) * 16 + (t & 3) * 4 + (t >> 2)] = static_cast<_Float16>(pr[r]);
     }
   }
-  float pv[4][G];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float* src = lds_p + (4 * i + tg) * G;
-    if constexpr (G >= 4) {
-#pragma unroll
-      for (int j4 = 0; j4 < G; j4 += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + j4);
-        pv[i][j4] = x[0];
-        pv[i][j4 + 1] = x[1];
-        pv[i][j4 + 2] = x[2];
-        pv[i][j4 + 3] = x[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < G; ++j) pv[i][j] = src[j];
-    }
-  }
+  half4_t pa = {0, 0, 0, 0};
+  if (t < G) pa = *reinterpret_cast<const half4_t*>(reinterpret_cast<const _Float16*>(lds_p) +
+                                                   t * 16 + c * 4);
 
-  // acc += p v; a token past the end contributes an exact zero row (selected,
-  // so a NaN in an unused slot cannot leak through 0 * NaN)
+  // V as the B operands: tile u covers dims 8n + u (n = lane & 15); lane (c, n)
+  // needs v[token 4i + c][8n + u], i = 0..3, which is element u of its own four
+  // V loads.  A token past the end is an exact zero row (selected, so a NaN in
+  // an unused slot cannot leak through 0 * NaN).
   if constexpr (kFp8) {
-    // FP8: packed fp16 dot products over the token pairs (4i + tg, 4(i+1) + tg),
-    // i = 0, 2: the codes of the two tokens are interleaved byte by byte, so
-    // one exact E4M3 -> fp16 conversion yields (v[t0][d], v[t1][d]), and p of
-    // the two tokens is rounded to fp16 for the product (sums stay fp32).
     u32x2 vv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       vv[i] = (!kMasked || 4 * i + tg < nvalid) ? vr[i] : u32x2{0u, 0u};   // code 0 = +0
 #pragma unroll
-    for (int i0 = 0; i0 < 4; i0 += 2) {
-      half2_t pp[G];
+    for (int w = 0; w < 2; ++w) {
+      // 4x4 byte transpose of the four tokens' codes of dims 4w .. 4w+3
+      const unsigned ab_lo = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05010400u);
+      const unsigned ab_hi = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07030602u);
+      const unsigned cd_lo = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05010400u);
+      const unsigned cd_hi = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07030602u);
+      const unsigned tcol[4] = {__builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),
+                                __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),
+                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),
+                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};
 #pragma unroll
-      for (int j = 0; j < G; ++j)
-        pp[j] = half2_t{static_cast<_Float16>(pv[i0][j]), static_cast<_Float16>(pv[i0 + 1][j])};
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {                  // dims 4w .. 4w+3 of this lane's 8
-        const unsigned a = vv[i0][w], b = vv[i0 + 1][w];
-        const unsigned lo = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-        const unsigned hi = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-        const half2_t v2[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false),
-                               __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int j = 0; j < G; ++j)
-            st.acc[j][4 * w + e] = __builtin_amdgcn_fdot2(pp[j], v2[e], st.acc[j][4 * w + e],
-                                                          false);
+      for (int e = 0; e < 4; ++e) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, true);
+        const half4_t vb = {lo[0], lo[1], hi[0], hi[1]};
+        st.acc[4 * w + e] =
+            __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, st.acc[4 * w + e], 0, 0, 0);
       }
     }
   } else {
+    u32x4 vv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = !kMasked || (4 * i + tg < nvalid);
-      const _Float16* vh = reinterpret_cast<const _Float16*>(&vr[i]);
+    for (int i = 0; i < 4; ++i)
+      vv[i] = (!kMasked || 4 * i + tg < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float x = static_cast<float>(vh[e]);
-        if (kMasked) x = valid ? x : 0.0f;
-#pragma unroll
-        for (int j = 0; j < G; ++j) st.acc[j][e] = fmaf(pv[i][j], x, st.acc[j][e]);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int w = u / 2;
+      const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+      const unsigned d01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
+      const unsigned d23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
+      const half4_t vb = __builtin_bit_cast(half4_t, u32x2{d01, d23});
+      st.acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, st.acc[u], 0, 0, 0);
     }
   }
 }
@@ -402,11 +389,9 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
 
   Seg<G> st;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    st.m[j] = -INFINITY;
+  for (int j = 0; j < G; ++j) st.m[j] = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.0f;
-  }
+  for (int u = 0; u < 8; ++u) st.acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int r = 0; r < 4; ++r) st.lp[r] = 0.0f;
 
@@ -472,34 +457,39 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
 #pragma unroll
     for (int cc = 0; cc * 4 + r < G; ++cc) l_tot[cc * 4 + r] = uniform_f32(x, 16 * cc);
   }
+  // lane (c, n) holds head 4c + r, dims 8n .. 8n+7 in tiles 0..7, register r
   const int hq0 = g * G;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    float o[8];
+  for (int r = 0; r < kR; ++r) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = add_xor32(add_xor16(st.acc[j][e]));
-    if ((j & 3) != tg) continue;
-    const float inv = p.v_scale / l_tot[j];
-    const float lse = (st.m[j] + __builtin_log2f(l_tot[j])) * kLn2;
-    if (whole) {
-      const long long dst = ((long long)b * p.Hq + hq0 + j) * kD + 8 * ds;
-      if (p.out_f16) {
-        half8_t h;
+    for (int cc = 0; cc * 4 + r < G; ++cc) {
+      if (c != cc) continue;
+      const int j = cc * 4 + r;
+      const float inv = p.v_scale / l_tot[j];
+      const float lse = (st.m[j] + __builtin_log2f(l_tot[j])) * kLn2;
+      float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(o[e] * inv);
-        *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = h;
+      for (int u = 0; u < 8; ++u) o[u] = st.acc[u][r] * inv;
+      if (whole) {
+        const long long dst = ((long long)b * p.Hq + hq0 + j) * kD + 8 * ds;
+        if (p.out_f16) {
+          half8_t h;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(o[e]);
+          *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = h;
+        } else {
+          float* d = static_cast<float*>(p.out) + dst;
+          *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+        if (p.lse_out && ds == 0) p.lse_out[(long long)b * p.Hq + hq0 + j] = lse;
       } else {
-        float* d = static_cast<float*>(p.out) + dst;
-        *reinterpret_cast<f32x4*>(d) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-        *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        const long long sl = (long long)slot * p.Hq + hq0 + j;
+        float* d = p.ws_o + sl * kD + 8 * ds;
+        *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        if (ds == 0) p.ws_lse[sl] = lse;
       }
-      if (p.lse_out && ds == 0) p.lse_out[(long long)b * p.Hq + hq0 + j] = lse;
-    } else {
-      const long long sl = (long long)slot * p.Hq + hq0 + j;
-      float* d = p.ws_o + sl * kD + 8 * ds;
-      *reinterpret_cast<f32x4*>(d) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-      if (ds == 0) p.ws_lse[sl] = lse;
     }
   }
 }
@@ -508,7 +498,7 @@ template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMaxWavesPerWG)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu(G, kFp8))))
 void split_kernel(SplitParams p) {
-  __shared__ float lds[kMaxWavesPerWG][kBS * G];
+  __shared__ float lds[kMaxWavesPerWG][kBS * 16 / 2];   // one 16x16 fp16 P tile per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_hgroups = p.Hkv / p.hg;

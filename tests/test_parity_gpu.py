@@ -16,7 +16,7 @@ import torch
 import decode_attention_paged_attn_amd as pda
 from decode_attention_paged_attn_amd import workloads as W
 import oracle.paged_attention as O
-from tests.parity import compare_lse, compare_out, compare_ulps, to_np
+from tests.parity import ROW_REL_TOL, compare_lse, compare_out, compare_ulps, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +152,16 @@ def test_bitwise_deterministic():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
+def _p_rounding_bound(v):
+    """Largest move of a normalised output from rounding p to fp16 before PV.
+
+    With p_i >= 0 and relative rounding |d_i| <= 2^-11,
+    |sum d_i p_i v_i| / sum p_i <= 2^-11 max|v|; 1e-5 covers fp32 summation.
+    Poison (NaN) slots in the pool are ignored.
+    """
+    return 2.0 ** -11 * float(np.nanmax(np.abs(np.asarray(v, dtype=np.float64)))) + 1e-5
+
+
 @pytest.mark.parametrize("P", [0, 64, 2048])
 def test_split_partials_in_workspace(P):
     """Every stored partial equals the oracle's attention over the same token range."""
@@ -189,7 +199,8 @@ def test_split_partials_in_workspace(P):
             heads = slice(g * 4, g * 4 + 4)
             o_ref, l_ref = O.attend(q[b, heads], K, V, case.scale)
             compare_lse(l_ws[w + b, heads], l_ref, what=f"lse w={w} b={b} [{lo},{hi})")
-            compare_out(o_ws[w + b, heads], o_ref, abs_tol=1e-4, row_rel_tol=1e-4,
+            compare_out(o_ws[w + b, heads], o_ref, abs_tol=_p_rounding_bound(V),
+                        row_rel_tol=ROW_REL_TOL,
                         what=f"o w={w} b={b} [{lo},{hi})")
     assert split > 0, "the case should split at least one sequence"
     ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
@@ -213,9 +224,9 @@ def test_partial_api_and_merge():
     merged, mlse = pda.merge_partials(torch.stack(o_parts).contiguous(),
                                       torch.stack(l_parts).contiguous())
     single, slse = run(case)
-    ulp = np.abs(to_np(merged) - to_np(single)) / np.maximum(
-        np.spacing(np.abs(to_np(single)).astype(np.float16)).astype(np.float64), 2.0 ** -24)
-    assert ulp.max() <= 2, ulp.max()
+    # p enters the PV product rounded to fp16 relative to each range's own
+    # running max, so the two schedules agree to fp16 ulps of each row's scale
+    compare_ulps(to_np(merged), to_np(single), ulps=2, rowwise=True)
     q, k, v, table, ln = W.host_full(case)
     ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
     compare_out(to_np(merged), ref)
@@ -224,7 +235,8 @@ def test_partial_api_and_merge():
     for r in range(R):
         o_ref, l_ref = O.partial_attention(q, k, v, table[:, r * cols:(r + 1) * cols],
                                            [per] * 3, case.scale)
-        compare_out(to_np(o_parts[r]), o_ref, abs_tol=1e-4, row_rel_tol=1e-4)
+        compare_out(to_np(o_parts[r]), o_ref, abs_tol=_p_rounding_bound(v),
+                    row_rel_tol=ROW_REL_TOL)
         compare_lse(to_np(l_parts[r]), l_ref)
 
 
@@ -313,10 +325,7 @@ def test_full_size_partial_merge():
                                       o=o_parts[r], lse=l_parts[r])
     merged, mlse = pda.merge_partials(o_parts, l_parts)
     single, slse = run(case)
-    m, s = to_np(merged), to_np(single)
-    ulp = np.abs(m - s) / np.maximum(np.spacing(np.abs(s).astype(np.float16)).astype(np.float64),
-                                     2.0 ** -24)
-    assert ulp.max() <= 2, ulp.max()
+    compare_ulps(to_np(merged), to_np(single), ulps=2, rowwise=True)
     _check_sampled(case, merged, mlse, [0, 17, 31])
     del case
     torch.cuda.empty_cache()
