@@ -28,13 +28,21 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "KV-read GB/s and % of HBM peak; decode-attn tokens/s at Llama-3.1-8B shape"
-SRC = os.path.join(ROOT, "decode_attention_paged_attn_amd", "csrc", "paged_attn.hip")
+CSRC = os.path.join(ROOT, "decode_attention_paged_attn_amd", "csrc")
+# the sources each timed kernel is built from (a counter record is valid only
+# for the sources it was taken on)
+KERNEL_SOURCES = {
+    "attention": ("paged_attn.hip", "pda_common.h"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash():
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(op="attention"):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[op]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kv_bytes(lens, Hkv, D=128, elem=2):
@@ -42,14 +50,14 @@ def kv_bytes(lens, Hkv, D=128, elem=2):
     return int(sum(int(n) for n in lens)) * 2 * Hkv * D * elem
 
 
-def measured_traffic(config_name):
-    """Counter-measured HBM bytes per call, if taken on the current kernel source."""
+def measured_traffic(key, op="attention"):
+    """Counter-measured HBM bytes per call, if taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(config_name)
+            rec = json.load(f).get(key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256_16") != source_hash():
+    if not rec or rec.get("source_sha256_16") != source_hash(op):
         return None
     return rec.get("bytes_per_call")
 
@@ -247,7 +255,7 @@ def main():
     m = measure(case, P, args.steps, args.warmup, args.flush_mib)
     nbytes = m["kv_bytes"]
     B, Hq, Hkv = case.B, case.Hq, case.Hkv
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(f"{args.config}/{case.kv_dtype}")
     rec = {
         "metric": METRIC,
         "value": m["value"],

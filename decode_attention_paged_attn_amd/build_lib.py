@@ -1,18 +1,19 @@
 """Compile the HIP library in-tree for gfx950.
 
 ``python -m decode_attention_paged_attn_amd.build_lib`` (or ``build()``) runs
-hipcc on ``csrc/paged_attn.hip`` and writes ``libpagedattn.so`` next to this
-file.  It always recompiles.
+hipcc on the HIP sources under ``csrc/`` and links them into
+``libpagedattn.so`` next to this file.  It always recompiles.
 """
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "paged_attn.hip")
+CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
@@ -38,7 +39,8 @@ def hipcc():
 
 def build(verbose=False, extra_flags=()):
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -30,10 +30,12 @@
 //     64 contiguous bytes of all 16 token rows); QK^T of the 16 tokens and G
 //     heads is 4 v_mfma_f32_16x16x32_f16 (fp16 products, fp32 sums);
 //   * softmax: fp32 online softmax with a running max per head; scores are in
-//     base-2 units (the scale is folded with log2(e)); p goes through a
-//     small LDS slot to the lanes that hold V;
+//     base-2 units (the scale is folded with log2(e)); p is rounded to fp16
+//     and reaches the A-operand layout of the PV product through a 16x16 LDS
+//     tile;
 //   * V: per block, 4 loads of 16 bytes per lane (each load instruction reads
-//     4 whole 256-byte token rows); acc += p * v with fp16 -> fp32 fused FMAs.
+//     4 whole 256-byte token rows); p.V is 8 v_mfma_f32_16x16x16_f16 whose B
+//     operands are byte permutes of the lane's own V loads (fp32 sums).
 // A segment that is a whole sequence writes the final output; otherwise its
 // normalised partial and log-sum-exp go to workspace slot w + b, and the
 // merge kernel combines the slots of each (sequence, query head).
@@ -49,21 +51,44 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
-#include <type_traits>
 #include <vector>
 
 #include "paged_attn.h"
+#include "pda_common.h"
+
+namespace pda {
+
+thread_local std::string t_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return code;
+}
+
+int ok() {
+  t_last_error.clear();
+  return PDA_OK;
+}
+
+}  // namespace pda
 
 namespace {
 
-constexpr int kD = 128;               // head dim
-constexpr int kBS = 16;               // tokens per block
-constexpr int kWave = 64;
+using namespace pda;
+
 constexpr int kMaxKvHeads = 8;        // one wave per KV head
 constexpr int kMaxWavesPerWG = 4;     // KV heads of one work-group
-// occupancy target of the split kernel: 2 waves per SIMD with two blocks of
-// K/V in flight per wave measured faster than 3 waves per SIMD squeezed into
-// 168 VGPRs
+// occupancy target of the split kernel and the depth of its ring of K/V
+// register buffers (blocks in flight + 1).  Measured on MI355X: fp16 runs best
+// at 2 waves per SIMD with ring 2 (ring 3 is no faster, 3 waves per SIMD in
+// 168 VGPRs are slower); FP8 blocks are half the bytes and run best at 2
+// waves per SIMD with ring 4 (rings 2, 3, 5, 6 and 8, and 3 or 4 waves per
+// SIMD, are slower).
 #ifndef PDA_WAVES_PER_EU_FP8
 #define PDA_WAVES_PER_EU_FP8 2
 #endif
@@ -71,79 +96,11 @@ constexpr int kMaxWavesPerWG = 4;     // KV heads of one work-group
 #define PDA_RING_FP16 2
 #endif
 #ifndef PDA_RING_FP8
-#define PDA_RING_FP8 3
+#define PDA_RING_FP8 4
 #endif
 constexpr int waves_per_eu(int G, bool fp8) { return fp8 && G <= 4 ? PDA_WAVES_PER_EU_FP8 : 2; }
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kHdrInts = 4;           // k, U, n_runs, P, then units_before[b]
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// ---------------------------------------------------------------------------
-// cross-lane helpers
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
-}
-
-// All-reduce over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-  x += dpp_f32<0x141>(x);  // row_half_mirror: other quad of the half row
-  x += dpp_f32<0x140>(x);  // row_mirror: other half of the row
-  return x;
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f32<0xB1>(x));
-  x = fmaxf(x, dpp_f32<0x4E>(x));
-  x = fmaxf(x, dpp_f32<0x141>(x));
-  x = fmaxf(x, dpp_f32<0x140>(x));
-  return x;
-}
-
-// x[l] + x[l ^ 16] and x[l] + x[l ^ 32].  (Once per segment, so a plain
-// shuffle; the gfx950 lane-swap builtins mis-compile here when both of their
-// operands are the same value.)
-__device__ __forceinline__ float add_xor16(float x) { return x + __shfl_xor(x, 16, kWave); }
-__device__ __forceinline__ float add_xor32(float x) { return x + __shfl_xor(x, 32, kWave); }
-
-__device__ __forceinline__ int wave_sum_i32(int x) {
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-  return x;
-}
-__device__ __forceinline__ int wave_inclusive_scan_i32(int x, int lane) {
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(x, o, kWave);
-    if (lane >= o) x += t;
-  }
-  return x;
-}
-__device__ __forceinline__ float wave_max_f32(float x) {
-  for (int m = 1; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
-}
-__device__ __forceinline__ float wave_sum_f32(float x) {
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-  return x;
-}
-
-__device__ __forceinline__ float uniform_f32(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) {  // v_exp_f32; exp2(-inf) = 0
-  return __builtin_amdgcn_exp2f(x);
-}
 
 // ---------------------------------------------------------------------------
 // split kernel
@@ -176,22 +133,6 @@ __device__ __forceinline__ int seq_len(const SplitParams& p, int b) {
   return min(max(p.ctx[b], 0), p.max_tokens);
 }
 
-// K/V element storage.  fp16 elements are used as stored.  FP8 elements are
-// E4M3 codes, decoded exactly (every E4M3 value is an fp16 value) to fp16 for
-// the MFMA operands of K and to fp32 for V; the per-tensor scales are folded
-// into the softmax scale and the output normalisation.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-template <bool kFp8>
-struct KvFmt {
-  static constexpr int kElemBytes = kFp8 ? 1 : 2;
-  static constexpr int kKLoads = kFp8 ? 2 : 4;     // 16-byte K loads per lane per block
-  using VRow = typename std::conditional<kFp8, u32x2, u32x4>::type;   // 8 V elements
-  // MFMA k-chunk i (8 dims), lane group c: first head dimension it covers
-  __device__ static constexpr int q_dim(int i, int c) {
-    return kFp8 ? 64 * (i / 2) + 16 * c + 8 * (i % 2) : 32 * i + 8 * c;
-  }
-};
-
 // Per-wave state of one segment for KV head g and its G query heads.
 template <int G>
 struct Seg {
@@ -211,23 +152,7 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
 
   // K as MFMA B operands: lane (c, t) holds token t, dims KvFmt::q_dim(i, c) + 0..7
   half8_t kop[4];
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kr[j][w], 1.0f, false);
-        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(kr[j][w], 1.0f, true);
-        half8_t& dst = kop[2 * j + w / 2];
-        dst[4 * (w % 2) + 0] = lo[0];
-        dst[4 * (w % 2) + 1] = lo[1];
-        dst[4 * (w % 2) + 2] = hi[0];
-        dst[4 * (w % 2) + 3] = hi[1];
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kop[i] = __builtin_bit_cast(half8_t, kr[i]);
-  }
+  k_operands<kFp8>(kr, kop);
 
   // scores: D[head][token] = sum_d q[head][d] k[token][d]
   f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -304,50 +229,7 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
   if (t < G) pa = *reinterpret_cast<const half4_t*>(reinterpret_cast<const _Float16*>(lds_p) +
                                                    t * 16 + c * 4);
 
-  // V as the B operands: tile u covers dims 8n + u (n = lane & 15); lane (c, n)
-  // needs v[token 4i + c][8n + u], i = 0..3, which is element u of its own four
-  // V loads.  A token past the end is an exact zero row (selected, so a NaN in
-  // an unused slot cannot leak through 0 * NaN).
-  if constexpr (kFp8) {
-    u32x2 vv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vv[i] = (!kMasked || 4 * i + tg < nvalid) ? vr[i] : u32x2{0u, 0u};   // code 0 = +0
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      // 4x4 byte transpose of the four tokens' codes of dims 4w .. 4w+3
-      const unsigned ab_lo = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05010400u);
-      const unsigned ab_hi = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07030602u);
-      const unsigned cd_lo = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05010400u);
-      const unsigned cd_hi = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07030602u);
-      const unsigned tcol[4] = {__builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),
-                                __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),
-                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),
-                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, false);
-        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, true);
-        const half4_t vb = {lo[0], lo[1], hi[0], hi[1]};
-        st.acc[4 * w + e] =
-            __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, st.acc[4 * w + e], 0, 0, 0);
-      }
-    }
-  } else {
-    u32x4 vv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vv[i] = (!kMasked || 4 * i + tg < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int w = u / 2;
-      const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-      const unsigned d01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
-      const unsigned d23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
-      const half4_t vb = __builtin_bit_cast(half4_t, u32x2{d01, d23});
-      st.acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, st.acc[u], 0, 0, 0);
-    }
-  }
+  pv_mfma<kMasked, kFp8>(st.acc, pa, vr, tg, nvalid);
 }
 
 // One wave: KV head g of sequence b over tokens [tok_lo, tok_hi).
@@ -699,23 +581,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // host side
 
-thread_local std::string t_last_error;
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  t_last_error = buf;
-  return code;
-}
-
-int ok() {
-  t_last_error.clear();
-  return PDA_OK;
-}
-
 // Per-device launch facts, filled once: CU count and how many split-kernel
 // work-groups of each (G, KV format, waves per work-group) shape fit on a CU.
 constexpr int kMaxDevices = 64;
@@ -780,8 +645,6 @@ int run_count(int G, int Hkv, bool fp8) {
   });
   return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][fp8 ? 1 : 0][hg] / n_hgroups);
 }
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plan {
   int P = 0;                 // unit length in tokens
@@ -858,12 +721,6 @@ int debug_validate(const int32_t* bt, long long bt_stride, const int32_t* ctx, i
 }
 
 // Shared body of paged_decode_attn and paged_decode_attn_partial.
-bool finite(float x) {
-  uint32_t bits;
-  std::memcpy(&bits, &x, sizeof(bits));
-  return (bits & 0x7F800000u) != 0x7F800000u;
-}
-
 int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const void* k_cache,
                   const void* v_cache, const int32_t* bt, int64_t bt_stride, const int32_t* ctx,
                   int B, int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
@@ -879,7 +736,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
     return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
                 (long long)bt_stride, max_blocks);
   if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
-  if (!finite(scale) || !finite(k_scale) || !finite(v_scale))
+  if (!finite_f32(scale) || !finite_f32(k_scale) || !finite_f32(v_scale))
     return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
   const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, fp8);
@@ -1100,7 +957,7 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
   return ok();
 }
 
-const char* pda_last_error(void) { return t_last_error.c_str(); }
+const char* pda_last_error(void) { return pda::t_last_error.c_str(); }
 
 const char* pda_version(void) { return "paged-decode-attn gfx950 0.2"; }
 
