@@ -7,24 +7,32 @@ built the calls raise; there is no fallback.
 """
 from ._binding import (  # noqa: F401
     PdaError,
+    cascade_decode_attn,
     library_path,
     load_library,
     merge_partials,
+    multi_query_workspace_size,
     paged_decode_attn,
     paged_decode_attn_partial,
     paged_kv_append,
+    paged_multi_query_attn,
+    paged_multi_query_attn_partial,
     workspace_layout,
     workspace_size,
 )
 
 __all__ = [
     "PdaError",
+    "cascade_decode_attn",
     "library_path",
     "load_library",
     "merge_partials",
+    "multi_query_workspace_size",
     "paged_decode_attn",
     "paged_decode_attn_partial",
     "paged_kv_append",
+    "paged_multi_query_attn",
+    "paged_multi_query_attn_partial",
     "workspace_layout",
     "workspace_size",
 ]

@@ -57,6 +57,15 @@ _SIGNATURES = {
     "merge_partials": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "paged_kv_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
                                  _c_int, _c_i64, _c_int, _vp]),
+    "pda_multi_query_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                _c_int, _c_int, ctypes.POINTER(_c_size)]),
+    "paged_multi_query_attn": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_i64, _vp,
+                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                        _c_float, _c_int, _c_int, _vp, _c_size, _vp]),
+    "paged_multi_query_attn_partial": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_i64,
+                                                _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                _c_i64, _c_int, _c_float, _c_int, _c_int, _vp,
+                                                _c_size, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -293,3 +302,127 @@ def paged_kv_append(k_cache, v_cache, k_new, v_new, block_table, context_lens,
     _check(load_library().paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
                                           _ptr(block_table), bt_stride, _ptr(context_lens), B,
                                           Hkv, D, bs, num_blocks, mb, _stream(dev)))
+
+
+# --- several query tokens per sequence, and cascade attention ------------------
+
+_mq_ws_cache = {}
+
+
+def multi_query_workspace_size(S, num_queries, Hq, Hkv, max_blocks_per_seq, partition_tokens=0,
+                               D=HEAD_DIM, block_size=BLOCK_SIZE, device=None):
+    """Bytes of workspace for a multi-query call of this shape."""
+    dev = torch.cuda.current_device() if device is None and torch.cuda.is_available() else device
+    key = (S, num_queries, Hq, Hkv, max_blocks_per_seq, partition_tokens, D, block_size, dev)
+    n = _mq_ws_cache.get(key)
+    if n is None:
+        c = _c_size(0)
+        _check(load_library().pda_multi_query_workspace_size(
+            S, num_queries, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens,
+            ctypes.byref(c)))
+        n = _mq_ws_cache[key] = int(c.value)
+    return n
+
+
+def _run_mq(partial, q, k_cache, v_cache, block_table, context_lens, query_start, scale, causal,
+            out, lse, need_lse, partition_tokens, workspace, max_blocks_per_seq):
+    if q.dtype != torch.float16 or k_cache.dtype != torch.float16 or v_cache.dtype != torch.float16:
+        raise TypeError("multi-query attention takes fp16 q and fp16 caches")
+    if (block_table.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start.dtype != torch.int32):
+        raise TypeError("block_table, context_lens and query_start must be int32")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t in (k_cache, v_cache, block_table, context_lens, query_start):
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q is [T, Hq, D]; k_cache and v_cache are [num_blocks, bs, Hkv, D]")
+    if not all(t.is_contiguous() for t in (q, k_cache, v_cache, context_lens, query_start)):
+        raise ValueError("q, k_cache, v_cache, context_lens and query_start must be contiguous")
+    S = context_lens.shape[0]
+    if (context_lens.dim() != 1 or block_table.dim() != 2 or block_table.shape[0] != S
+            or query_start.shape != (S + 1,)):
+        raise ValueError("block_table is [S, width], context_lens [S] and query_start [S + 1]")
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous (stride(1) == 1)")
+    T, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    width = block_table.shape[1]
+    mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    if mb > width:
+        raise ValueError("max_blocks_per_seq exceeds the block table width")
+    bt_stride = block_table.stride(0) if S > 0 else max(mb, 1)
+    ws_bytes = multi_query_workspace_size(S, T, Hq, Hkv, mb, partition_tokens, D, bs, dev.index)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace needs {ws_bytes} bytes")
+    out_dtype = torch.float32 if partial else torch.float16
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=dev)
+    if out.dtype != out_dtype or out.shape != (T, Hq, D) or not out.is_contiguous():
+        raise ValueError(f"output must be contiguous {out_dtype} [T, Hq, D]")
+    if lse is None and need_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (T, Hq)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous float32 [T, Hq]")
+    lib = load_library()
+    fn = lib.paged_multi_query_attn_partial if partial else lib.paged_multi_query_attn
+    _check(fn(_ptr(out), _ptr(lse), _ptr(q), _ptr(query_start), T, _ptr(k_cache), _ptr(v_cache),
+              _ptr(block_table), bt_stride, _ptr(context_lens), S, Hq, Hkv, D, bs, num_blocks, mb,
+              float(scale), int(bool(causal)), int(partition_tokens), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
+
+
+def paged_multi_query_attn(q, k_cache, v_cache, block_table, context_lens, query_start, scale,
+                           causal=True, out=None, lse_out=None, return_lse=False,
+                           partition_tokens=0, workspace=None, max_blocks_per_seq=None):
+    """Several query tokens per sequence over a paged KV cache; see include/paged_attn.h.
+
+    q fp16 [T, Hq, D] with the queries of sequence s in rows
+    query_start[s] .. query_start[s+1]-1 (the last tokens of the sequence).
+    Returns ``out`` (fp16 [T, Hq, D]) or ``(out, lse)``.
+    """
+    out, lse = _run_mq(False, q, k_cache, v_cache, block_table, context_lens, query_start, scale,
+                       causal, out, lse_out, return_lse, partition_tokens, workspace,
+                       max_blocks_per_seq)
+    return (out, lse) if (return_lse or lse_out is not None) else out
+
+
+def paged_multi_query_attn_partial(q, k_cache, v_cache, block_table, context_lens, query_start,
+                                   scale, causal=True, o=None, lse=None, partition_tokens=0,
+                                   workspace=None, max_blocks_per_seq=None):
+    """Normalised partial (o fp32 [T, Hq, D], lse fp32 [T, Hq]) of multi-query attention."""
+    return _run_mq(True, q, k_cache, v_cache, block_table, context_lens, query_start, scale,
+                   causal, o, lse, True, partition_tokens, workspace, max_blocks_per_seq)
+
+
+def cascade_decode_attn(q, k_cache, v_cache, prefix_table, prefix_lens, group_start,
+                        suffix_table, suffix_lens, scale, out=None, lse_out=None,
+                        return_lse=False, partials=None):
+    """Decode attention of B requests whose contexts are a shared prefix then a suffix.
+
+    Requests group_start[r] .. group_start[r+1]-1 share prefix r (prefix_table
+    row r, prefix_lens[r] tokens); request b continues with suffix_lens[b]
+    tokens of suffix_table row b.  Three library calls: the prefix pass with
+    every request of a group as a query of its prefix (no mask), the suffix
+    pass, and the log-sum-exp merge of the two partials.  ``partials`` may
+    pass preallocated (o fp32 [2, B, Hq, D], lse fp32 [2, B, Hq]).
+    """
+    B, Hq, D = q.shape
+    if partials is None:
+        o_parts = torch.empty((2, B, Hq, D), dtype=torch.float32, device=q.device)
+        l_parts = torch.empty((2, B, Hq), dtype=torch.float32, device=q.device)
+    else:
+        o_parts, l_parts = partials
+    paged_multi_query_attn_partial(q, k_cache, v_cache, prefix_table, prefix_lens, group_start,
+                                   scale, causal=False, o=o_parts[0], lse=l_parts[0])
+    paged_decode_attn_partial(q, k_cache, v_cache, suffix_table, suffix_lens, scale,
+                              o=o_parts[1], lse=l_parts[1])
+    res = merge_partials(o_parts, l_parts, out=out, lse_out=lse_out,
+                         return_lse=return_lse or lse_out is not None)
+    return res

@@ -491,49 +491,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     slot_step = p.B;
   }
 
-  // pass 1: the largest lse; pass 2: weights (one partial per lane) and sums
-  float L = -INFINITY;
-  for (int s = lane; s < nseg; s += kWave)
-    L = fmaxf(L, p.lse[(slot0 + s * slot_step) * p.Hq + h]);
-  L = wave_max_f32(L);
-  f32x2 res = {0.0f, 0.0f};
-  float lse_res = -INFINITY;
-  if (L != -INFINITY) {
-    float wsum = 0.0f;
-    f32x2 acc = {0.0f, 0.0f};
-    const long long ostep = slot_step * p.Hq * kD;
-    for (int s0 = 0; s0 < nseg; s0 += kWave) {
-      const int s = s0 + lane;
-      const float wl =
-          s < nseg ? fast_exp2((p.lse[(slot0 + s * slot_step) * p.Hq + h] - L) * kLog2e) : 0.0f;
-      wsum += wl;
-      const int cnt = min(kWave, nseg - s0);
-      const float* ob = p.o + ((slot0 + (long long)s0 * slot_step) * p.Hq + h) * kD + 2 * lane;
-      int j = 0;
-      for (; j + 8 <= cnt; j += 8) {
-        f32x2 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x2*>(ob + (j + u) * ostep);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wj = uniform_f32(wl, j + u);
-          acc.x = fmaf(wj, v[u].x, acc.x);
-          acc.y = fmaf(wj, v[u].y, acc.y);
-        }
-      }
-      for (; j < cnt; ++j) {
-        const f32x2 v = *reinterpret_cast<const f32x2*>(ob + j * ostep);
-        const float wj = uniform_f32(wl, j);
-        acc.x = fmaf(wj, v.x, acc.x);
-        acc.y = fmaf(wj, v.y, acc.y);
-      }
-    }
-    wsum = wave_sum_f32(wsum);
-    const float inv = 1.0f / wsum;
-    res.x = acc.x * inv;
-    res.y = acc.y * inv;
-    lse_res = L + __builtin_logf(wsum);
-  }
+  f32x2 res;
+  float lse_res;
+  merge_row(p.o, p.lse, slot0, slot_step, nseg, p.Hq, h, lane, res, lse_res);
   const long long dst = ((long long)b * p.Hq + h) * kD + 2 * lane;
   if (p.out_f16) {
     half2_t hv = {static_cast<_Float16>(res.x), static_cast<_Float16>(res.y)};

@@ -178,6 +178,60 @@ __device__ __forceinline__ void pv_mfma(f32x4 (&acc)[8], half4_t pa,
 }
 
 // ---------------------------------------------------------------------------
+// log-sum-exp merge of one output row over nseg normalised partials
+//
+// Partial s of the row sits at o + (slot(s) * rows + row) * D and
+// lse + slot(s) * rows + row, with slot(s) = slot0 + s * slot_step.  With
+// L = max_s lse_s and w_s = exp(lse_s - L): out = sum_s w_s o_s / sum_s w_s
+// and lse = L + ln(sum_s w_s).  Partials with lse = -inf weigh nothing; if
+// every partial is empty the row is 0 with lse -inf.  One wave per row; lane
+// l returns dims 2l and 2l + 1.
+__device__ __forceinline__ void merge_row(const float* o, const float* lse, long long slot0,
+                                          long long slot_step, int nseg, long long rows,
+                                          long long row, int lane, f32x2& res, float& lse_res) {
+  float L = -INFINITY;
+  for (int s = lane; s < nseg; s += kWave) L = fmaxf(L, lse[(slot0 + s * slot_step) * rows + row]);
+  L = wave_max_f32(L);
+  res = f32x2{0.0f, 0.0f};
+  lse_res = -INFINITY;
+  if (L == -INFINITY) return;
+  float wsum = 0.0f;
+  f32x2 acc = {0.0f, 0.0f};
+  const long long ostep = slot_step * rows * kD;
+  for (int s0 = 0; s0 < nseg; s0 += kWave) {
+    const int s = s0 + lane;
+    const float wl =
+        s < nseg ? fast_exp2((lse[(slot0 + s * slot_step) * rows + row] - L) * kLog2e) : 0.0f;
+    wsum += wl;
+    const int cnt = min(kWave, nseg - s0);
+    const float* ob = o + ((slot0 + (long long)s0 * slot_step) * rows + row) * kD + 2 * lane;
+    int j = 0;
+    for (; j + 8 <= cnt; j += 8) {
+      f32x2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x2*>(ob + (j + u) * ostep);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = uniform_f32(wl, j + u);
+        acc.x = fmaf(wj, v[u].x, acc.x);
+        acc.y = fmaf(wj, v[u].y, acc.y);
+      }
+    }
+    for (; j < cnt; ++j) {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(ob + j * ostep);
+      const float wj = uniform_f32(wl, j);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+    }
+  }
+  wsum = wave_sum_f32(wsum);
+  const float inv = 1.0f / wsum;
+  res.x = acc.x * inv;
+  res.y = acc.y * inv;
+  lse_res = L + __builtin_logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
 // host side: the thread-local message behind pda_last_error()
 
 __attribute__((visibility("hidden"))) int fail(int code, const char* fmt, ...)

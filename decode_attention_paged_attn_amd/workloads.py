@@ -349,10 +349,192 @@ def host_full(case: Case):
             case.block_table_host.copy(), case.lens.copy())
 
 
+# --- several query tokens per sequence, and shared prefixes ---------------------
+
+@dataclasses.dataclass
+class MqCase:
+    """A multi-query batch: the last n_q tokens of each sequence are queries."""
+    name: str
+    q: torch.Tensor              # [T, Hq, D] fp16
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: torch.Tensor    # [S, width] int32
+    context_lens: torch.Tensor   # [S] int32, the query tokens included
+    query_start: torch.Tensor    # [S + 1] int32
+    scale: float
+    lens: np.ndarray
+    n_queries: np.ndarray
+    block_table_host: np.ndarray
+    causal: bool
+    seed: int
+
+    @property
+    def S(self):
+        return self.context_lens.shape[0]
+
+    @property
+    def T(self):
+        return self.q.shape[0]
+
+    @property
+    def Hq(self):
+        return self.q.shape[1]
+
+    @property
+    def Hkv(self):
+        return self.k_cache.shape[2]
+
+
+def _queries(T, Hq, D, seed, device):
+    """N(0, 1) fp16 query rows, drawn after the pool (seed + 1, torch on the device)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) + 1)
+    return torch.randn((T, Hq, D), generator=gen, device=device,
+                       dtype=torch.float32).to(torch.float16)
+
+
+def build_mq_case(lens, n_queries, Hq, Hkv, *, causal=True, seed=0, device="cpu",
+                  rng_backend="numpy", name="mq_custom", pool_blocks=None) -> MqCase:
+    """Pool and tables as build_case draws them, then sum(n_queries) query rows."""
+    base = build_case(lens, Hq, Hkv, seed=seed, device=device, rng_backend=rng_backend,
+                      name=name, pool_blocks=pool_blocks)
+    n_queries = np.asarray(n_queries, dtype=np.int64)
+    qs = np.concatenate([[0], np.cumsum(n_queries)]).astype(np.int32)
+    q = _queries(int(qs[-1]), Hq, base.D, seed, device)
+    return MqCase(name=name, q=q, k_cache=base.k_cache, v_cache=base.v_cache,
+                  block_table=base.block_table, context_lens=base.context_lens,
+                  query_start=torch.from_numpy(qs).to(device), scale=base.scale,
+                  lens=base.lens, n_queries=n_queries, block_table_host=base.block_table_host,
+                  causal=causal, seed=seed)
+
+
+def spec_verify(seed=0, device="cpu", rng_backend="torch"):
+    """Speculative verification: 32 sequences of 4096 tokens, 6 query tokens each.
+
+    The 5 proposed tokens of a draft model (5 to 6 in the speculative-decoding
+    knob of "Optimising decode in vLLM") plus the last accepted token are
+    checked causally in one pass; batches above ~32 requests gain little there.
+    """
+    return build_mq_case([4096] * 32, [6] * 32, 32, 8, causal=True, seed=seed, device=device,
+                         rng_backend=rng_backend, name="spec_verify_b32_ctx4096_q6")
+
+
+def chunked_prefill(seed=0, device="cpu", rng_backend="torch"):
+    """Chunked prefill: 4 prompts, each at a 1024-token chunk (chunks 1, 3, 7, 15).
+
+    The chunk attends to the earlier chunks unmasked and to itself causally
+    ("Mathematical Formulation of Chunked Attention"; 1024-token chunks in
+    the chunk schedule figure of the same section).
+    """
+    chunks = [1, 3, 7, 15]
+    lens = [(c + 1) * K1 for c in chunks]
+    return build_mq_case(lens, [K1] * 4, 32, 8, causal=True, seed=seed, device=device,
+                         rng_backend=rng_backend, name="prefill_s4_chunk1024_at_1_3_7_15")
+
+
+@dataclasses.dataclass
+class CascadeCase:
+    """Decode requests in groups that share a prefix (cascade attention)."""
+    name: str
+    q: torch.Tensor              # [B, Hq, D]
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    prefix_table: torch.Tensor   # [R, width]
+    prefix_lens: torch.Tensor    # [R]
+    group_start: torch.Tensor    # [R + 1]
+    suffix_table: torch.Tensor   # [B, width]
+    suffix_lens: torch.Tensor    # [B]
+    scale: float
+    prefix_lens_host: np.ndarray
+    group_start_host: np.ndarray
+    suffix_lens_host: np.ndarray
+    prefix_table_host: np.ndarray
+    suffix_table_host: np.ndarray
+    seed: int
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def Hq(self):
+        return self.q.shape[1]
+
+    @property
+    def Hkv(self):
+        return self.k_cache.shape[2]
+
+    def naive_table(self):
+        """Per request: prefix frames then suffix frames (prefixes of whole blocks only)."""
+        pl = self.prefix_lens_host
+        if np.any(pl % BLOCK_SIZE):
+            raise ValueError("a prefix that ends inside a block has no single-table form")
+        rows, lens = [], []
+        for r in range(len(pl)):
+            for b in range(int(self.group_start_host[r]), int(self.group_start_host[r + 1])):
+                nb = -(-int(self.suffix_lens_host[b]) // BLOCK_SIZE)
+                rows.append(list(self.prefix_table_host[r, :pl[r] // BLOCK_SIZE]) +
+                            list(self.suffix_table_host[b, :nb]))
+                lens.append(int(pl[r]) + int(self.suffix_lens_host[b]))
+        width = max(max(len(x) for x in rows), 1)
+        table = np.full((len(rows), width), -1, dtype=np.int64)
+        for i, x in enumerate(rows):
+            table[i, :len(x)] = x
+        dev = self.q.device
+        return (torch.from_numpy(table.astype(np.int32)).to(dev),
+                torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(dev))
+
+
+def build_cascade_case(prefix_lens, group_sizes, suffix_lens, Hq, Hkv, *, seed=0, device="cpu",
+                       rng_backend="numpy", name="cascade_custom") -> CascadeCase:
+    """One pool dealt to R prefix rows then B suffix rows, then B query rows."""
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    suffix_lens = np.asarray(suffix_lens, dtype=np.int64)
+    R = len(prefix_lens)
+    base = build_case(np.concatenate([prefix_lens, suffix_lens]), Hq, Hkv, seed=seed,
+                      device=device, rng_backend=rng_backend, name=name)
+    gs = np.concatenate([[0], np.cumsum(group_sizes)]).astype(np.int64)
+    B = int(gs[-1])
+    assert B == len(suffix_lens)
+    q = _queries(B, Hq, base.D, seed, device)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.int32)).to(device)
+    return CascadeCase(name=name, q=q, k_cache=base.k_cache, v_cache=base.v_cache,
+                       prefix_table=i32(base.block_table_host[:R]), prefix_lens=i32(prefix_lens),
+                       group_start=i32(gs), suffix_table=i32(base.block_table_host[R:]),
+                       suffix_lens=i32(suffix_lens), scale=base.scale,
+                       prefix_lens_host=prefix_lens, group_start_host=gs,
+                       suffix_lens_host=suffix_lens,
+                       prefix_table_host=base.block_table_host[:R].copy(),
+                       suffix_table_host=base.block_table_host[R:].copy(), seed=seed)
+
+
+def shared_prefix(seed=0, device="cpu", rng_backend="torch"):
+    """Cascade decode: 4 groups of 50 requests, each group sharing a 16K-token prefix.
+
+    50 requests per shared prefix as in the worked example of "What
+    FlashInfer brings: JIT and cascade attention"; the prefix is 16K tokens
+    (a long shared system prompt or document) and each request's own suffix
+    is uniform on [1, 1024] tokens.  32/8 heads.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed + 7))
+    suffix = rng.integers(1, K1, size=200, endpoint=True)
+    return build_cascade_case([16 * K1] * 4, [50] * 4, suffix, 32, 8, seed=seed, device=device,
+                              rng_backend=rng_backend, name="cascade_g4x50_prefix16k_suffix1k")
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama8b_4k": llama8b_4k,
     "agentic_80k": agentic_80k,
     "ragged_mixed": ragged_mixed,
     "disagg_merge": disagg_merge,
+}
+
+MQ_CONFIGS = {
+    "spec_verify": spec_verify,
+    "chunked_prefill": chunked_prefill,
+}
+
+CASCADE_CONFIGS = {
+    "shared_prefix": shared_prefix,
 }

@@ -253,6 +253,75 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
                     int B, int Hkv, int D, int block_size, int64_t num_blocks,
                     int max_blocks_per_seq, void* stream);
 
+/*
+ * Multi-query attention: several query tokens of each sequence at once, the
+ * last n_q tokens of the sequence, over its paged K/V.  Covers a prefill
+ * chunk, whose queries see the earlier chunks unmasked and the current chunk
+ * causally ("Mathematical Formulation of Chunked Attention" on the
+ * disaggregated-inference page), the k tokens a draft model proposed, which
+ * the verifier checks in one pass (speculative decoding in the post
+ * "Optimising decode in vLLM: squeezing every token out of small hardware"),
+ * and the shared-prefix pass of cascade attention, where the decode queries
+ * of every request that shares a prefix attend to it at once without a mask
+ * ("What FlashInfer brings: JIT and cascade attention" on the page "The
+ * signature-dish specialist: vLLM's attention backend").
+ *
+ * q            fp16  [num_queries, Hq, D]; rows query_start[s] ..
+ *              query_start[s+1]-1 are the queries of sequence s, in position
+ *              order.
+ * query_start  int32 [S + 1], non-decreasing, query_start[0] = 0 and
+ *              query_start[S] = num_queries (values are clamped into
+ *              [0, num_queries] on the device).
+ * block_table  int32 [S, block_table_stride]; context_lens int32 [S]: cached
+ *              tokens of sequence s, its n_q query tokens included.
+ * causal != 0: query i (0-based) of sequence s, with n = context_lens[s] and
+ *              n_q its query count, sits at position n - n_q + i and attends to
+ *              tokens 0 .. n - n_q + i.  causal == 0: every query attends to all
+ *              n tokens.  A query with nothing to attend to (n_q > n) gets
+ *              out = 0 and lse = -inf.
+ * out          fp16 [num_queries, Hq, D]; lse_out fp32 [num_queries, Hq] or
+ *              NULL.  The _partial form writes fp32 o and a non-NULL lse
+ *              instead (a partial for merge_partials).
+ * partition_tokens: 0 = automatic, else the unit length in tokens (a
+ *              multiple of 16) by which the work is balanced over the GPU.
+ * workspace    device memory of at least pda_multi_query_workspace_size()
+ *              bytes, 256-byte aligned; it holds the schedule and partials.
+ * Shapes as for paged_decode_attn (fp16 caches, D = 128, block_size = 16,
+ * Hq / Hkv in {1, 2, 4, 8}, Hkv <= 8), and S <= 8192.
+ *
+ * Cascade attention for B decode requests in R groups that share a prefix
+ * (requests group_start[r] .. group_start[r+1]-1 share prefix r): call
+ * paged_multi_query_attn_partial with the R prefix rows as the sequences,
+ * query_start = group_start and causal = 0; call paged_decode_attn_partial
+ * with the B suffix rows; then merge_partials with R = 2 over the two
+ * (o, lse) pairs.
+ */
+int pda_multi_query_workspace_size(int S, int num_queries, int Hq, int Hkv, int D,
+                                   int block_size, int max_blocks_per_seq,
+                                   int partition_tokens, size_t* bytes);
+
+int paged_multi_query_attn(void* out, float* lse_out, const void* q,
+                           const int32_t* query_start, int num_queries,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, int64_t block_table_stride,
+                           const int32_t* context_lens, int S, int Hq, int Hkv,
+                           int D, int block_size, int64_t num_blocks,
+                           int max_blocks_per_seq, float scale, int causal,
+                           int partition_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+int paged_multi_query_attn_partial(float* o, float* lse, const void* q,
+                                   const int32_t* query_start, int num_queries,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table,
+                                   int64_t block_table_stride,
+                                   const int32_t* context_lens, int S, int Hq,
+                                   int Hkv, int D, int block_size,
+                                   int64_t num_blocks, int max_blocks_per_seq,
+                                   float scale, int causal, int partition_tokens,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pda_last_error(void);
 

@@ -63,3 +63,13 @@ def compare_ulps(a, b, ulps=2, rowwise=False, what="merge"):
     worst = float((np.abs(a - b) / unit).max())
     assert worst <= ulps, f"{what}: {worst:.1f} fp16 ulps > {ulps}"
     return worst
+
+
+def p_rounding_bound(v):
+    """Largest move of a normalised output from rounding p to fp16 before p.V.
+
+    With p_i >= 0 and relative rounding |d_i| <= 2^-11,
+    |sum d_i p_i v_i| / sum p_i <= 2^-11 max|v|; 1e-5 covers fp32 summation.
+    Poison (NaN) slots in the pool are ignored.
+    """
+    return 2.0 ** -11 * float(np.nanmax(np.abs(np.asarray(v, dtype=np.float64)))) + 1e-5

@@ -1,0 +1,286 @@
+"""Multi-query and cascade attention on the GPU against the float64 oracle.
+
+Every call goes through the C ABI (ctypes binding).  Small cases are checked
+in full; the full-size workloads on sampled queries, which the oracle
+computes one by one from its definition, in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_paged_attn_amd as pda
+from decode_attention_paged_attn_amd import workloads as W
+import oracle.multi_query as MQ
+import oracle.paged_attention as O
+from tests.parity import compare_lse, compare_out, p_rounding_bound, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pda.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_mq(case, P=0, **kw):
+    _say(f"[mq] {case.name} S={case.S} T={case.T} Hq={case.Hq} Hkv={case.Hkv} "
+         f"causal={case.causal} P={P}")
+    out, lse = pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                          case.context_lens, case.query_start, case.scale,
+                                          causal=case.causal, return_lse=True,
+                                          partition_tokens=P, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def host_mq(case):
+    return (case.q.cpu().numpy(), case.k_cache.cpu().numpy(), case.v_cache.cpu().numpy(),
+            case.block_table_host.copy(), case.lens.copy(),
+            case.query_start.cpu().numpy().astype(np.int64))
+
+
+def oracle_mq(case):
+    q, k, v, table, lens, qs = host_mq(case)
+    return MQ.multi_query_attention(q, k, v, table, lens, qs, case.scale, causal=case.causal)
+
+
+SMALL_LENS = [0, 1, 5, 16, 17, 40, 100, 257, 600, 33]
+SMALL_NQ = [2, 1, 8, 3, 0, 17, 5, 33, 64, 1]
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("P", [0, 32, 256])
+def test_small_all_group_sizes(G, Hkv, causal, P):
+    case = W.build_mq_case(SMALL_LENS, SMALL_NQ, G * Hkv, Hkv, causal=causal, seed=40 + G,
+                           device="cuda", name=f"mq_small_G{G}")
+    out, lse = run_mq(case, P)
+    ref, ref_lse = oracle_mq(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_single_query_is_decode():
+    lens = [1, 2, 15, 16, 17, 100, 511, 1537]
+    case = W.build_mq_case(lens, [1] * len(lens), 32, 8, causal=True, seed=41, device="cuda",
+                           name="mq_one_query")
+    out, lse = run_mq(case)
+    dec, dlse = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                      case.context_lens, case.scale, return_lse=True)
+    q, k, v, table, ln, qs = host_mq(case)
+    ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
+    compare_out(to_np(out), ref)
+    compare_out(to_np(dec), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_queries_past_context_and_empty():
+    case = W.build_mq_case([3, 0, 20, 16], [5, 2, 0, 16], 8, 2, causal=True, seed=42,
+                           device="cuda", name="mq_degenerate")
+    out, lse = run_mq(case)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(o[0:2] == 0) and np.all(np.isneginf(l[0:2]))      # see nothing
+    assert np.all(o[5:7] == 0) and np.all(np.isneginf(l[5:7]))      # empty context
+    ref, ref_lse = oracle_mq(case)
+    compare_out(o, ref)
+    compare_lse(l, ref_lse)
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_partial_entry_point(P):
+    case = W.build_mq_case(SMALL_LENS, SMALL_NQ, 16, 4, causal=True, seed=43, device="cuda",
+                           name="mq_partial")
+    o, lse = pda.paged_multi_query_attn_partial(case.q, case.k_cache, case.v_cache,
+                                                case.block_table, case.context_lens,
+                                                case.query_start, case.scale, causal=True,
+                                                partition_tokens=P)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_mq(case)
+    v = case.v_cache.cpu().numpy()
+    compare_out(to_np(o), ref, abs_tol=p_rounding_bound(v))
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_bitwise_deterministic():
+    case = W.build_mq_case(SMALL_LENS * 3, SMALL_NQ * 3, 32, 8, causal=True, seed=44,
+                           device="cuda", name="mq_det")
+    a, la = run_mq(case, 32)
+    b, lb = run_mq(case, 32)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_scale_sign_and_zero():
+    case = W.build_mq_case([37, 300], [4, 9], 8, 2, causal=True, seed=45, device="cuda",
+                           name="mq_scale")
+    q, k, v, table, lens, qs = host_mq(case)
+    for scale in (-0.2, 0.0):
+        case.scale = scale
+        out, lse = run_mq(case)
+        ref, ref_lse = MQ.multi_query_attention(q, k, v, table, lens, qs, scale, causal=True)
+        compare_out(to_np(out), ref)
+        compare_lse(to_np(lse), ref_lse)
+
+
+def test_graph_capture_replays_match_eager():
+    case = W.build_mq_case(SMALL_LENS, SMALL_NQ, 32, 8, causal=True, seed=46, device="cuda",
+                           name="mq_graph")
+    ws = torch.empty(pda.multi_query_workspace_size(case.S, case.T, 32, 8,
+                                                    case.block_table.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.T, 32, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((case.T, 32), dtype=torch.float32, device="cuda")
+    eager, eager_lse = run_mq(case, workspace=ws)
+    eager, eager_lse = eager.clone(), eager_lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                       case.context_lens, case.query_start, case.scale,
+                                       causal=True, out=out, lse_out=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager) and torch.equal(lse, eager_lse), f"replay {i}"
+
+
+# --- cascade (shared prefix) ----------------------------------------------------
+
+def host_cascade(c):
+    return (c.q.cpu().numpy(), c.k_cache.cpu().numpy(), c.v_cache.cpu().numpy(),
+            c.prefix_table_host, c.prefix_lens_host, c.group_start_host, c.suffix_table_host,
+            c.suffix_lens_host)
+
+
+def run_cascade(c):
+    _say(f"[cascade] {c.name} B={c.B} groups={len(c.prefix_lens_host)}")
+    out, lse = pda.cascade_decode_attn(c.q, c.k_cache, c.v_cache, c.prefix_table, c.prefix_lens,
+                                       c.group_start, c.suffix_table, c.suffix_lens, c.scale,
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_cascade_page_example_shape():
+    """50 requests sharing a 1000-token prefix, as in the page's worked example."""
+    rng = np.random.default_rng(47)
+    suffix = rng.integers(0, 200, size=50)
+    c = W.build_cascade_case([1000], [50], suffix, 32, 8, seed=47, device="cuda",
+                             name="cascade_r50_p1000")
+    out, lse = run_cascade(c)
+    ref, ref_lse = MQ.cascade_attention(*host_cascade(c), c.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+def test_cascade_groups_and_edges(G, Hkv):
+    # group 2 has an empty prefix; some requests have no suffix
+    c = W.build_cascade_case([64, 37, 0, 16], [3, 5, 2, 1], [5, 0, 17, 16, 1, 40, 0, 3, 9, 0, 2],
+                             G * Hkv, Hkv, seed=48 + G, device="cuda", name=f"cascade_G{G}")
+    out, lse = run_cascade(c)
+    ref, ref_lse = MQ.cascade_attention(*host_cascade(c), c.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_cascade_equals_naive_decode():
+    c = W.build_cascade_case([256, 512], [6, 4], list(range(1, 200, 20)), 32, 8, seed=50,
+                             device="cuda", name="cascade_vs_naive")
+    out, _ = run_cascade(c)
+    table, lens = c.naive_table()
+    naive = pda.paged_decode_attn(c.q, c.k_cache, c.v_cache, table, lens, c.scale)
+    torch.cuda.synchronize()
+    ref, _ = MQ.cascade_attention(*host_cascade(c), c.scale)
+    compare_out(to_np(out), ref)
+    compare_out(to_np(naive), ref)
+
+
+# --- full-size workloads, sampled ------------------------------------------------
+
+def sampled_mq_oracle(case, picks):
+    """Oracle rows for (sequence, query index) picks, from the sequence's own blocks."""
+    Hq, Hkv = case.Hq, case.Hkv
+    G = Hq // Hkv
+    qs = case.query_start.cpu().numpy()
+    res = []
+    for s, i in picks:
+        n = int(case.lens[s])
+        nq = int(case.n_queries[s])
+        vis = MQ.visible_tokens(n, nq, i, case.causal)
+        nb = -(-vis // 16)
+        idx = torch.tensor([int(x) for x in case.block_table_host[s, :nb]], dtype=torch.int64,
+                           device=case.k_cache.device)
+        kp = case.k_cache.index_select(0, idx).cpu().numpy()
+        vp = case.v_cache.index_select(0, idx).cpu().numpy()
+        qrow = case.q[int(qs[s]) + i].cpu().numpy()
+        o = np.zeros((Hq, 128))
+        l = np.zeros(Hq)
+        for g in range(Hkv):
+            K = O._gather_sequence_blocks(kp, np.arange(nb), vis, g, 16)
+            V = O._gather_sequence_blocks(vp, np.arange(nb), vis, g, 16)
+            o[g * G:(g + 1) * G], l[g * G:(g + 1) * G] = O.attend(qrow[g * G:(g + 1) * G], K, V,
+                                                                 case.scale)
+        res.append((int(qs[s]) + i, o, l))
+    return res
+
+
+@pytest.mark.parametrize("config", ["spec_verify", "chunked_prefill"])
+def test_full_size_sampled(config):
+    case = W.MQ_CONFIGS[config](device="cuda")
+    out, lse = run_mq(case)
+    rng = np.random.default_rng(51)
+    picks = []
+    for s in range(case.S):
+        nq = int(case.n_queries[s])
+        cand = sorted({0, nq - 1, *rng.integers(0, nq, size=3).tolist()})
+        picks += [(s, int(i)) for i in cand][:5 if config == "chunked_prefill" else 2]
+    if config == "spec_verify":
+        picks = picks[:24]
+    o, l = to_np(out), to_np(lse)
+    for row, ref, ref_l in sampled_mq_oracle(case, picks):
+        compare_out(o[row], ref, what=f"row {row}")
+        compare_lse(l[row], ref_l, what=f"lse row {row}")
+    assert np.all(np.isfinite(o))
+    del case
+    torch.cuda.empty_cache()
+
+
+def test_full_size_cascade_sampled():
+    c = W.shared_prefix(device="cuda")
+    out, lse = run_cascade(c)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(o))
+    rng = np.random.default_rng(52)
+    gs = c.group_start_host
+    for b in sorted({0, c.B - 1, *rng.integers(0, c.B, size=6).tolist()}):
+        r = int(np.searchsorted(gs, b, side="right") - 1)
+        pl, sl = int(c.prefix_lens_host[r]), int(c.suffix_lens_host[b])
+        frames = (list(c.prefix_table_host[r, :-(-pl // 16)]) +
+                  list(c.suffix_table_host[b, :-(-sl // 16)]))
+        idx = torch.tensor([int(x) for x in frames], dtype=torch.int64, device="cuda")
+        kp = c.k_cache.index_select(0, idx).cpu().numpy()
+        vp = c.v_cache.index_select(0, idx).cpu().numpy()
+        npb = -(-pl // 16)
+        ref, ref_l = MQ.cascade_attention(
+            c.q[b:b + 1].cpu().numpy(), kp, vp, np.arange(npb)[None], [pl], [0, 1],
+            np.arange(npb, len(frames))[None], [sl], c.scale)
+        compare_out(o[b:b + 1], ref, what=f"request {b}")
+        compare_lse(l[b:b + 1], ref_l, what=f"lse request {b}")
+    del c
+    torch.cuda.empty_cache()

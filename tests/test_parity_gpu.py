@@ -16,7 +16,8 @@ import torch
 import decode_attention_paged_attn_amd as pda
 from decode_attention_paged_attn_amd import workloads as W
 import oracle.paged_attention as O
-from tests.parity import ROW_REL_TOL, compare_lse, compare_out, compare_ulps, to_np
+from tests.parity import (ROW_REL_TOL, compare_lse, compare_out, compare_ulps, p_rounding_bound,
+                          to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,16 +153,6 @@ def test_bitwise_deterministic():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
-def _p_rounding_bound(v):
-    """Largest move of a normalised output from rounding p to fp16 before PV.
-
-    With p_i >= 0 and relative rounding |d_i| <= 2^-11,
-    |sum d_i p_i v_i| / sum p_i <= 2^-11 max|v|; 1e-5 covers fp32 summation.
-    Poison (NaN) slots in the pool are ignored.
-    """
-    return 2.0 ** -11 * float(np.nanmax(np.abs(np.asarray(v, dtype=np.float64)))) + 1e-5
-
-
 @pytest.mark.parametrize("P", [0, 64, 2048])
 def test_split_partials_in_workspace(P):
     """Every stored partial equals the oracle's attention over the same token range."""
@@ -199,7 +190,7 @@ def test_split_partials_in_workspace(P):
             heads = slice(g * 4, g * 4 + 4)
             o_ref, l_ref = O.attend(q[b, heads], K, V, case.scale)
             compare_lse(l_ws[w + b, heads], l_ref, what=f"lse w={w} b={b} [{lo},{hi})")
-            compare_out(o_ws[w + b, heads], o_ref, abs_tol=_p_rounding_bound(V),
+            compare_out(o_ws[w + b, heads], o_ref, abs_tol=p_rounding_bound(V),
                         row_rel_tol=ROW_REL_TOL,
                         what=f"o w={w} b={b} [{lo},{hi})")
     assert split > 0, "the case should split at least one sequence"
@@ -235,7 +226,7 @@ def test_partial_api_and_merge():
     for r in range(R):
         o_ref, l_ref = O.partial_attention(q, k, v, table[:, r * cols:(r + 1) * cols],
                                            [per] * 3, case.scale)
-        compare_out(to_np(o_parts[r]), o_ref, abs_tol=_p_rounding_bound(v),
+        compare_out(to_np(o_parts[r]), o_ref, abs_tol=p_rounding_bound(v),
                     row_rel_tol=ROW_REL_TOL)
         compare_lse(to_np(l_parts[r]), l_ref)
 
