@@ -27,12 +27,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0     # dense fp16 MFMA peak of MI355X
 METRIC = "KV-read GB/s and % of HBM peak; decode-attn tokens/s at Llama-3.1-8B shape"
 CSRC = os.path.join(ROOT, "decode_attention_paged_attn_amd", "csrc")
 # the sources each timed kernel is built from (a counter record is valid only
 # for the sources it was taken on)
 KERNEL_SOURCES = {
     "attention": ("paged_attn.hip", "pda_common.h"),
+    "multi_query": ("multi_query.hip", "pda_common.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -174,6 +176,149 @@ def measure(case, P, steps, warmup, flush_mib=0):
     }
 
 
+def _time_events(step, steps, warmup):
+    """Mean ms per step: wall clock and HIP events on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / steps * 1e3
+    ev = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    return wall_ms, sum(ev) / len(ev), ev[len(ev) // 2]
+
+
+def mq_work(case):
+    """(unique K/V bytes, algorithmic FLOPs) of one multi-query call.
+
+    Bytes: every cached token of a sequence that some query sees, K and V, all
+    KV heads, once.  FLOPs: 4 * D per (query, query head, visible token): the
+    q.k dot product and the p.v accumulation, 2 * D each.
+    """
+    Hkv, Hq, D = case.Hkv, case.Hq, 128
+    nbytes = flops = 0
+    for n, nq in zip(case.lens, case.n_queries):
+        n, nq = int(n), int(nq)
+        if nq == 0:
+            continue
+        if case.causal:
+            vis = [max(0, n - nq + i + 1) for i in range(nq)]
+        else:
+            vis = [n] * nq
+        nbytes += max(vis) * 2 * Hkv * D * 2
+        flops += 4 * D * Hq * sum(vis)
+    return nbytes, flops
+
+
+def bench_multi_query(case, P, steps, warmup):
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    ws = torch.empty(max(pda.multi_query_workspace_size(case.S, case.T, case.Hq, case.Hkv,
+                                                        case.block_table.shape[1], P), 1),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.T, case.Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((case.T, case.Hq), dtype=torch.float32, device="cuda")
+
+    def step():
+        pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                   case.context_lens, case.query_start, case.scale,
+                                   causal=case.causal, out=out, lse_out=lse,
+                                   partition_tokens=P, workspace=ws)
+
+    wall_ms, ev_ms, ev_med = _time_events(step, steps, warmup)
+    nbytes, flops = mq_work(case)
+    # the bound: HBM for the unique K/V bytes, or the fp16 MFMA peak for the flops
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_FP16_PEAK_TFLOPS * 1e12)
+    hbm_bound = t_hbm >= t_mfma
+    roof = ({"bound": "hbm", "achieved": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+             "peak": HBM_PEAK_GBS, "unit": "GB/s"} if hbm_bound else
+            {"bound": "mfma", "achieved": round(flops / (ev_ms / 1e3) / 1e12, 2),
+             "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s"})
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = "paged_multi_query_attn call (plan + tile + merge kernels)"
+    roof["traffic"] = None
+    value = roof["achieved"] * ev_ms / wall_ms
+    print(json.dumps({
+        "metric": "multi-query paged attention: " + ("KV-read GB/s" if hbm_bound else "TFLOP/s"),
+        "op": "paged_multi_query_attn", "value": round(value, 2), "unit": roof["unit"],
+        "ms_per_step": round(wall_ms, 5), "event_ms": {"mean": round(ev_ms, 5),
+                                                        "p50": round(ev_med, 5)},
+        "query_tokens_per_s": round(case.T / (wall_ms / 1e3), 1),
+        "kv_bytes_unique": nbytes, "flops": flops,
+        "tflops": round(flops / (ev_ms / 1e3) / 1e12, 2),
+        "kv_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+        "roofline": roof, "steps": steps, "warmup": warmup, "dtype": "fp16",
+        "data": "synthetic", "kernel_source_sha256_16": source_hash("multi_query"),
+        "config": {"workload": case.name, "sequences": case.S, "query_tokens": case.T,
+                   "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 128,
+                   "causal": case.causal, "partition_tokens": P,
+                   "context_tokens": int(case.lens.sum())}}), flush=True)
+
+
+def bench_cascade(case, steps, warmup):
+    """Cascade (prefix pass + suffix pass + merge) against naive decode of the same batch."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    B, Hq = case.B, case.Hq
+    o_parts = torch.empty((2, B, Hq, 128), dtype=torch.float32, device="cuda")
+    l_parts = torch.empty((2, B, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+
+    def step():
+        pda.cascade_decode_attn(case.q, case.k_cache, case.v_cache, case.prefix_table,
+                                case.prefix_lens, case.group_start, case.suffix_table,
+                                case.suffix_lens, case.scale, out=out,
+                                partials=(o_parts, l_parts))
+
+    wall_ms, ev_ms, ev_med = _time_events(step, steps, warmup)
+    table, lens = case.naive_table()
+    naive_out = torch.empty_like(out)
+
+    def naive():
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, table, lens, case.scale,
+                              out=naive_out)
+
+    n_wall, n_ev, _ = _time_events(naive, steps, warmup)
+    row = 2 * case.Hkv * 128 * 2                              # K and V bytes per token
+    # tokens read: naive decode reads each group's prefix once per request,
+    # cascade once per group; both read every suffix once
+    naive_tok, unique_tok = 0, 0
+    for r in range(len(case.prefix_lens_host)):
+        lo, hi = int(case.group_start_host[r]), int(case.group_start_host[r + 1])
+        suffix = int(case.suffix_lens_host[lo:hi].sum())
+        naive_tok += (hi - lo) * int(case.prefix_lens_host[r]) + suffix
+        unique_tok += int(case.prefix_lens_host[r]) + suffix
+    print(json.dumps({
+        "metric": "cascade decode: requests/s (unique KV-read GB/s in roofline)",
+        "op": "cascade_decode_attn", "value": round(B / (wall_ms / 1e3), 1), "unit": "requests/s",
+        "ms_per_step": round(wall_ms, 5), "event_ms": {"mean": round(ev_ms, 5),
+                                                        "p50": round(ev_med, 5)},
+        "naive_decode_ms": round(n_ev, 5), "speedup_vs_naive_decode": round(n_ev / ev_ms, 3),
+        "naive_kv_bytes": naive_tok * row, "unique_kv_bytes": unique_tok * row,
+        "naive_decode_GBps": round(naive_tok * row / (n_ev / 1e3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(unique_tok * row / (ev_ms / 1e3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(unique_tok * row / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel": "cascade call (prefix pass + suffix pass + merge)",
+                     "traffic": None},
+        "steps": steps, "warmup": warmup, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": case.name, "requests": B,
+                   "groups": len(case.prefix_lens_host),
+                   "prefix_tokens": [int(x) for x in case.prefix_lens_host],
+                   "suffix_tokens_total": int(case.suffix_lens_host.sum()),
+                   "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}), flush=True)
+
+
 def bench_append(case, steps, warmup):
     """Time paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16)."""
     import torch
@@ -218,9 +363,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--also", default="llama8b_4k",
                     help="comma-separated extra workloads reported under 'also'")
-    ap.add_argument("--op", default="attention", choices=["attention", "append"],
+    ap.add_argument("--op", default="attention",
+                    choices=["attention", "append", "multi_query", "cascade"],
                     help="attention (default): paged_decode_attn; append: paged_kv_append of "
-                         "one token per sequence")
+                         "one token per sequence; multi_query: paged_multi_query_attn on "
+                         "--config spec_verify or chunked_prefill; cascade: "
+                         "cascade_decode_attn on --config shared_prefix")
     ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
                     help="element type of the K/V cache (fp8: E4M3 codes with per-tensor scales)")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -247,6 +395,15 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     pda.load_library()
+    if args.op == "multi_query":
+        name = args.config if args.config in W.MQ_CONFIGS else "spec_verify"
+        case = W.MQ_CONFIGS[name](device="cuda")
+        bench_multi_query(case, args.partition_tokens or 0, args.steps, args.warmup)
+        return
+    if args.op == "cascade":
+        case = W.CASCADE_CONFIGS["shared_prefix"](device="cuda")
+        bench_cascade(case, args.steps, args.warmup)
+        return
     case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if args.op == "append":
         bench_append(case, args.steps, args.warmup)
