@@ -15,25 +15,34 @@
 // last n_q tokens of a sequence of n tokens sits at position n - n_q + i; with
 // the causal mask it sees tokens 0 .. n - n_q + i, without it all n.
 //
-// Work decomposition.  The queries of a sequence are cut into tiles of
-// 16 / G query tokens, so that a tile's G query heads per KV head fill the 16
-// rows of the MFMA tiles: row m is query m / G, head m % G.  Every tile reads
-// its sequence's K/V up to the furthest position one of its queries sees, in
-// units of P tokens.  A one-wave plan kernel lists the tiles, their units and
-// the prefix sums of the units; the units of all tiles, in order, form one
-// stream cut into n_runs equal runs (as for single-token decode), and the
-// persistent grid has one work-group per (run, group of up to 4 KV heads),
-// one wave per KV head.  A tile that lies inside one run writes its output
-// directly; a tile cut by run boundaries writes normalised partials (slot
-// w + its rank among the cut tiles, so at most 2 * n_runs slots) that the
-// merge kernel combines by log-sum-exp.  Tiles that see no token at all are
-// written as 0 with lse -inf by the merge kernel.
+// Work decomposition.  The queries of a sequence are cut into tiles of Qt
+// query tokens whose Qt x G (query, head) rows fill MFMA row blocks of 16: row
+// m is query m / G, head m % G.  Every tile reads its sequence's K/V up to the
+// furthest position one of its queries sees, in units of P tokens.  A one-wave
+// plan kernel lists the tiles, their units and the prefix sums of the units;
+// the units of all tiles, in order, form one stream cut into n_runs equal runs
+// (as for single-token decode).  A tile that lies inside one run writes its
+// output directly; a tile cut by run boundaries writes normalised partials
+// (slot w + its rank among the cut tiles, so at most 2 * n_runs slots) that
+// the merge kernel combines by log-sum-exp, one wave per row.  Tiles that see
+// no token are written as 0 with lse -inf by the merge kernel.
 //
-// Per segment a wave walks the 16-token blocks through the block table as the
-// decode kernel does (the same K/V loads, QK^T and p.V MFMAs), but the
-// running max and sum of the softmax are per row and live in the lanes that
-// hold the row (lane group c holds rows 4c .. 4c+3), and each row has its own
-// last visible token; blocks that every row sees in full skip the mask.
+// Two tile kernels, picked by the average query rows per sequence:
+//   * register kernel (up to 16 rows): one work-group per (run, group of up to
+//     4 KV heads), one wave per KV head, a 16-row tile per wave; each wave
+//     streams its own K/V through a ring of register buffers, as the decode
+//     kernel does;
+//   * shared kernel (more rows): one work-group of 4 waves per (run, KV head)
+//     and a tile of 64 * NT rows, 16 * NT per wave; the 256 threads load each
+//     16-token block of K and V once (16 bytes of each per thread, a few blocks
+//     ahead in registers) into a double-buffered LDS stage, and every wave
+//     folds its rows from there, so the tile's K/V is read once for all its
+//     rows.
+// Per block a wave runs the decode kernel's QK^T and p.V MFMAs; the running
+// max and sum of the softmax are per row and live in the lanes that hold the
+// row (lane group c holds rows 16b + 4c .. 16b + 4c + 3 of row block b), each
+// row has its own last visible token, and blocks every row sees in full skip
+// the mask.
 
 #include <hip/hip_runtime.h>
 
@@ -49,13 +58,16 @@ namespace {
 
 using namespace pda;
 
-constexpr int kMqWaves = 4;           // KV heads (waves) per work-group, at most
+constexpr int kMqWaves = 4;           // waves per work-group (KV heads, or row groups)
 constexpr int kMqMaxKvHeads = 8;
-constexpr int kMqMaxSeqs = 8192;      // sequences per call: their tile offsets live in LDS
+constexpr int kMqMaxSeqs = 4000;      // sequences per call: their facts live in the plan's LDS
 constexpr int kMqHdrInts = 8;         // k, U, n_runs, P, n_tiles, n_fix
 constexpr int kMqTileArrays = 8;      // seq, q0, nq, base, ntok, ub, rank, fix
 constexpr int kMqMaxPartition = 1 << 20;
-constexpr int kMqRing = 2;            // K/V register buffers per wave (blocks in flight + 1)
+constexpr int kRegRing = 2;           // register kernel: K/V buffers per wave (blocks in flight + 1)
+constexpr int kShPrefetch = 4;        // shared kernel: blocks each thread holds (in flight + 1)
+constexpr int kLdsRow = 272;          // shared kernel: bytes per token row in LDS (256 + 16 padding)
+constexpr int kNoMask = -(1 << 30);   // causal base of a tile without the causal mask
 
 struct MqParams {
   const _Float16* q;        // [T, Hq, D]
@@ -78,14 +90,14 @@ struct MqParams {
   // per tile (tiles_max entries each)
   int32_t* t_seq;           // sequence
   int32_t* t_q0;            // first query row of the tile
-  int32_t* t_nq;            // queries in the tile (1 .. 16 / G)
+  int32_t* t_nq;            // queries in the tile (1 .. Qt)
   int32_t* t_base;          // causal: query qi of the tile sees base + qi tokens (clamped)
   int32_t* t_ntok;          // tokens the tile reads: what its furthest query sees
   int32_t* t_ub;            // units of all earlier tiles
   int32_t* t_rank;          // rank among the tiles cut by run boundaries, else -1
   int32_t* t_fix;           // [n_fix] tiles the merge kernel writes: cut ones and empty ones
-  float* ws_o;              // [2 * n_runs, 16 / G, Hq, D] normalised partials
-  float* ws_lse;            // [2 * n_runs, 16 / G, Hq]
+  float* ws_o;              // [2 * n_runs, Qt, Hq, D] normalised partials
+  float* ws_lse;            // [2 * n_runs, Qt, Hq]
   void* out;                // [T, Hq, D] fp16, or fp32 for the partial entry point
   float* lse_out;           // [T, Hq] or null
   int out_f16;
@@ -106,17 +118,27 @@ __device__ __forceinline__ int mq_q_end(const MqParams& p, int s) {
 // ---------------------------------------------------------------------------
 // plan: the tiles, their units and the run schedule (one wave)
 
-template <int G>
+template <int Qt>
 __global__ __launch_bounds__(kWave) void mq_plan_kernel(MqParams p) {
-  constexpr int Qt = 16 / G;
-  __shared__ int toff[kMqMaxSeqs + 1];             // first tile of each sequence
+  // per sequence: first tile, first query row, query count, cached tokens
+  __shared__ int toff[kMqMaxSeqs + 1];
+  __shared__ int sqb[kMqMaxSeqs];
+  __shared__ int snq[kMqMaxSeqs];
+  __shared__ int sn[kMqMaxSeqs];
   const int lane = threadIdx.x;
 
   int carry = 0;
   for (int s0 = 0; s0 < p.S; s0 += kWave) {
     const int s = s0 + lane;
     int nt = 0;
-    if (s < p.S) nt = (mq_q_end(p, s) - mq_q_begin(p, s) + Qt - 1) / Qt;
+    if (s < p.S) {
+      const int qb = mq_q_begin(p, s);
+      const int nq = mq_q_end(p, s) - qb;
+      sqb[s] = qb;
+      snq[s] = nq;
+      sn[s] = mq_seq_len(p, s);
+      nt = (nq + Qt - 1) / Qt;
+    }
     const int incl = carry + wave_inclusive_scan_i32(nt, lane);
     if (s < p.S) toff[s] = incl - nt;
     carry = __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -134,11 +156,10 @@ __global__ __launch_bounds__(kWave) void mq_plan_kernel(MqParams p) {
     }
     s = lo;
     const int j = i - toff[s];
-    const int qb = mq_q_begin(p, s);
-    const int nq_seq = mq_q_end(p, s) - qb;
-    q0 = qb + j * Qt;
+    const int nq_seq = snq[s];
+    q0 = sqb[s] + j * Qt;
     nq = min(Qt, nq_seq - j * Qt);
-    const int n = mq_seq_len(p, s);
+    const int n = sn[s];
     if (p.causal) {
       base = n - nq_seq + j * Qt + 1;
       ntok = min(max(base + nq - 1, 0), n);
@@ -199,222 +220,14 @@ __global__ __launch_bounds__(kWave) void mq_plan_kernel(MqParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// tile kernel
-
-// Per-wave softmax state of one segment: rows 4c + r (r = 0..3) in lane group c.
-struct MqSeg {
-  float m[4];               // running max of the row (base 2)
-  float lp[4];              // running sum of p of this lane's token slot
-  f32x4 acc[8];             // p.V tiles: lane (c, n), tile u, reg r = row 4c + r, dim 8n + u
-};
-
-// One 16-token block starting at token t0.  rend[r]: the row's visible tokens
-// end (exclusive) inside this segment; nvalid: tokens of the block before the
-// segment's end.
-template <bool kMasked>
-__device__ __forceinline__ void mq_fold(MqSeg& st, const half8_t (&qa)[4], const u32x4 (&kr)[4],
-                                        const u32x4 (&vr)[4], float* lds_p, float qk_scale,
-                                        int lane, int t0, const int (&rend)[4], int nvalid) {
-  const int t = lane & 15;
-  const int c = lane >> 4;
-  half8_t kop[4];
-  k_operands<false>(kr, kop);
-  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[i], kop[i], sc, 0, 0, 0);
-
-  bool valid[4];
-  float s[4], mb[4];
-  bool grow = false;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    valid[r] = !kMasked || t0 + t < rend[r];
-    s[r] = valid[r] ? sc[r] : -INFINITY;
-    const float x = row16_max(s[r]);
-    mb[r] = x == -INFINITY ? -INFINITY : x * qk_scale;   // a fully masked row stays -inf
-    grow |= mb[r] > st.m[r];
-  }
-  if (__ballot(grow) != 0) {        // uniform branch: some row's running max moved
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mn = fmaxf(st.m[r], mb[r]);
-      const float a = mn == st.m[r] ? 1.0f : fast_exp2(st.m[r] - mn);   // 0 on a row's first token
-      st.m[r] = mn;
-      st.lp[r] *= a;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) st.acc[u][r] *= a;
-    }
-  }
-  float pr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pr[r] = fast_exp2(fmaf(s[r], qk_scale, -st.m[r]));
-    if (kMasked) pr[r] = valid[r] ? pr[r] : 0.0f;        // -inf - (-inf) would be NaN
-    st.lp[r] += pr[r];
-  }
-  // P as the A operand of the p.V MFMAs through a 16x16 fp16 LDS tile laid
-  // out [row][c][i] = p[row][token 4i + c]
-  _Float16* tile = reinterpret_cast<_Float16*>(lds_p);
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    tile[(4 * c + r) * 16 + (t & 3) * 4 + (t >> 2)] = static_cast<_Float16>(pr[r]);
-  const half4_t pa = *reinterpret_cast<const half4_t*>(tile + t * 16 + c * 4);
-  pv_mfma<kMasked, false>(st.acc, pa, vr, c, nvalid);
-}
-
-// One wave: KV head g of tile i over tokens [tok_lo, tok_hi).
-template <int G>
-__device__ void mq_segment(const MqParams& p, float* lds_p, int lane, int g, int i, int tok_lo,
-                           int tok_hi, bool whole, int slot) {
-  constexpr int Qt = 16 / G;
-  const int c = lane >> 4, t = lane & 15;
-  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
-  const int n = mq_seq_len(p, s);
-
-  // Q as the MFMA A operand: row t is query t / G, head g*G + t % G
-  // (rows past the tile's queries load the tile's last query and are zeroed)
-  half8_t qa[4];
-  {
-    const int qi = t / G, j = t % G;
-    const int row = q0 + min(qi, nq - 1);
-    const _Float16* qrow = p.q + ((long long)row * p.Hq + (long long)g * G + j) * kD;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KvFmt<false>::q_dim(ii, c)) ^ p.q_sign;
-      if (qi >= nq) x = u32x4{0u, 0u, 0u, 0u};
-      qa[ii] = __builtin_bit_cast(half8_t, x);
-    }
-  }
-  // where each of this lane group's rows stops seeing tokens in this segment;
-  // rows past the tile's queries are never stored and see everything
-  int rend[4];
-  int row_min = tok_hi;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qi = (4 * c + r) / G;
-    int e = tok_hi;
-    if (qi < nq && p.causal) e = min(min(max(base + qi, 0), n), tok_hi);
-    rend[r] = e;
-    row_min = min(row_min, e);
-  }
-  // blocks wholly before every row's end skip the mask (uniform over the wave)
-  for (int m = 16; m < kWave; m <<= 1) row_min = min(row_min, __shfl_xor(row_min, m, kWave));
-  const int full_end = __builtin_amdgcn_readfirstlane(row_min);
-
-  const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
-  const long long block_bytes = (long long)kBS * row_bytes;
-  const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * 2 + 16 * c);
-  const unsigned v_lane = (unsigned)((c * p.Hkv + g) * kD * 2 + 16 * t);
-  const char* kbytes = reinterpret_cast<const char*>(p.k);
-  const char* vbytes = reinterpret_cast<const char*>(p.v);
-  const int32_t* bt_row = p.bt + (long long)s * p.bt_stride + tok_lo / kBS;
-  const int ntok = tok_hi - tok_lo;
-  const int nblk = (ntok + kBS - 1) / kBS;
-
-  MqSeg st;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    st.m[r] = -INFINITY;
-    st.lp[r] = 0.0f;
-  }
-#pragma unroll
-  for (int u = 0; u < 8; ++u) st.acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  int window = lane < nblk ? bt_row[lane] : 0;
-  auto block_off = [&](int kb) -> long long {
-    if ((kb & 63) == 0 && kb > 0) {
-      const int idx = kb + lane;
-      window = idx < nblk ? bt_row[idx] : 0;
-    }
-    const unsigned raw = (unsigned)__builtin_amdgcn_readlane(window, kb & 63);
-    const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
-    return blk * block_bytes;
-  };
-  auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
-    const char* kb = kbytes + off;
-    const char* vb = vbytes + off;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      kr[ii] = *reinterpret_cast<const u32x4*>(kb + k_lane + 64 * ii);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      vr[ii] = *reinterpret_cast<const u32x4*>(vb + v_lane + 4 * ii * row_bytes);
-  };
-  auto fold = [&](const u32x4 (&kr)[4], const u32x4 (&vr)[4], int kb) {
-    const int t0 = tok_lo + kb * kBS;
-    if (t0 + kBS > full_end)
-      mq_fold<true>(st, qa, kr, vr, lds_p, p.qk_scale, lane, t0, rend, tok_hi - t0);
-    else
-      mq_fold<false>(st, qa, kr, vr, lds_p, p.qk_scale, lane, t0, rend, kBS);
-  };
-
-  constexpr int NB = kMqRing;
-  u32x4 kbuf[NB][4], vbuf[NB][4];
-#pragma unroll
-  for (int ii = 0; ii < NB - 1; ++ii)
-    if (ii < nblk) load(block_off(ii), kbuf[ii], vbuf[ii]);
-  for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
-#pragma unroll
-    for (int sl = 0; sl < NB; ++sl) {
-      const int cur = kb0 + sl;
-      if (cur >= nblk) break;
-      const int nxt = cur + NB - 1;
-      if (nxt < nblk) load(block_off(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
-      fold(kbuf[sl], vbuf[sl], cur);
-    }
-  }
-
-  // epilogue: lane (c, n) holds rows 4c + r, dims 8n .. 8n+7
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float l = row16_sum(st.lp[r]);
-    const int row = 4 * c + r;
-    const int qi = row / G, j = row % G;
-    if (qi >= nq) continue;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const float lse = l > 0.0f ? (st.m[r] + __builtin_log2f(l)) * kLn2 : -INFINITY;
-    float o[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = st.acc[u][r] * inv;
-    const int h = g * G + j;
-    if (whole) {
-      const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 8 * t;
-      if (p.out_f16) {
-        half8_t hv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(o[e]);
-        *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
-      } else {
-        float* d = static_cast<float*>(p.out) + dst;
-        *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      }
-      if (p.lse_out && t == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse;
-    } else {
-      const long long sl = ((long long)slot * Qt + qi) * p.Hq + h;
-      float* d = p.ws_o + sl * kD + 8 * t;
-      *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      if (t == 0) p.ws_lse[sl] = lse;
-    }
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
-void mq_kernel(MqParams p) {
-  __shared__ float lds[kMqWaves][kBS * 16 / 2];    // one 16x16 fp16 P tile per wave
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int n_hgroups = p.Hkv / p.hg;
-  const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
-  const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
+// The segments of run w, in order: (tile i, tokens [tok_lo, tok_hi), whole
+// tile?, partial slot).  Uniform over the work-group.
+template <typename F>
+__device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& fn) {
   const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4];
   const int u_lo = w * k;
   const int u_hi = min(u_lo + k, U);
   if (u_lo >= u_hi || n_tiles <= 0) return;
-
   // the tile holding unit u_lo: the last tile whose first unit is <= u_lo
   int lo = 0, hi = n_tiles - 1;
   while (lo < hi) {
@@ -428,25 +241,403 @@ void mq_kernel(MqParams p) {
     const int p_lo = u - before;
     const int p_hi = min(u_hi - before, nu);
     if (p_hi <= p_lo) continue;
-    const int tok_lo = p_lo * p.P;
-    const int tok_hi = min(p_hi * p.P, p.t_ntok[i]);
-    mq_segment<G>(p, lds[wave], lane, g, i, tok_lo, tok_hi, p_lo == 0 && p_hi == nu,
-                  w + p.t_rank[i]);
+    fn(i, p_lo * p.P, min(p_hi * p.P, p.t_ntok[i]), p_lo == 0 && p_hi == nu, w + p.t_rank[i]);
     u = before + p_hi;
   }
 }
 
 // ---------------------------------------------------------------------------
-// merge: tiles cut by run boundaries, and tiles that see no token
+// per-wave fold of 16-token blocks
+
+// Softmax state of NT row blocks of 16 rows; in block b, lane group c holds
+// rows row0 + 16b + 4c + r (r = 0..3).
+template <int NT>
+struct MqSeg {
+  float m[NT][4];           // running max of the row (base 2)
+  float lp[NT][4];          // running sum of p of this lane's token slot
+  f32x4 acc[NT][8];         // p.V tiles: lane (c, n), tile u, reg r, dim 8n + u
+};
+
+template <int NT>
+__device__ __forceinline__ void mq_seg_init(MqSeg<NT>& st) {
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st.m[b][r] = -INFINITY;
+      st.lp[b][r] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st.acc[b][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
+// B operands of the 8 p.V MFMA tiles from one block's fp16 V loads, shared by
+// the NT row blocks: tile u covers dims 8n + u and the contraction index 4c + i
+// stands for token 4i + c, so lane (c, n) takes element u of its own four V
+// rows (the fp16 layout of pv_mfma).  Tokens at or past nvalid are exact zero
+// rows.
+template <bool kMasked>
+__device__ __forceinline__ void mq_v_operands(const u32x4 (&vr)[4], int c, int nvalid,
+                                              half4_t (&vb)[8]) {
+  u32x4 vv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    vv[i] = (!kMasked || 4 * i + c < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int w = u / 2;
+    const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+    const unsigned d01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
+    const unsigned d23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
+    vb[u] = __builtin_bit_cast(half4_t, u32x2{d01, d23});
+  }
+}
+
+// One 16-token block starting at token t0, one row block at a time (scores,
+// max, rescale, p, p.V).  kr: K token t (lane & 15), 16 bytes at 16c + 64i; vr:
+// V tokens 4i + c, dims 8n .. 8n+7.  In a masked block, row row0 + 16b + 4c + r
+// (query qi of the tile) sees tokens before min(base + qi, n, tok_hi) when
+// causal, before tok_hi otherwise; rows past the tile's queries see everything
+// and are never stored.  Tokens at or past t0 + nvalid are exact zeros.
+template <int G, int NT, bool kMasked>
+__device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4],
+                                        const u32x4 (&kr)[4], const u32x4 (&vr)[4],
+                                        _Float16* lds_p, float qk_scale, int lane, int row0,
+                                        int t0, int nvalid, int causal_base, int n, int nq,
+                                        int tok_hi) {
+  const int t = lane & 15;
+  const int c = lane >> 4;
+  half8_t kop[4];
+  k_operands<false>(kr, kop);
+  half4_t vb[8];
+  mq_v_operands<kMasked>(vr, c, nvalid, vb);
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[b][i], kop[i], sc, 0, 0, 0);
+    bool valid[4];
+    float sv[4], mb[4];
+    bool grow = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (kMasked) {
+        const int qi = (row0 + 16 * b + 4 * c + r) / G;
+        int e = tok_hi;
+        if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n), tok_hi);
+        valid[r] = t0 + t < e;
+      } else {
+        valid[r] = true;
+      }
+      sv[r] = valid[r] ? sc[r] : -INFINITY;
+      const float x = row16_max(sv[r]);
+      mb[r] = x == -INFINITY ? -INFINITY : x * qk_scale;   // a fully masked row stays -inf
+      grow |= mb[r] > st.m[b][r];
+    }
+    if (__ballot(grow) != 0) {      // uniform branch: some row's running max moved
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mn = fmaxf(st.m[b][r], mb[r]);
+        const float a = mn == st.m[b][r] ? 1.0f : fast_exp2(st.m[b][r] - mn);
+        st.m[b][r] = mn;
+        st.lp[b][r] *= a;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) st.acc[b][u][r] *= a;
+      }
+    }
+    // p of this row block as the A operand of its p.V MFMAs, through a 16x16
+    // fp16 LDS tile laid out [row][c][i] = p[row][token 4i + c]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float pr = fast_exp2(fmaf(sv[r], qk_scale, -st.m[b][r]));
+      if (kMasked) pr = valid[r] ? pr : 0.0f;            // -inf - (-inf) would be NaN
+      st.lp[b][r] += pr;
+      lds_p[b * 256 + (4 * c + r) * 16 + (t & 3) * 4 + (t >> 2)] = static_cast<_Float16>(pr);
+    }
+    const half4_t pa = *reinterpret_cast<const half4_t*>(lds_p + b * 256 + t * 16 + c * 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      st.acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb[u], st.acc[b][u], 0, 0, 0);
+  }
+}
+
+// Q as the MFMA A operands of rows row0 .. row0 + 16 NT - 1 of a tile: row m
+// is query m / G, head g*G + m % G; rows past the tile's queries load its last
+// query and are zeroed.
+template <int G, int NT>
+__device__ __forceinline__ void mq_load_q(const MqParams& p, int g, int q0, int nq, int row0,
+                                          int lane, half8_t (&qa)[NT][4]) {
+  const int c = lane >> 4, t = lane & 15;
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    const int m = row0 + 16 * b + t;
+    const int qi = m / G, j = m % G;
+    const int row = q0 + min(qi, nq - 1);
+    const _Float16* qrow = p.q + ((long long)row * p.Hq + (long long)g * G + j) * kD;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KvFmt<false>::q_dim(ii, c)) ^ p.q_sign;
+      if (qi >= nq) x = u32x4{0u, 0u, 0u, 0u};
+      qa[b][ii] = __builtin_bit_cast(half8_t, x);
+    }
+  }
+}
+
+// Normalise and store rows row0 .. of the wave: lane (c, n) holds rows
+// row0 + 16b + 4c + r, dims 8n .. 8n+7.  A whole tile writes the output; a
+// segment of a cut tile writes its partial to slot `slot`.
+template <int G, int NT, int Qt>
+__device__ __forceinline__ void mq_store(const MqParams& p, MqSeg<NT>& st, int g, int q0, int nq,
+                                         int row0, int lane, bool whole, int slot) {
+  const int c = lane >> 4, t = lane & 15;
+#pragma unroll
+  for (int b = 0; b < NT; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float l = row16_sum(st.lp[b][r]);
+      const int row = row0 + 16 * b + 4 * c + r;
+      const int qi = row / G, j = row % G;
+      if (qi >= nq) continue;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const float lse = l > 0.0f ? (st.m[b][r] + __builtin_log2f(l)) * kLn2 : -INFINITY;
+      float o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = st.acc[b][u][r] * inv;
+      const int h = g * G + j;
+      if (whole) {
+        const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 8 * t;
+        if (p.out_f16) {
+          half8_t hv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(o[e]);
+          *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+        } else {
+          float* d = static_cast<float*>(p.out) + dst;
+          *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        }
+        if (p.lse_out && t == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse;
+      } else {
+        const long long sl = ((long long)slot * Qt + qi) * p.Hq + h;
+        float* d = p.ws_o + sl * kD + 8 * t;
+        *reinterpret_cast<f32x4*>(d) = f32x4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4], o[5], o[6], o[7]};
+        if (t == 0) p.ws_lse[sl] = lse;
+      }
+    }
+}
+
+// The block-table window of a segment: lane i holds the id of block (window
+// base + i); ids outside the pool are clamped (a broken table gives wrong
+// numbers, not a fault).
+struct BlockWindow {
+  const int32_t* row;
+  int nblk, lane, ids;
+  long long num_blocks, block_bytes;
+  __device__ BlockWindow(const int32_t* r, int nb, int ln, long long nblocks, long long bbytes)
+      : row(r), nblk(nb), lane(ln), num_blocks(nblocks), block_bytes(bbytes) {
+    ids = lane < nblk ? row[lane] : 0;
+  }
+  __device__ __forceinline__ long long offset(int kb) {
+    if ((kb & 63) == 0 && kb > 0) {
+      const int idx = kb + lane;
+      ids = idx < nblk ? row[idx] : 0;
+    }
+    const unsigned raw = (unsigned)__builtin_amdgcn_readlane(ids, kb & 63);
+    const long long blk = raw < (unsigned long long)num_blocks ? (long long)raw : 0;
+    return blk * block_bytes;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// register kernel: one wave per KV head, one 16-row tile per wave
 
 template <int G>
-__global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
+__device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int g, int i,
+                               int tok_lo, int tok_hi, bool whole, int slot) {
   constexpr int Qt = 16 / G;
+  const int c = lane >> 4, t = lane & 15;
+  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
+  const int n = mq_seq_len(p, s);
+  half8_t qa[1][4];
+  mq_load_q<G, 1>(p, g, q0, nq, 0, lane, qa);
+  // blocks wholly before the tile's first query's end skip the mask
+  const int causal_base = p.causal ? base : kNoMask;
+  const int full_end = p.causal ? min(min(max(base, 0), n), tok_hi) : tok_hi;
+
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
+  const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * 2 + 16 * c);
+  const unsigned v_lane = (unsigned)((c * p.Hkv + g) * kD * 2 + 16 * t);
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
+  const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
+  BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
+                  (long long)kBS * row_bytes);
+
+  MqSeg<1> st;
+  mq_seg_init(st);
+  auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      kr[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + k_lane + 64 * ii);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      vr[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + v_lane + 4 * ii * row_bytes);
+  };
+  constexpr int NB = kRegRing;
+  u32x4 kbuf[NB][4], vbuf[NB][4];
+#pragma unroll
+  for (int ii = 0; ii < NB - 1; ++ii)
+    if (ii < nblk) load(win.offset(ii), kbuf[ii], vbuf[ii]);
+  for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
+#pragma unroll
+    for (int sl = 0; sl < NB; ++sl) {
+      const int cur = kb0 + sl;
+      if (cur >= nblk) break;
+      const int nxt = cur + NB - 1;
+      if (nxt < nblk) load(win.offset(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
+      const int t0 = tok_lo + cur * kBS;
+      if (t0 + kBS > full_end)
+        mq_fold<G, 1, true>(st, qa, kbuf[sl], vbuf[sl], lds_p, p.qk_scale, lane, 0, t0,
+                            tok_hi - t0, causal_base, n, nq, tok_hi);
+      else
+        mq_fold<G, 1, false>(st, qa, kbuf[sl], vbuf[sl], lds_p, p.qk_scale, lane, 0, t0, kBS,
+                             causal_base, n, nq, tok_hi);
+    }
+  }
+  mq_store<G, 1, Qt>(p, st, g, q0, nq, 0, lane, whole, slot);
+}
+
+template <int G>
+__global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void mq_reg_kernel(MqParams p) {
+  __shared__ _Float16 lds[kMqWaves][256];          // one 16x16 fp16 P tile per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n_hgroups = p.Hkv / p.hg;
+  const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
+  const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
+  for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
+    mq_reg_segment<G>(p, lds[wave], lane, g, i, tok_lo, tok_hi, whole, slot);
+  });
+}
+
+// ---------------------------------------------------------------------------
+// shared kernel: 4 waves per KV head share each K/V block through LDS
+
+template <int G, int NT>
+__device__ void mq_shared_segment(const MqParams& p, char* kv, _Float16* lds_p, int lane, int wave,
+                                  int g, int i, int tok_lo, int tok_hi, bool whole, int slot) {
+  constexpr int Qt = 64 * NT / G;
+  constexpr int kStage = 2 * kBS * kLdsRow;        // K rows then V rows of one block
+  const int c = lane >> 4, t = lane & 15;
+  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
+  const int n = mq_seq_len(p, s);
+  const int row0 = wave * 16 * NT;                  // this wave's first row of the tile
+  const bool idle = row0 / G >= nq;                 // none of the tile's queries (uniform)
+  half8_t qa[NT][4];
+  mq_load_q<G, NT>(p, g, q0, nq, row0, lane, qa);
+  const int causal_base = p.causal ? base : kNoMask;
+  const int full_end = p.causal ? min(min(max(base + row0 / G, 0), n), tok_hi) : tok_hi;
+
+  // thread (wave, lane) moves 16 bytes of K and of V of each block: token
+  // tid / 16, bytes 16 * (tid % 16) of the 256-byte row of KV head g
+  const int tid = wave * kWave + lane;
+  const int ltok = tid >> 4, lchunk = tid & 15;
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
+  const unsigned g_off = (unsigned)((ltok * p.Hkv + g) * kD * 2 + 16 * lchunk);
+  const int s_off = ltok * kLdsRow + 16 * lchunk;
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
+  const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
+  BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
+                  (long long)kBS * row_bytes);
+
+  MqSeg<NT> st;
+  mq_seg_init(st);
+  constexpr int NB = kShPrefetch;                  // even: stage = block parity = slot parity
+  u32x4 pk[NB], pv[NB];
+#pragma unroll
+  for (int ii = 0; ii < NB - 1; ++ii)
+    if (ii < nblk) {
+      const long long off = win.offset(ii);
+      pk[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + g_off);
+      pv[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + g_off);
+    }
+  for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
+#pragma unroll
+    for (int sl = 0; sl < NB; ++sl) {
+      const int cur = kb0 + sl;
+      if (cur >= nblk) break;
+      const int nxt = cur + NB - 1;
+      if (nxt < nblk) {
+        const long long off = win.offset(nxt);
+        pk[(sl + NB - 1) % NB] = *reinterpret_cast<const u32x4*>(kbytes + off + g_off);
+        pv[(sl + NB - 1) % NB] = *reinterpret_cast<const u32x4*>(vbytes + off + g_off);
+      }
+      // stage block cur; every wave finished the block that last used this
+      // stage before the previous barrier
+      char* stage = kv + (sl & 1) * kStage;
+      *reinterpret_cast<u32x4*>(stage + s_off) = pk[sl];
+      *reinterpret_cast<u32x4*>(stage + kBS * kLdsRow + s_off) = pv[sl];
+      __syncthreads();
+      if (!idle) {
+        u32x4 kr[4], vr[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          kr[ii] = *reinterpret_cast<const u32x4*>(stage + t * kLdsRow + 16 * c + 64 * ii);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          vr[ii] = *reinterpret_cast<const u32x4*>(stage + kBS * kLdsRow +
+                                                   (4 * ii + c) * kLdsRow + 16 * t);
+        const int t0 = tok_lo + cur * kBS;
+        if (t0 + kBS > full_end)
+          mq_fold<G, NT, true>(st, qa, kr, vr, lds_p, p.qk_scale, lane, row0, t0, tok_hi - t0,
+                               causal_base, n, nq, tok_hi);
+        else
+          mq_fold<G, NT, false>(st, qa, kr, vr, lds_p, p.qk_scale, lane, row0, t0, kBS,
+                                causal_base, n, nq, tok_hi);
+      }
+    }
+  }
+  __syncthreads();                                  // the stages are free for the next segment
+  if (!idle) mq_store<G, NT, Qt>(p, st, g, q0, nq, row0, lane, whole, slot);
+}
+
+template <int G, int NT>
+__global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void mq_shared_kernel(MqParams p) {
+  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kBS * kLdsRow];   // 2 stages of K, V
+  __shared__ _Float16 lds[kMqWaves][NT * 256];     // NT 16x16 fp16 P tiles per wave
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
+  const int g = blockIdx.x % p.Hkv;                 // KV head
+  for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
+    mq_shared_segment<G, NT>(p, kv, lds[wave], lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+  });
+}
+
+// ---------------------------------------------------------------------------
+// merge: the rows of tiles cut by run boundaries, and of tiles that see no
+// token; one wave per (listed tile, row), spread over the grid
+
+template <int Qt>
+__global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4], n_fix = p.hdr[5];
-  for (int f = blockIdx.x; f < n_fix; f += gridDim.x) {
+  const long long rows = (long long)Qt * p.Hq;
+  const long long total = (long long)n_fix * rows;
+  for (long long idx = (long long)blockIdx.x * 4 + wave; idx < total;
+       idx += (long long)gridDim.x * 4) {
+    const int f = (int)(idx / rows);
+    const int row = (int)(idx % rows);
     const int i = p.t_fix[f];
+    const int qi = row / p.Hq, h = row % p.Hq;
+    if (qi >= p.t_nq[i]) continue;
     const int ub = p.t_ub[i];
     const int nu = (i + 1 < n_tiles ? p.t_ub[i + 1] : U) - ub;
     int nseg = 0;
@@ -456,21 +647,17 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
       nseg = w1 - w0 + 1;
       slot0 = (long long)w0 + p.t_rank[i];
     }
-    const int q0 = p.t_q0[i], nq = p.t_nq[i];
-    for (int row = wave; row < nq * p.Hq; row += 4) {
-      const int qi = row / p.Hq, h = row % p.Hq;
-      f32x2 res;
-      float lse_res;
-      merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, (long long)Qt * p.Hq, row, lane, res, lse_res);
-      const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 2 * lane;
-      if (p.out_f16) {
-        half2_t hv = {static_cast<_Float16>(res.x), static_cast<_Float16>(res.y)};
-        *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
-      } else {
-        *reinterpret_cast<f32x2*>(static_cast<float*>(p.out) + dst) = res;
-      }
-      if (p.lse_out && lane == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse_res;
+    f32x2 res;
+    float lse_res;
+    merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, rows, row, lane, res, lse_res);
+    const long long dst = ((long long)(p.t_q0[i] + qi) * p.Hq + h) * kD + 2 * lane;
+    if (p.out_f16) {
+      half2_t hv = {static_cast<_Float16>(res.x), static_cast<_Float16>(res.y)};
+      *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+    } else {
+      *reinterpret_cast<f32x2*>(static_cast<float*>(p.out) + dst) = res;
     }
+    if (p.lse_out && lane == 0) p.lse_out[(long long)(p.t_q0[i] + qi) * p.Hq + h] = lse_res;
   }
 }
 
@@ -478,23 +665,34 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
 // host side
 
 constexpr int kMaxDevices = 64;
+// tile kernel variants: 0 = register kernel, 1 = shared NT = 1, 2 = shared NT = 2
+constexpr int kMqVariants = 3;
 struct MqDeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMqWaves + 1] = {};   // [log2 G][waves per work-group]
+  int wg_per_cu[4][kMqVariants][kMqWaves + 1] = {};   // [log2 G][variant][waves per group]
 };
 MqDeviceFacts g_mq_dev[kMaxDevices];
 
-const void* mq_kernel_ptr(int G) {
-  switch (G) {
-    case 1: return reinterpret_cast<const void*>(&mq_kernel<1>);
-    case 2: return reinterpret_cast<const void*>(&mq_kernel<2>);
-    case 4: return reinterpret_cast<const void*>(&mq_kernel<4>);
-    default: return reinterpret_cast<const void*>(&mq_kernel<8>);
+int mq_log2(int x) { return x == 1 ? 0 : x == 2 ? 1 : x == 4 ? 2 : 3; }
+
+template <int G>
+const void* mq_kernel_ptr_g(int variant) {
+  switch (variant) {
+    case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G>);
+    case 1: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1>);
+    default: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 2>);
   }
 }
 
-int mq_log2(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
+const void* mq_kernel_ptr(int G, int variant) {
+  switch (G) {
+    case 1: return mq_kernel_ptr_g<1>(variant);
+    case 2: return mq_kernel_ptr_g<2>(variant);
+    case 4: return mq_kernel_ptr_g<4>(variant);
+    default: return mq_kernel_ptr_g<8>(variant);
+  }
+}
 
 int mq_head_group(int Hkv) {
   for (int hg = kMqWaves; hg > 1; --hg)
@@ -502,13 +700,33 @@ int mq_head_group(int Hkv) {
   return 1;
 }
 
+#ifndef PDA_MQ_MAX_VARIANT
+#define PDA_MQ_MAX_VARIANT 2      // largest tile kernel variant the host picks
+#endif
+
+// Tile kernel for the average query rows per sequence (query tokens x G).  Up
+// to 32 rows the register kernel (16-row tiles; a second tile of the same
+// sequence re-reads its K/V mostly from L2, and there is no barrier per block),
+// measured faster than one shared 64-row tile on MI355X (speculative
+// verification, 24 rows: 144 vs 218 us); above, the shared kernel with 64
+// (NT = 1) or 128 (NT = 2) rows per tile, so that a sequence's K/V is read by
+// few tiles (chunked prefill, 4096 rows: 1.72 ms at NT = 2, 1.84 ms at NT = 1,
+// 3.76 ms with 16-row register tiles).
+int mq_variant(int S, int T, int G) {
+  const long long rows = (long long)((T + S - 1) / std::max(S, 1)) * G;
+  const int v = rows <= 32 ? 0 : rows <= 64 ? 1 : 2;
+  return std::min(v, PDA_MQ_MAX_VARIANT);
+}
+
+int mq_tile_queries(int variant, int G) { return (variant == 0 ? 16 : 64 * variant) / G; }
+
 // Runs of the unit stream: as many work-groups as fit on all CUs at once,
-// divided by the head groups.
-int mq_run_count(int G, int Hkv) {
-  const int hg = mq_head_group(Hkv);
-  const int n_hgroups = Hkv / hg;
+// divided by the work-groups one run has (its head groups, or its KV heads).
+int mq_run_count(int G, int variant, int Hkv) {
+  const int waves = variant == 0 ? mq_head_group(Hkv) : kMqWaves;
+  const int per_run = variant == 0 ? Hkv / mq_head_group(Hkv) : Hkv;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024 / n_hgroups;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024 / per_run;
   MqDeviceFacts& f = g_mq_dev[dev];
   std::call_once(f.once, [&f, dev] {
     int cus = 0;
@@ -517,20 +735,21 @@ int mq_run_count(int G, int Hkv) {
       cus = 256;
     f.cus = cus;
     for (int lg = 0; lg < 4; ++lg)
-      for (int w = 1; w <= kMqWaves; ++w) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mq_kernel_ptr(1 << lg), w * kWave, 0) !=
-                hipSuccess ||
-            n <= 0)
-          n = 1;
-        f.wg_per_cu[lg][w] = n;
-      }
+      for (int v = 0; v < kMqVariants; ++v)
+        for (int w = 1; w <= kMqWaves; ++w) {
+          int n = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mq_kernel_ptr(1 << lg, v),
+                                                           w * kWave, 0) != hipSuccess ||
+              n <= 0)
+            n = 1;
+          f.wg_per_cu[lg][v][w] = n;
+        }
   });
-  return std::max(1, f.cus * f.wg_per_cu[mq_log2(G)][hg] / n_hgroups);
+  return std::max(1, f.cus * f.wg_per_cu[mq_log2(G)][variant][waves] / per_run);
 }
 
 struct MqPlan {
-  int Qt = 0, P = 0, n_runs = 0, hg = 0, max_tokens = 0, tiles_max = 0, n_slots = 0;
+  int variant = 0, Qt = 0, P = 0, n_runs = 0, hg = 0, max_tokens = 0, tiles_max = 0, n_slots = 0;
   size_t hdr_offset = 0, tiles_offset = 0, lse_offset = 0, o_offset = 0, total = 0;
 };
 
@@ -566,9 +785,10 @@ int mq_check(int S, int T, int Hq, int Hkv, int D, int block_size, int max_block
 MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition_tokens) {
   MqPlan pl;
   const int G = Hq / Hkv;
-  pl.Qt = 16 / G;
+  pl.variant = mq_variant(S, T, G);
+  pl.Qt = mq_tile_queries(pl.variant, G);
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_runs = mq_run_count(G, Hkv);
+  pl.n_runs = mq_run_count(G, pl.variant, Hkv);
   pl.hg = mq_head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
   pl.tiles_max = (T + pl.Qt - 1) / pl.Qt + S;
@@ -584,10 +804,28 @@ MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition
 
 template <int G>
 void mq_launch(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
-  hipLaunchKernelGGL((mq_plan_kernel<G>), dim3(1), dim3(kWave), 0, stream, mp);
-  const dim3 grid((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
-  hipLaunchKernelGGL((mq_kernel<G>), grid, block, 0, stream, mp);
-  hipLaunchKernelGGL((mq_merge_kernel<G>), dim3((unsigned)pl.n_runs), dim3(256), 0, stream, mp);
+  constexpr int kQtReg = 16 / G, kQt1 = 64 / G, kQt2 = 128 / G;
+  // one wave per row of the at most n_runs - 1 cut tiles (the rows of empty
+  // tiles, rare, are covered by the grid-stride loop)
+  const long long merge_rows = (long long)std::max(pl.n_runs - 1, 1) * pl.Qt * mp.Hq;
+  const dim3 merge_grid((unsigned)std::min<long long>((merge_rows + 3) / 4, 1 << 20)),
+      merge_block(256);
+  if (pl.variant == 0) {
+    hipLaunchKernelGGL((mq_plan_kernel<kQtReg>), dim3(1), dim3(kWave), 0, stream, mp);
+    hipLaunchKernelGGL((mq_reg_kernel<G>), dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
+                       dim3((unsigned)(pl.hg * kWave)), 0, stream, mp);
+    hipLaunchKernelGGL((mq_merge_kernel<kQtReg>), merge_grid, merge_block, 0, stream, mp);
+  } else if (pl.variant == 1) {
+    hipLaunchKernelGGL((mq_plan_kernel<kQt1>), dim3(1), dim3(kWave), 0, stream, mp);
+    hipLaunchKernelGGL((mq_shared_kernel<G, 1>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+                       dim3(kMqWaves * kWave), 0, stream, mp);
+    hipLaunchKernelGGL((mq_merge_kernel<kQt1>), merge_grid, merge_block, 0, stream, mp);
+  } else {
+    hipLaunchKernelGGL((mq_plan_kernel<kQt2>), dim3(1), dim3(kWave), 0, stream, mp);
+    hipLaunchKernelGGL((mq_shared_kernel<G, 2>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+                       dim3(kMqWaves * kWave), 0, stream, mp);
+    hipLaunchKernelGGL((mq_merge_kernel<kQt2>), merge_grid, merge_block, 0, stream, mp);
+  }
 }
 
 int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,

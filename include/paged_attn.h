@@ -287,7 +287,7 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
  * workspace    device memory of at least pda_multi_query_workspace_size()
  *              bytes, 256-byte aligned; it holds the schedule and partials.
  * Shapes as for paged_decode_attn (fp16 caches, D = 128, block_size = 16,
- * Hq / Hkv in {1, 2, 4, 8}, Hkv <= 8), and S <= 8192.
+ * Hq / Hkv in {1, 2, 4, 8}, Hkv <= 8), and S <= 4000.
  *
  * Cascade attention for B decode requests in R groups that share a prefix
  * (requests group_start[r] .. group_start[r+1]-1 share prefix r): call

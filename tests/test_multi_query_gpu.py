@@ -70,6 +70,29 @@ def test_small_all_group_sizes(G, Hkv, causal, P):
     compare_lse(to_np(lse), ref_lse)
 
 
+# The library picks its tile kernel from the average query rows per sequence
+# (query tokens x G): up to 32 rows the register kernel, up to 64 the shared
+# kernel with 64-row tiles, above that 128-row tiles.  Each pattern lands in
+# one of the three, at every group size.
+VARIANT_ROWS = {"register": 24, "shared64": 48, "shared128": 200}
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("variant", sorted(VARIANT_ROWS))
+@pytest.mark.parametrize("causal", [True, False])
+def test_tile_kernel_variants(G, Hkv, variant, causal):
+    per_seq = max(1, VARIANT_ROWS[variant] // G)
+    lens = [per_seq + 3, 700, 95, per_seq]            # some sequences barely hold their queries
+    nq = [per_seq] * len(lens)
+    case = W.build_mq_case(lens, nq, G * Hkv, Hkv, causal=causal, seed=60 + G, device="cuda",
+                           name=f"mq_{variant}_G{G}")
+    for P in (0, 48):
+        out, lse = run_mq(case, P)
+        ref, ref_lse = oracle_mq(case)
+        compare_out(to_np(out), ref)
+        compare_lse(to_np(lse), ref_lse)
+
+
 def test_single_query_is_decode():
     lens = [1, 2, 15, 16, 17, 100, 511, 1537]
     case = W.build_mq_case(lens, [1] * len(lens), 32, 8, causal=True, seed=41, device="cuda",
