@@ -68,6 +68,7 @@ constexpr int kRegRing = 2;           // register kernel: K/V buffers per wave (
 constexpr int kShPrefetch = 4;        // shared kernel: blocks each thread holds (in flight + 1)
 constexpr int kLdsRow = 272;          // shared kernel: bytes per token row in LDS (256 + 16 padding)
 constexpr int kNoMask = -(1 << 30);   // causal base of a tile without the causal mask
+constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a row's reference max
 
 struct MqParams {
   const _Float16* q;        // [T, Hq, D]
@@ -249,41 +250,42 @@ __device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& f
 // ---------------------------------------------------------------------------
 // per-wave fold of 16-token blocks
 
-// Softmax state of NT row blocks of 16 rows; in block b, lane group c holds
-// rows row0 + 16b + 4c + r (r = 0..3).
+// Softmax state of NT row blocks of 16 rows.  The scores are computed
+// transposed, S^T = K Q^T, so lane (c, n) (c = lane >> 4, n = lane & 15) holds
+// row row0 + 16b + n at tokens 4c .. 4c+3 of a block: the running max and sum
+// are one value per lane for its row (the sum over the lane's own tokens).  The
+// p.V output holds rows row0 + 16b + 4c + r at lane (c, n), register r.
 template <int NT>
 struct MqSeg {
-  float m[NT][4];           // running max of the row (base 2)
-  float lp[NT][4];          // running sum of p of this lane's token slot
-  f32x4 acc[NT][8];         // p.V tiles: lane (c, n), tile u, reg r, dim 8n + u
+  float m[NT];              // running max of row n (base 2)
+  float lp[NT];             // running sum of p over this lane's tokens of row n
+  f32x4 acc[NT][8];         // p.V tiles: lane (c, n), tile u, reg r = row 4c + r, dim 8n + u
 };
 
 template <int NT>
 __device__ __forceinline__ void mq_seg_init(MqSeg<NT>& st) {
 #pragma unroll
   for (int b = 0; b < NT; ++b) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      st.m[b][r] = -INFINITY;
-      st.lp[b][r] = 0.0f;
-    }
+    st.m[b] = -INFINITY;
+    st.lp[b] = 0.0f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) st.acc[b][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 }
 
-// B operands of the 8 p.V MFMA tiles from one block's fp16 V loads, shared by
-// the NT row blocks: tile u covers dims 8n + u and the contraction index 4c + i
-// stands for token 4i + c, so lane (c, n) takes element u of its own four V
-// rows (the fp16 layout of pv_mfma).  Tokens at or past nvalid are exact zero
-// rows.
+// B operands of the 8 p.V MFMA tiles (v_mfma_f32_16x16x16_f16) from one
+// block's fp16 V rows, shared by the NT row blocks: tile u covers dims 8n + u,
+// and the contraction index 4c + i is token 4c + i, so lane (c, n) takes
+// element u of its own V rows 4c .. 4c+3 (loaded as dims 8n .. 8n+7).  Tokens
+// at or past nvalid are exact zero rows (selected, so a NaN in an unowned slot
+// cannot leak through 0 * NaN).
 template <bool kMasked>
 __device__ __forceinline__ void mq_v_operands(const u32x4 (&vr)[4], int c, int nvalid,
                                               half4_t (&vb)[8]) {
   u32x4 vv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    vv[i] = (!kMasked || 4 * i + c < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+    vv[i] = (!kMasked || 4 * c + i < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int w = u / 2;
@@ -294,19 +296,23 @@ __device__ __forceinline__ void mq_v_operands(const u32x4 (&vr)[4], int c, int n
   }
 }
 
-// One 16-token block starting at token t0, one row block at a time (scores,
-// max, rescale, p, p.V).  kr: K token t (lane & 15), 16 bytes at 16c + 64i; vr:
-// V tokens 4i + c, dims 8n .. 8n+7.  In a masked block, row row0 + 16b + 4c + r
-// (query qi of the tile) sees tokens before min(base + qi, n, tok_hi) when
-// causal, before tok_hi otherwise; rows past the tile's queries see everything
-// and are never stored.  Tokens at or past t0 + nvalid are exact zeros.
+// One 16-token block starting at token t0, one row block at a time.
+//   kr: K token n, 16 bytes at 16c + 64i; vr: V tokens 4c + i, dims 8n .. 8n+7.
+//   S^T = K Q^T: the K operands are the A side and the query rows the B side
+//   of four v_mfma_f32_16x16x32_f16, so lane (c, n) gets row n at tokens
+//   4c + r, which is also the lane's A operand of p.V (row n, contraction
+//   indices 4c .. 4c+3): p goes from the score registers to the p.V MFMAs
+//   without a transpose.
+// In a masked block, row row0 + 16b + n (query qi of the tile) sees tokens
+// before min(base + qi, n_seq, tok_hi) when causal, before tok_hi otherwise;
+// rows past the tile's queries see everything and are never stored.  Tokens at
+// or past t0 + nvalid are exact zeros.
 template <int G, int NT, bool kMasked>
 __device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4],
                                         const u32x4 (&kr)[4], const u32x4 (&vr)[4],
-                                        _Float16* lds_p, float qk_scale, int lane, int row0,
-                                        int t0, int nvalid, int causal_base, int n, int nq,
-                                        int tok_hi) {
-  const int t = lane & 15;
+                                        float qk_scale, int lane, int row0, int t0, int nvalid,
+                                        int causal_base, int n_seq, int nq, int tok_hi) {
+  const int n = lane & 15;
   const int c = lane >> 4;
   half8_t kop[4];
   k_operands<false>(kr, kop);
@@ -317,46 +323,50 @@ __device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[b][i], kop[i], sc, 0, 0, 0);
-    bool valid[4];
-    float sv[4], mb[4];
-    bool grow = false;
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[i], qa[b][i], sc, 0, 0, 0);
+    float sv[4];
+    if (kMasked) {
+      const int qi = (row0 + 16 * b + n) / G;
+      int e = tok_hi;
+      if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n_seq), tok_hi);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (kMasked) {
-        const int qi = (row0 + 16 * b + 4 * c + r) / G;
-        int e = tok_hi;
-        if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n), tok_hi);
-        valid[r] = t0 + t < e;
-      } else {
-        valid[r] = true;
-      }
-      sv[r] = valid[r] ? sc[r] : -INFINITY;
-      const float x = row16_max(sv[r]);
-      mb[r] = x == -INFINITY ? -INFINITY : x * qk_scale;   // a fully masked row stays -inf
-      grow |= mb[r] > st.m[b][r];
+      for (int r = 0; r < 4; ++r) sv[r] = t0 + 4 * c + r < e ? sc[r] : -INFINITY;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sc[r];
     }
-    if (__ballot(grow) != 0) {      // uniform branch: some row's running max moved
+    // The reference m of a row only has to be the same for all its tokens:
+    // it moves when a score exceeds it by more than kLazyMax (so p <= 2^kLazyMax
+    // in between), and then to the exact running max.  The check takes the
+    // lane's own 4 tokens; the max over the 4 lane groups only when it fires.
+    const float xl = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    if (__ballot(xl * qk_scale > st.m[b] + kLazyMax) != 0) {   // uniform branch
+      float x = fmaxf(xl, __shfl_xor(xl, 16, kWave));
+      x = fmaxf(x, __shfl_xor(x, 32, kWave));
+      float mb = x * qk_scale;
+      if (kMasked) mb = x == -INFINITY ? -INFINITY : mb;   // a fully masked row stays -inf
+      const float mn = fmaxf(st.m[b], mb);
+      const float a = mn == st.m[b] ? 1.0f : fast_exp2(st.m[b] - mn);   // 0 on a first token
+      st.m[b] = mn;
+      st.lp[b] *= a;
+      // the p.V output rows of this lane are 4c + r: their factors live in
+      // lanes 4c + r of lane group 0
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float mn = fmaxf(st.m[b][r], mb[r]);
-        const float a = mn == st.m[b][r] ? 1.0f : fast_exp2(st.m[b][r] - mn);
-        st.m[b][r] = mn;
-        st.lp[b][r] *= a;
+        const float ar = __shfl(a, 4 * c + r, kWave);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) st.acc[b][u][r] *= a;
+        for (int u = 0; u < 8; ++u) st.acc[b][u][r] *= ar;
       }
     }
-    // p of this row block as the A operand of its p.V MFMAs, through a 16x16
-    // fp16 LDS tile laid out [row][c][i] = p[row][token 4i + c]
+    float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float pr = fast_exp2(fmaf(sv[r], qk_scale, -st.m[b][r]));
-      if (kMasked) pr = valid[r] ? pr : 0.0f;            // -inf - (-inf) would be NaN
-      st.lp[b][r] += pr;
-      lds_p[b * 256 + (4 * c + r) * 16 + (t & 3) * 4 + (t >> 2)] = static_cast<_Float16>(pr);
+      pr[r] = fast_exp2(fmaf(sv[r], qk_scale, -st.m[b]));
+      if (kMasked) pr[r] = sv[r] == -INFINITY ? 0.0f : pr[r];   // -inf - (-inf) would be NaN
     }
-    const half4_t pa = *reinterpret_cast<const half4_t*>(lds_p + b * 256 + t * 16 + c * 4);
+    st.lp[b] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const half4_t pa = {static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
+                        static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       st.acc[b][u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb[u], st.acc[b][u], 0, 0, 0);
@@ -393,15 +403,26 @@ __device__ __forceinline__ void mq_store(const MqParams& p, MqSeg<NT>& st, int g
                                          int row0, int lane, bool whole, int slot) {
   const int c = lane >> 4, t = lane & 15;
 #pragma unroll
-  for (int b = 0; b < NT; ++b)
+  for (int b = 0; b < NT; ++b) {
+    // sum of row n over the 4 lane groups; then the values of the output rows
+    // 4c + r from lanes 4c + r
+    float lrow = st.lp[b];
+    lrow += __shfl_xor(lrow, 16, kWave);
+    lrow += __shfl_xor(lrow, 32, kWave);
+    float lr[4], mr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float l = row16_sum(st.lp[b][r]);
+      lr[r] = __shfl(lrow, 4 * c + r, kWave);
+      mr[r] = __shfl(st.m[b], 4 * c + r, kWave);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float l = lr[r];
       const int row = row0 + 16 * b + 4 * c + r;
       const int qi = row / G, j = row % G;
       if (qi >= nq) continue;
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      const float lse = l > 0.0f ? (st.m[b][r] + __builtin_log2f(l)) * kLn2 : -INFINITY;
+      const float lse = l > 0.0f ? (mr[r] + __builtin_log2f(l)) * kLn2 : -INFINITY;
       float o[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) o[u] = st.acc[b][u][r] * inv;
@@ -427,6 +448,7 @@ __device__ __forceinline__ void mq_store(const MqParams& p, MqSeg<NT>& st, int g
         if (t == 0) p.ws_lse[sl] = lse;
       }
     }
+  }
 }
 
 // The block-table window of a segment: lane i holds the id of block (window
@@ -455,8 +477,8 @@ struct BlockWindow {
 // register kernel: one wave per KV head, one 16-row tile per wave
 
 template <int G>
-__device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int g, int i,
-                               int tok_lo, int tok_hi, bool whole, int slot) {
+__device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
+                               bool whole, int slot) {
   constexpr int Qt = 16 / G;
   const int c = lane >> 4, t = lane & 15;
   const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
@@ -469,7 +491,7 @@ __device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int
 
   const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
   const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * 2 + 16 * c);
-  const unsigned v_lane = (unsigned)((c * p.Hkv + g) * kD * 2 + 16 * t);
+  const unsigned v_lane = (unsigned)((4 * c * p.Hkv + g) * kD * 2 + 16 * t);   // tokens 4c + i
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
@@ -484,7 +506,7 @@ __device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int
       kr[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + k_lane + 64 * ii);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-      vr[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + v_lane + 4 * ii * row_bytes);
+      vr[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + v_lane + ii * row_bytes);
   };
   constexpr int NB = kRegRing;
   u32x4 kbuf[NB][4], vbuf[NB][4];
@@ -500,10 +522,10 @@ __device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int
       if (nxt < nblk) load(win.offset(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
       const int t0 = tok_lo + cur * kBS;
       if (t0 + kBS > full_end)
-        mq_fold<G, 1, true>(st, qa, kbuf[sl], vbuf[sl], lds_p, p.qk_scale, lane, 0, t0,
-                            tok_hi - t0, causal_base, n, nq, tok_hi);
+        mq_fold<G, 1, true>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, tok_hi - t0,
+                            causal_base, n, nq, tok_hi);
       else
-        mq_fold<G, 1, false>(st, qa, kbuf[sl], vbuf[sl], lds_p, p.qk_scale, lane, 0, t0, kBS,
+        mq_fold<G, 1, false>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
                              causal_base, n, nq, tok_hi);
     }
   }
@@ -513,14 +535,13 @@ __device__ void mq_reg_segment(const MqParams& p, _Float16* lds_p, int lane, int
 template <int G>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_reg_kernel(MqParams p) {
-  __shared__ _Float16 lds[kMqWaves][256];          // one 16x16 fp16 P tile per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_hgroups = p.Hkv / p.hg;
   const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
   const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_reg_segment<G>(p, lds[wave], lane, g, i, tok_lo, tok_hi, whole, slot);
+    mq_reg_segment<G>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
@@ -528,8 +549,8 @@ void mq_reg_kernel(MqParams p) {
 // shared kernel: 4 waves per KV head share each K/V block through LDS
 
 template <int G, int NT>
-__device__ void mq_shared_segment(const MqParams& p, char* kv, _Float16* lds_p, int lane, int wave,
-                                  int g, int i, int tok_lo, int tok_hi, bool whole, int slot) {
+__device__ void mq_shared_segment(const MqParams& p, char* kv, int lane, int wave, int g, int i,
+                                  int tok_lo, int tok_hi, bool whole, int slot) {
   constexpr int Qt = 64 * NT / G;
   constexpr int kStage = 2 * kBS * kLdsRow;        // K rows then V rows of one block
   const int c = lane >> 4, t = lane & 15;
@@ -591,14 +612,14 @@ __device__ void mq_shared_segment(const MqParams& p, char* kv, _Float16* lds_p, 
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
           vr[ii] = *reinterpret_cast<const u32x4*>(stage + kBS * kLdsRow +
-                                                   (4 * ii + c) * kLdsRow + 16 * t);
+                                                   (4 * c + ii) * kLdsRow + 16 * t);
         const int t0 = tok_lo + cur * kBS;
         if (t0 + kBS > full_end)
-          mq_fold<G, NT, true>(st, qa, kr, vr, lds_p, p.qk_scale, lane, row0, t0, tok_hi - t0,
+          mq_fold<G, NT, true>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, tok_hi - t0,
                                causal_base, n, nq, tok_hi);
         else
-          mq_fold<G, NT, false>(st, qa, kr, vr, lds_p, p.qk_scale, lane, row0, t0, kBS,
-                                causal_base, n, nq, tok_hi);
+          mq_fold<G, NT, false>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, kBS, causal_base, n,
+                                nq, tok_hi);
       }
     }
   }
@@ -610,13 +631,12 @@ template <int G, int NT>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_shared_kernel(MqParams p) {
   __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kBS * kLdsRow];   // 2 stages of K, V
-  __shared__ _Float16 lds[kMqWaves][NT * 256];     // NT 16x16 fp16 P tiles per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
   const int g = blockIdx.x % p.Hkv;                 // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_shared_segment<G, NT>(p, kv, lds[wave], lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+    mq_shared_segment<G, NT>(p, kv, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
