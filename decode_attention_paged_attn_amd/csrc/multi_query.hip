@@ -476,15 +476,15 @@ struct BlockWindow {
 // ---------------------------------------------------------------------------
 // register kernel: one wave per KV head, one 16-row tile per wave
 
-template <int G>
+template <int G, int NT>
 __device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
                                bool whole, int slot) {
-  constexpr int Qt = 16 / G;
+  constexpr int Qt = 16 * NT / G;
   const int c = lane >> 4, t = lane & 15;
   const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
   const int n = mq_seq_len(p, s);
-  half8_t qa[1][4];
-  mq_load_q<G, 1>(p, g, q0, nq, 0, lane, qa);
+  half8_t qa[NT][4];
+  mq_load_q<G, NT>(p, g, q0, nq, 0, lane, qa);
   // blocks wholly before the tile's first query's end skip the mask
   const int causal_base = p.causal ? base : kNoMask;
   const int full_end = p.causal ? min(min(max(base, 0), n), tok_hi) : tok_hi;
@@ -498,7 +498,7 @@ __device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int to
   BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
                   (long long)kBS * row_bytes);
 
-  MqSeg<1> st;
+  MqSeg<NT> st;
   mq_seg_init(st);
   auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
 #pragma unroll
@@ -522,17 +522,17 @@ __device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int to
       if (nxt < nblk) load(win.offset(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
       const int t0 = tok_lo + cur * kBS;
       if (t0 + kBS > full_end)
-        mq_fold<G, 1, true>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, tok_hi - t0,
-                            causal_base, n, nq, tok_hi);
-      else
-        mq_fold<G, 1, false>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
+        mq_fold<G, NT, true>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, tok_hi - t0,
                              causal_base, n, nq, tok_hi);
+      else
+        mq_fold<G, NT, false>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
+                              causal_base, n, nq, tok_hi);
     }
   }
-  mq_store<G, 1, Qt>(p, st, g, q0, nq, 0, lane, whole, slot);
+  mq_store<G, NT, Qt>(p, st, g, q0, nq, 0, lane, whole, slot);
 }
 
-template <int G>
+template <int G, int NT>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_reg_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -541,7 +541,7 @@ void mq_reg_kernel(MqParams p) {
   const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
   const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_reg_segment<G>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
+    mq_reg_segment<G, NT>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
@@ -685,8 +685,9 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
 // host side
 
 constexpr int kMaxDevices = 64;
-// tile kernel variants: 0 = register kernel, 1 = shared NT = 1, 2 = shared NT = 2
-constexpr int kMqVariants = 3;
+// tile kernel variants: 0, 1 = register kernel with NT = 1, 2 (16- and 32-row
+// tiles); 2, 3 = shared kernel with NT = 1, 2 (64- and 128-row tiles)
+constexpr int kMqVariants = 4;
 struct MqDeviceFacts {
   std::once_flag once;
   int cus = 0;
@@ -699,8 +700,9 @@ int mq_log2(int x) { return x == 1 ? 0 : x == 2 ? 1 : x == 4 ? 2 : 3; }
 template <int G>
 const void* mq_kernel_ptr_g(int variant) {
   switch (variant) {
-    case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G>);
-    case 1: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1>);
+    case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 1>);
+    case 1: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 2>);
+    case 2: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1>);
     default: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 2>);
   }
 }
@@ -721,30 +723,33 @@ int mq_head_group(int Hkv) {
 }
 
 #ifndef PDA_MQ_MAX_VARIANT
-#define PDA_MQ_MAX_VARIANT 2      // largest tile kernel variant the host picks
+#define PDA_MQ_MAX_VARIANT 3      // largest tile kernel variant the host picks
 #endif
 
-// Tile kernel for the average query rows per sequence (query tokens x G).  Up
-// to 32 rows the register kernel (16-row tiles; a second tile of the same
-// sequence re-reads its K/V mostly from L2, and there is no barrier per block),
-// measured faster than one shared 64-row tile on MI355X (speculative
-// verification, 24 rows: 144 vs 218 us); above, the shared kernel with 64
-// (NT = 1) or 128 (NT = 2) rows per tile, so that a sequence's K/V is read by
-// few tiles (chunked prefill, 4096 rows: 1.72 ms at NT = 2, 1.84 ms at NT = 1,
-// 3.76 ms with 16-row register tiles).
+// Tile kernel for the average query rows per sequence (query tokens x G): the
+// register kernel with one or two 16-row blocks per wave up to 16 or 32 rows
+// (no barrier per block; each wave streams its own K/V), above that the
+// shared kernel with 64 (NT = 1) or 128 (NT = 2) rows per tile, so that a
+// sequence's K/V is read by few tiles.  Measured on MI355X: a 24-row workload
+// (speculative verification) ran faster on 16-row register tiles than on one
+// shared 64-row tile (144 vs 218 us); chunked prefill (4096 rows per
+// sequence) took 1.72 ms with 128-row shared tiles, 1.84 ms with 64-row ones
+// and 3.76 ms with 16-row register tiles (before the transposed-score fold).
 int mq_variant(int S, int T, int G) {
   const long long rows = (long long)((T + S - 1) / std::max(S, 1)) * G;
-  const int v = rows <= 32 ? 0 : rows <= 64 ? 1 : 2;
+  const int v = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
   return std::min(v, PDA_MQ_MAX_VARIANT);
 }
 
-int mq_tile_queries(int variant, int G) { return (variant == 0 ? 16 : 64 * variant) / G; }
+int mq_tile_queries(int variant, int G) { return (16 << variant) / G; }
+
+bool mq_is_shared(int variant) { return variant >= 2; }
 
 // Runs of the unit stream: as many work-groups as fit on all CUs at once,
 // divided by the work-groups one run has (its head groups, or its KV heads).
 int mq_run_count(int G, int variant, int Hkv) {
-  const int waves = variant == 0 ? mq_head_group(Hkv) : kMqWaves;
-  const int per_run = variant == 0 ? Hkv / mq_head_group(Hkv) : Hkv;
+  const int waves = mq_is_shared(variant) ? kMqWaves : mq_head_group(Hkv);
+  const int per_run = mq_is_shared(variant) ? Hkv : Hkv / mq_head_group(Hkv);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024 / per_run;
   MqDeviceFacts& f = g_mq_dev[dev];
@@ -822,29 +827,41 @@ MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition
   return pl;
 }
 
-template <int G>
-void mq_launch(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
-  constexpr int kQtReg = 16 / G, kQt1 = 64 / G, kQt2 = 128 / G;
+template <int Qt>
+void mq_launch_aux(bool plan, const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
+  if (plan) {
+    hipLaunchKernelGGL((mq_plan_kernel<Qt>), dim3(1), dim3(kWave), 0, stream, mp);
+    return;
+  }
   // one wave per row of the at most n_runs - 1 cut tiles (the rows of empty
   // tiles, rare, are covered by the grid-stride loop)
-  const long long merge_rows = (long long)std::max(pl.n_runs - 1, 1) * pl.Qt * mp.Hq;
-  const dim3 merge_grid((unsigned)std::min<long long>((merge_rows + 3) / 4, 1 << 20)),
-      merge_block(256);
-  if (pl.variant == 0) {
-    hipLaunchKernelGGL((mq_plan_kernel<kQtReg>), dim3(1), dim3(kWave), 0, stream, mp);
-    hipLaunchKernelGGL((mq_reg_kernel<G>), dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
-                       dim3((unsigned)(pl.hg * kWave)), 0, stream, mp);
-    hipLaunchKernelGGL((mq_merge_kernel<kQtReg>), merge_grid, merge_block, 0, stream, mp);
-  } else if (pl.variant == 1) {
-    hipLaunchKernelGGL((mq_plan_kernel<kQt1>), dim3(1), dim3(kWave), 0, stream, mp);
-    hipLaunchKernelGGL((mq_shared_kernel<G, 1>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+  const long long merge_rows = (long long)std::max(pl.n_runs - 1, 1) * Qt * mp.Hq;
+  hipLaunchKernelGGL((mq_merge_kernel<Qt>),
+                     dim3((unsigned)std::min<long long>((merge_rows + 3) / 4, 1 << 20)),
+                     dim3(256), 0, stream, mp);
+}
+
+template <int G, int V>
+void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
+  constexpr int Qt = (16 << V) / G;
+  mq_launch_aux<Qt>(true, mp, pl, stream);
+  if constexpr (V >= 2) {
+    hipLaunchKernelGGL((mq_shared_kernel<G, V - 1>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
                        dim3(kMqWaves * kWave), 0, stream, mp);
-    hipLaunchKernelGGL((mq_merge_kernel<kQt1>), merge_grid, merge_block, 0, stream, mp);
   } else {
-    hipLaunchKernelGGL((mq_plan_kernel<kQt2>), dim3(1), dim3(kWave), 0, stream, mp);
-    hipLaunchKernelGGL((mq_shared_kernel<G, 2>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
-                       dim3(kMqWaves * kWave), 0, stream, mp);
-    hipLaunchKernelGGL((mq_merge_kernel<kQt2>), merge_grid, merge_block, 0, stream, mp);
+    hipLaunchKernelGGL((mq_reg_kernel<G, V + 1>), dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
+                       dim3((unsigned)(pl.hg * kWave)), 0, stream, mp);
+  }
+  mq_launch_aux<Qt>(false, mp, pl, stream);
+}
+
+template <int G>
+void mq_launch(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
+  switch (pl.variant) {
+    case 0: mq_launch_v<G, 0>(mp, pl, stream); break;
+    case 1: mq_launch_v<G, 1>(mp, pl, stream); break;
+    case 2: mq_launch_v<G, 2>(mp, pl, stream); break;
+    default: mq_launch_v<G, 3>(mp, pl, stream); break;
   }
 }
 

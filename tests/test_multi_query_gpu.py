@@ -71,10 +71,11 @@ def test_small_all_group_sizes(G, Hkv, causal, P):
 
 
 # The library picks its tile kernel from the average query rows per sequence
-# (query tokens x G): up to 32 rows the register kernel, up to 64 the shared
-# kernel with 64-row tiles, above that 128-row tiles.  Each pattern lands in
-# one of the three, at every group size.
-VARIANT_ROWS = {"register": 24, "shared64": 48, "shared128": 200}
+# (query tokens x G): up to 16 and 32 rows the register kernel with one or two
+# 16-row blocks per wave, up to 64 the shared kernel with 64-row tiles, above
+# that 128-row tiles.  Each pattern lands in one of the four, at every group
+# size.
+VARIANT_ROWS = {"register16": 12, "register32": 28, "shared64": 48, "shared128": 200}
 
 
 @pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1)])
