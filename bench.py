@@ -35,6 +35,7 @@ CSRC = os.path.join(ROOT, "decode_attention_paged_attn_amd", "csrc")
 KERNEL_SOURCES = {
     "attention": ("paged_attn.hip", "pda_common.h"),
     "multi_query": ("multi_query.hip", "pda_common.h"),
+    "cascade": ("multi_query.hip", "paged_attn.hip", "pda_common.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -246,7 +247,7 @@ def bench_multi_query(case, P, steps, warmup):
              "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s"})
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = "paged_multi_query_attn call (plan + tile + merge kernels)"
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(f"multi_query:{case.name}", "multi_query")
     value = roof["achieved"] * ev_ms / wall_ms
     print(json.dumps({
         "metric": "multi-query paged attention: " + ("KV-read GB/s" if hbm_bound else "TFLOP/s"),
@@ -310,7 +311,7 @@ def bench_cascade(case, steps, warmup):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(unique_tok * row / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "cascade call (prefix pass + suffix pass + merge)",
-                     "traffic": None},
+                     "traffic": measured_traffic(f"cascade:{case.name}", "cascade")},
         "steps": steps, "warmup": warmup, "dtype": "fp16", "data": "synthetic",
         "config": {"workload": case.name, "requests": B,
                    "groups": len(case.prefix_lens_host),
