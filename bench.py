@@ -320,6 +320,54 @@ def bench_cascade(case, steps, warmup):
                    "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}), flush=True)
 
 
+def bench_partial_merge(case, steps, warmup):
+    """R range partials (paged_decode_attn_partial over block-table column slices)
+    plus merge_partials, against single-pass attention over the same batch."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    from decode_attention_paged_attn_amd import workloads as W
+    R = case.ranges
+    views = W.range_views(case, R)
+    B, Hq = case.B, case.Hq
+    o_parts = torch.empty((R, B, Hq, 128), dtype=torch.float32, device="cuda")
+    l_parts = torch.empty((R, B, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pda.workspace_size(B, Hq, case.Hkv, case.block_table.shape[1], 0), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def split_path():
+        for r, (bt, ln) in enumerate(views):
+            pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln, case.scale,
+                                          o=o_parts[r], lse=l_parts[r], workspace=ws)
+        pda.merge_partials(o_parts, l_parts, out=out, lse_out=lse)
+
+    def single():
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                              case.context_lens, case.scale, out=out, lse_out=lse, workspace=ws)
+
+    wall_ms, ev_ms, _ = _time_events(split_path, steps, warmup)
+    s_wall, s_ev, _ = _time_events(single, steps, warmup)
+    nbytes = kv_bytes(case.lens, case.Hkv)
+    print(json.dumps({
+        "metric": "disaggregated partial merge: KV-read GB/s (R range partials + merge_partials)",
+        "op": "paged_decode_attn_partial x R + merge_partials", "unit": "GB/s",
+        "value": round(nbytes / (wall_ms / 1e3) / 1e9, 2),
+        "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+        "ms_per_step": round(wall_ms, 5), "event_ms": round(ev_ms, 5),
+        "single_pass_event_ms": round(s_ev, 5),
+        "single_pass_event_GBps": round(nbytes / (s_ev / 1e3) / 1e9, 2),
+        "split_over_single_time": round(ev_ms / s_ev, 4),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel": "R partial calls + merge_partials", "traffic": None},
+        "steps": steps, "warmup": warmup, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": case.name, "batch": B, "q_heads": Hq, "kv_heads": case.Hkv,
+                   "head_dim": 128, "ranges": R, "tokens_per_sequence": int(case.lens[0]),
+                   "kv_bytes_per_step": nbytes}}), flush=True)
+
+
 def bench_append(case, steps, warmup):
     """Time paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16)."""
     import torch
@@ -365,11 +413,12 @@ def main():
     ap.add_argument("--also", default="llama8b_4k",
                     help="comma-separated extra workloads reported under 'also'")
     ap.add_argument("--op", default="attention",
-                    choices=["attention", "append", "multi_query", "cascade"],
+                    choices=["attention", "append", "multi_query", "cascade", "partial_merge"],
                     help="attention (default): paged_decode_attn; append: paged_kv_append of "
                          "one token per sequence; multi_query: paged_multi_query_attn on "
                          "--config spec_verify or chunked_prefill; cascade: "
-                         "cascade_decode_attn on --config shared_prefix")
+                         "cascade_decode_attn on --config shared_prefix; partial_merge: 4 range "
+                         "partials + merge_partials on disagg_merge, against single pass")
     ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
                     help="element type of the K/V cache (fp8: E4M3 codes with per-tensor scales)")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -404,6 +453,9 @@ def main():
     if args.op == "cascade":
         case = W.CASCADE_CONFIGS["shared_prefix"](device="cuda")
         bench_cascade(case, args.steps, args.warmup)
+        return
+    if args.op == "partial_merge":
+        bench_partial_merge(W.disagg_merge(device="cuda"), args.steps, args.warmup)
         return
     case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if args.op == "append":
