@@ -202,10 +202,12 @@ def mq_work(case):
     """(unique K/V bytes, algorithmic FLOPs) of one multi-query call.
 
     Bytes: every cached token of a sequence that some query sees, K and V, all
-    KV heads, once.  FLOPs: 4 * D per (query, query head, visible token): the
-    q.k dot product and the p.v accumulation, 2 * D each.
+    KV heads, once (2 bytes an element, 1 for an FP8 cache).  FLOPs: 4 * D per
+    (query, query head, visible token): the q.k dot product and the p.v
+    accumulation, 2 * D each.
     """
     Hkv, Hq, D = case.Hkv, case.Hq, 128
+    elem = 1 if case.kv_dtype == "fp8" else 2
     nbytes = flops = 0
     for n, nq in zip(case.lens, case.n_queries):
         n, nq = int(n), int(nq)
@@ -215,7 +217,7 @@ def mq_work(case):
             vis = [max(0, n - nq + i + 1) for i in range(nq)]
         else:
             vis = [n] * nq
-        nbytes += max(vis) * 2 * Hkv * D * 2
+        nbytes += max(vis) * 2 * Hkv * D * elem
         flops += 4 * D * Hq * sum(vis)
     return nbytes, flops
 
@@ -233,7 +235,7 @@ def bench_multi_query(case, P, steps, warmup):
         pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                    case.context_lens, case.query_start, case.scale,
                                    causal=case.causal, out=out, lse_out=lse,
-                                   partition_tokens=P, workspace=ws)
+                                   partition_tokens=P, workspace=ws, **case.attn_kwargs())
 
     wall_ms, ev_ms, ev_med = _time_events(step, steps, warmup)
     nbytes, flops = mq_work(case)
@@ -258,11 +260,11 @@ def bench_multi_query(case, P, steps, warmup):
         "kv_bytes_unique": nbytes, "flops": flops,
         "tflops": round(flops / (ev_ms / 1e3) / 1e12, 2),
         "kv_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
-        "roofline": roof, "steps": steps, "warmup": warmup, "dtype": "fp16",
+        "roofline": roof, "steps": steps, "warmup": warmup, "dtype": case.kv_dtype,
         "data": "synthetic", "kernel_source_sha256_16": source_hash("multi_query"),
         "config": {"workload": case.name, "sequences": case.S, "query_tokens": case.T,
                    "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 128,
-                   "causal": case.causal, "partition_tokens": P,
+                   "causal": case.causal, "partition_tokens": P, "kv_dtype": case.kv_dtype,
                    "context_tokens": int(case.lens.sum())}}), flush=True)
 
 
@@ -279,7 +281,7 @@ def bench_cascade(case, steps, warmup):
         pda.cascade_decode_attn(case.q, case.k_cache, case.v_cache, case.prefix_table,
                                 case.prefix_lens, case.group_start, case.suffix_table,
                                 case.suffix_lens, case.scale, out=out,
-                                partials=(o_parts, l_parts))
+                                partials=(o_parts, l_parts), **case.attn_kwargs())
 
     wall_ms, ev_ms, ev_med = _time_events(step, steps, warmup)
     table, lens = case.naive_table()
@@ -287,10 +289,10 @@ def bench_cascade(case, steps, warmup):
 
     def naive():
         pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, table, lens, case.scale,
-                              out=naive_out)
+                              out=naive_out, **case.attn_kwargs())
 
     n_wall, n_ev, _ = _time_events(naive, steps, warmup)
-    row = 2 * case.Hkv * 128 * 2                              # K and V bytes per token
+    row = 2 * case.Hkv * 128 * (1 if case.kv_dtype == "fp8" else 2)   # K and V bytes a token
     # tokens read: naive decode reads each group's prefix once per request,
     # cascade once per group; both read every suffix once
     naive_tok, unique_tok = 0, 0
@@ -312,8 +314,8 @@ def bench_cascade(case, steps, warmup):
                      "frac": round(unique_tok * row / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "cascade call (prefix pass + suffix pass + merge)",
                      "traffic": measured_traffic(f"cascade:{case.name}", "cascade")},
-        "steps": steps, "warmup": warmup, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": case.name, "requests": B,
+        "steps": steps, "warmup": warmup, "dtype": case.kv_dtype, "data": "synthetic",
+        "config": {"workload": case.name, "requests": B, "kv_dtype": case.kv_dtype,
                    "groups": len(case.prefix_lens_host),
                    "prefix_tokens": [int(x) for x in case.prefix_lens_host],
                    "suffix_tokens_total": int(case.suffix_lens_host.sum()),
@@ -447,11 +449,11 @@ def main():
     pda.load_library()
     if args.op == "multi_query":
         name = args.config if args.config in W.MQ_CONFIGS else "spec_verify"
-        case = W.MQ_CONFIGS[name](device="cuda")
+        case = W.MQ_CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)
         bench_multi_query(case, args.partition_tokens or 0, args.steps, args.warmup)
         return
     if args.op == "cascade":
-        case = W.CASCADE_CONFIGS["shared_prefix"](device="cuda")
+        case = W.CASCADE_CONFIGS["shared_prefix"](device="cuda", kv_dtype=args.kv_dtype)
         bench_cascade(case, args.steps, args.warmup)
         return
     if args.op == "partial_merge":

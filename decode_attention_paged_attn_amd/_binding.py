@@ -66,6 +66,14 @@ _SIGNATURES = {
                                                 _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                                 _c_i64, _c_int, _c_float, _c_int, _c_int, _vp,
                                                 _c_size, _vp]),
+    "paged_multi_query_attn_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_i64,
+                                            _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                            _c_int, _c_float, _c_float, _c_float, _c_int, _c_int,
+                                            _vp, _c_size, _vp]),
+    "paged_multi_query_attn_partial_fp8": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp,
+                                                    _c_i64, _vp, _c_int, _c_int, _c_int, _c_int,
+                                                    _c_int, _c_i64, _c_int, _c_float, _c_float,
+                                                    _c_float, _c_int, _c_int, _vp, _c_size, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -325,9 +333,14 @@ def multi_query_workspace_size(S, num_queries, Hq, Hkv, max_blocks_per_seq, part
 
 
 def _run_mq(partial, q, k_cache, v_cache, block_table, context_lens, query_start, scale, causal,
-            out, lse, need_lse, partition_tokens, workspace, max_blocks_per_seq):
-    if q.dtype != torch.float16 or k_cache.dtype != torch.float16 or v_cache.dtype != torch.float16:
-        raise TypeError("multi-query attention takes fp16 q and fp16 caches")
+            out, lse, need_lse, partition_tokens, workspace, max_blocks_per_seq, k_scale=None,
+            v_scale=None):
+    if q.dtype != torch.float16:
+        raise TypeError("q must be float16")
+    if not (k_cache.dtype == v_cache.dtype and
+            (k_cache.dtype == torch.float16 or k_cache.dtype in FP8_DTYPES)):
+        raise TypeError("k_cache and v_cache must both be float16, or both FP8 E4M3 codes "
+                        "(uint8 or float8_e4m3fn)")
     if (block_table.dtype != torch.int32 or context_lens.dtype != torch.int32
             or query_start.dtype != torch.int32):
         raise TypeError("block_table, context_lens and query_start must be int32")
@@ -370,40 +383,53 @@ def _run_mq(partial, q, k_cache, v_cache, block_table, context_lens, query_start
                             or not lse.is_contiguous()):
         raise ValueError("lse must be contiguous float32 [T, Hq]")
     lib = load_library()
-    fn = lib.paged_multi_query_attn_partial if partial else lib.paged_multi_query_attn
-    _check(fn(_ptr(out), _ptr(lse), _ptr(q), _ptr(query_start), T, _ptr(k_cache), _ptr(v_cache),
-              _ptr(block_table), bt_stride, _ptr(context_lens), S, Hq, Hkv, D, bs, num_blocks, mb,
-              float(scale), int(bool(causal)), int(partition_tokens), _ptr(workspace),
-              workspace.numel() * workspace.element_size(), _stream(dev)))
+    head = (_ptr(out), _ptr(lse), _ptr(q), _ptr(query_start), T, _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), bt_stride, _ptr(context_lens), S, Hq, Hkv, D, bs, num_blocks, mb,
+            float(scale))
+    tail = (int(bool(causal)), int(partition_tokens), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    if is_fp8_cache(k_cache):
+        if k_scale is None or v_scale is None:
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        fn = (lib.paged_multi_query_attn_partial_fp8 if partial
+              else lib.paged_multi_query_attn_fp8)
+        _check(fn(*head, float(k_scale), float(v_scale), *tail))
+    else:
+        fn = lib.paged_multi_query_attn_partial if partial else lib.paged_multi_query_attn
+        _check(fn(*head, *tail))
     return out, lse
 
 
 def paged_multi_query_attn(q, k_cache, v_cache, block_table, context_lens, query_start, scale,
                            causal=True, out=None, lse_out=None, return_lse=False,
-                           partition_tokens=0, workspace=None, max_blocks_per_seq=None):
+                           partition_tokens=0, workspace=None, max_blocks_per_seq=None,
+                           k_scale=None, v_scale=None):
     """Several query tokens per sequence over a paged KV cache; see include/paged_attn.h.
 
     q fp16 [T, Hq, D] with the queries of sequence s in rows
     query_start[s] .. query_start[s+1]-1 (the last tokens of the sequence).
+    fp16 caches, or FP8 E4M3 caches with per-tensor ``k_scale`` and ``v_scale``.
     Returns ``out`` (fp16 [T, Hq, D]) or ``(out, lse)``.
     """
     out, lse = _run_mq(False, q, k_cache, v_cache, block_table, context_lens, query_start, scale,
                        causal, out, lse_out, return_lse, partition_tokens, workspace,
-                       max_blocks_per_seq)
+                       max_blocks_per_seq, k_scale, v_scale)
     return (out, lse) if (return_lse or lse_out is not None) else out
 
 
 def paged_multi_query_attn_partial(q, k_cache, v_cache, block_table, context_lens, query_start,
                                    scale, causal=True, o=None, lse=None, partition_tokens=0,
-                                   workspace=None, max_blocks_per_seq=None):
+                                   workspace=None, max_blocks_per_seq=None, k_scale=None,
+                                   v_scale=None):
     """Normalised partial (o fp32 [T, Hq, D], lse fp32 [T, Hq]) of multi-query attention."""
     return _run_mq(True, q, k_cache, v_cache, block_table, context_lens, query_start, scale,
-                   causal, o, lse, True, partition_tokens, workspace, max_blocks_per_seq)
+                   causal, o, lse, True, partition_tokens, workspace, max_blocks_per_seq, k_scale,
+                   v_scale)
 
 
 def cascade_decode_attn(q, k_cache, v_cache, prefix_table, prefix_lens, group_start,
                         suffix_table, suffix_lens, scale, out=None, lse_out=None,
-                        return_lse=False, partials=None):
+                        return_lse=False, partials=None, k_scale=None, v_scale=None):
     """Decode attention of B requests whose contexts are a shared prefix then a suffix.
 
     Requests group_start[r] .. group_start[r+1]-1 share prefix r (prefix_table
@@ -411,7 +437,8 @@ def cascade_decode_attn(q, k_cache, v_cache, prefix_table, prefix_lens, group_st
     tokens of suffix_table row b.  Three library calls: the prefix pass with
     every request of a group as a query of its prefix (no mask), the suffix
     pass, and the log-sum-exp merge of the two partials.  ``partials`` may
-    pass preallocated (o fp32 [2, B, Hq, D], lse fp32 [2, B, Hq]).
+    pass preallocated (o fp32 [2, B, Hq, D], lse fp32 [2, B, Hq]).  FP8 caches take
+    ``k_scale`` and ``v_scale`` as the other calls do.
     """
     B, Hq, D = q.shape
     if partials is None:
@@ -420,9 +447,10 @@ def cascade_decode_attn(q, k_cache, v_cache, prefix_table, prefix_lens, group_st
     else:
         o_parts, l_parts = partials
     paged_multi_query_attn_partial(q, k_cache, v_cache, prefix_table, prefix_lens, group_start,
-                                   scale, causal=False, o=o_parts[0], lse=l_parts[0])
+                                   scale, causal=False, o=o_parts[0], lse=l_parts[0],
+                                   k_scale=k_scale, v_scale=v_scale)
     paged_decode_attn_partial(q, k_cache, v_cache, suffix_table, suffix_lens, scale,
-                              o=o_parts[1], lse=l_parts[1])
+                              o=o_parts[1], lse=l_parts[1], k_scale=k_scale, v_scale=v_scale)
     res = merge_partials(o_parts, l_parts, out=out, lse_out=lse_out,
                          return_lse=return_lse or lse_out is not None)
     return res

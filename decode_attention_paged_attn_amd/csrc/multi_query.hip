@@ -66,15 +66,18 @@ constexpr int kMqTileArrays = 8;      // seq, q0, nq, base, ntok, ub, rank, fix
 constexpr int kMqMaxPartition = 1 << 20;
 constexpr int kRegRing = 2;           // register kernel: K/V buffers per wave (blocks in flight + 1)
 constexpr int kShPrefetch = 4;        // shared kernel: blocks each thread holds (in flight + 1)
-constexpr int kLdsRow = 272;          // shared kernel: bytes per token row in LDS (256 + 16 padding)
+// shared kernel: bytes per token row of one KV head in LDS (the row, 256 bytes
+// fp16 or 128 FP8, plus 16 bytes of padding: conflict-free operand reads)
+template <bool kFp8>
+constexpr int lds_row() { return 128 * KvFmt<kFp8>::kElemBytes + 16; }
 constexpr int kNoMask = -(1 << 30);   // causal base of a tile without the causal mask
 constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a row's reference max
 
 struct MqParams {
   const _Float16* q;        // [T, Hq, D]
   const int32_t* qs;        // [S + 1]: queries of sequence s are rows qs[s] .. qs[s+1]-1
-  const _Float16* k;        // [num_blocks, 16, Hkv, D]
-  const _Float16* v;
+  const void* k;            // [num_blocks, 16, Hkv, D] fp16, or FP8 E4M3 codes
+  const void* v;
   const int32_t* bt;        // [S, bt_stride]
   const int32_t* ctx;       // [S] cached tokens, the queries' own included
   long long bt_stride;
@@ -85,7 +88,7 @@ struct MqParams {
   int n_runs;
   int hg;                   // KV heads per work-group; Hkv / hg head groups
   int causal;
-  float qk_scale;           // |scale| * log2(e)
+  float qk_scale;           // |scale * k_scale| * log2(e)
   unsigned q_sign;          // 0x80008000 to negate q (scale < 0), else 0
   int32_t* hdr;             // [kMqHdrInts]
   // per tile (tiles_max entries each)
@@ -102,6 +105,9 @@ struct MqParams {
   void* out;                // [T, Hq, D] fp16, or fp32 for the partial entry point
   float* lse_out;           // [T, Hq] or null
   int out_f16;
+  // last: inserted before the pointers above, it changed the generated code of
+  // the fp16 kernels (up to 30 more VGPRs and spills at 2 row blocks per wave)
+  float v_scale;            // multiplies the output (FP8 V scale; 1 for fp16)
 };
 
 __device__ __forceinline__ int mq_seq_len(const MqParams& p, int s) {
@@ -274,25 +280,51 @@ __device__ __forceinline__ void mq_seg_init(MqSeg<NT>& st) {
 }
 
 // B operands of the 8 p.V MFMA tiles (v_mfma_f32_16x16x16_f16) from one
-// block's fp16 V rows, shared by the NT row blocks: tile u covers dims 8n + u,
-// and the contraction index 4c + i is token 4c + i, so lane (c, n) takes
-// element u of its own V rows 4c .. 4c+3 (loaded as dims 8n .. 8n+7).  Tokens
-// at or past nvalid are exact zero rows (selected, so a NaN in an unowned slot
-// cannot leak through 0 * NaN).
-template <bool kMasked>
-__device__ __forceinline__ void mq_v_operands(const u32x4 (&vr)[4], int c, int nvalid,
-                                              half4_t (&vb)[8]) {
-  u32x4 vv[4];
+// block's V rows, shared by the NT row blocks: tile u covers dims 8n + u, and
+// the contraction index 4c + i is token 4c + i, so lane (c, n) takes element u
+// of its own V rows 4c .. 4c+3 (loaded as dims 8n .. 8n+7; FP8 codes are
+// transposed 4x4 by bytes and decoded exactly to fp16).  Tokens at or past
+// nvalid are exact zero rows (selected, so a NaN in an unowned slot cannot
+// leak through 0 * NaN).
+template <bool kMasked, bool kFp8>
+__device__ __forceinline__ void mq_v_operands(const typename KvFmt<kFp8>::VRow (&vr)[4], int c,
+                                              int nvalid, half4_t (&vb)[8]) {
+  if constexpr (kFp8) {
+    u32x2 vv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vv[i] = (!kMasked || 4 * c + i < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i)
+      vv[i] = (!kMasked || 4 * c + i < nvalid) ? vr[i] : u32x2{0u, 0u};   // code 0 = +0
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int w = u / 2;
-    const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-    const unsigned d01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
-    const unsigned d23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
-    vb[u] = __builtin_bit_cast(half4_t, u32x2{d01, d23});
+    for (int w = 0; w < 2; ++w) {
+      // dims 8n + 4w + e of tokens 4c .. 4c+3: byte e of each token's word w
+      const unsigned ab_lo = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05010400u);
+      const unsigned ab_hi = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07030602u);
+      const unsigned cd_lo = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05010400u);
+      const unsigned cd_hi = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07030602u);
+      const unsigned tcol[4] = {__builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),
+                                __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),
+                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),
+                                __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tcol[e], 1.0f, true);
+        vb[4 * w + e] = half4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  } else {
+    u32x4 vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vv[i] = (!kMasked || 4 * c + i < nvalid) ? vr[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int w = u / 2;
+      const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+      const unsigned d01 = __builtin_amdgcn_perm(vv[1][w], vv[0][w], sel);
+      const unsigned d23 = __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel);
+      vb[u] = __builtin_bit_cast(half4_t, u32x2{d01, d23});
+    }
   }
 }
 
@@ -307,17 +339,18 @@ __device__ __forceinline__ void mq_v_operands(const u32x4 (&vr)[4], int c, int n
 // before min(base + qi, n_seq, tok_hi) when causal, before tok_hi otherwise;
 // rows past the tile's queries see everything and are never stored.  Tokens at
 // or past t0 + nvalid are exact zeros.
-template <int G, int NT, bool kMasked>
+template <int G, int NT, bool kMasked, bool kFp8>
 __device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4],
-                                        const u32x4 (&kr)[4], const u32x4 (&vr)[4],
+                                        const u32x4 (&kr)[KvFmt<kFp8>::kKLoads],
+                                        const typename KvFmt<kFp8>::VRow (&vr)[4],
                                         float qk_scale, int lane, int row0, int t0, int nvalid,
                                         int causal_base, int n_seq, int nq, int tok_hi) {
   const int n = lane & 15;
   const int c = lane >> 4;
   half8_t kop[4];
-  k_operands<false>(kr, kop);
+  k_operands<kFp8>(kr, kop);
   half4_t vb[8];
-  mq_v_operands<kMasked>(vr, c, nvalid, vb);
+  mq_v_operands<kMasked, kFp8>(vr, c, nvalid, vb);
 #pragma unroll
   for (int b = 0; b < NT; ++b) {
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -376,7 +409,7 @@ __device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4
 // Q as the MFMA A operands of rows row0 .. row0 + 16 NT - 1 of a tile: row m
 // is query m / G, head g*G + m % G; rows past the tile's queries load its last
 // query and are zeroed.
-template <int G, int NT>
+template <int G, int NT, bool kFp8>
 __device__ __forceinline__ void mq_load_q(const MqParams& p, int g, int q0, int nq, int row0,
                                           int lane, half8_t (&qa)[NT][4]) {
   const int c = lane >> 4, t = lane & 15;
@@ -388,7 +421,7 @@ __device__ __forceinline__ void mq_load_q(const MqParams& p, int g, int q0, int 
     const _Float16* qrow = p.q + ((long long)row * p.Hq + (long long)g * G + j) * kD;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KvFmt<false>::q_dim(ii, c)) ^ p.q_sign;
+      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KvFmt<kFp8>::q_dim(ii, c)) ^ p.q_sign;
       if (qi >= nq) x = u32x4{0u, 0u, 0u, 0u};
       qa[b][ii] = __builtin_bit_cast(half8_t, x);
     }
@@ -398,7 +431,7 @@ __device__ __forceinline__ void mq_load_q(const MqParams& p, int g, int q0, int 
 // Normalise and store rows row0 .. of the wave: lane (c, n) holds rows
 // row0 + 16b + 4c + r, dims 8n .. 8n+7.  A whole tile writes the output; a
 // segment of a cut tile writes its partial to slot `slot`.
-template <int G, int NT, int Qt>
+template <int G, int NT, int Qt, bool kFp8>
 __device__ __forceinline__ void mq_store(const MqParams& p, MqSeg<NT>& st, int g, int q0, int nq,
                                          int row0, int lane, bool whole, int slot) {
   const int c = lane >> 4, t = lane & 15;
@@ -421,7 +454,8 @@ __device__ __forceinline__ void mq_store(const MqParams& p, MqSeg<NT>& st, int g
       const int row = row0 + 16 * b + 4 * c + r;
       const int qi = row / G, j = row % G;
       if (qi >= nq) continue;
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      if constexpr (kFp8) inv *= p.v_scale;
       const float lse = l > 0.0f ? (mr[r] + __builtin_log2f(l)) * kLn2 : -INFINITY;
       float o[8];
 #pragma unroll
@@ -476,22 +510,26 @@ struct BlockWindow {
 // ---------------------------------------------------------------------------
 // register kernel: one wave per KV head, one 16-row tile per wave
 
-template <int G, int NT>
-__device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
+template <int G, int NT, bool kFp8>
+__device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
                                bool whole, int slot) {
+  using Fmt = KvFmt<kFp8>;
+  using VRow = typename Fmt::VRow;
+  constexpr int E = Fmt::kElemBytes;
+  constexpr int KL = Fmt::kKLoads;
   constexpr int Qt = 16 * NT / G;
   const int c = lane >> 4, t = lane & 15;
   const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
   const int n = mq_seq_len(p, s);
   half8_t qa[NT][4];
-  mq_load_q<G, NT>(p, g, q0, nq, 0, lane, qa);
+  mq_load_q<G, NT, kFp8>(p, g, q0, nq, 0, lane, qa);
   // blocks wholly before the tile's first query's end skip the mask
   const int causal_base = p.causal ? base : kNoMask;
   const int full_end = p.causal ? min(min(max(base, 0), n), tok_hi) : tok_hi;
 
-  const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
-  const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * 2 + 16 * c);
-  const unsigned v_lane = (unsigned)((4 * c * p.Hkv + g) * kD * 2 + 16 * t);   // tokens 4c + i
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);
+  const unsigned k_lane = (unsigned)((t * p.Hkv + g) * kD * E + 16 * c);
+  const unsigned v_lane = (unsigned)((4 * c * p.Hkv + g) * kD * E + 8 * E * t);   // tokens 4c + i
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
@@ -500,16 +538,17 @@ __device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int to
 
   MqSeg<NT> st;
   mq_seg_init(st);
-  auto load = [&](long long off, u32x4 (&kr)[4], u32x4 (&vr)[4]) {
+  auto load = [&](long long off, u32x4 (&kr)[KL], VRow (&vr)[4]) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < KL; ++ii)
       kr[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + k_lane + 64 * ii);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-      vr[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + v_lane + ii * row_bytes);
+      vr[ii] = *reinterpret_cast<const VRow*>(vbytes + off + v_lane + ii * row_bytes);
   };
   constexpr int NB = kRegRing;
-  u32x4 kbuf[NB][4], vbuf[NB][4];
+  u32x4 kbuf[NB][KL];
+  VRow vbuf[NB][4];
 #pragma unroll
   for (int ii = 0; ii < NB - 1; ++ii)
     if (ii < nblk) load(win.offset(ii), kbuf[ii], vbuf[ii]);
@@ -522,17 +561,17 @@ __device__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int to
       if (nxt < nblk) load(win.offset(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
       const int t0 = tok_lo + cur * kBS;
       if (t0 + kBS > full_end)
-        mq_fold<G, NT, true>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, tok_hi - t0,
-                             causal_base, n, nq, tok_hi);
+        mq_fold<G, NT, true, kFp8>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0,
+                                   tok_hi - t0, causal_base, n, nq, tok_hi);
       else
-        mq_fold<G, NT, false>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
-                              causal_base, n, nq, tok_hi);
+        mq_fold<G, NT, false, kFp8>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
+                                    causal_base, n, nq, tok_hi);
     }
   }
-  mq_store<G, NT, Qt>(p, st, g, q0, nq, 0, lane, whole, slot);
+  mq_store<G, NT, Qt, kFp8>(p, st, g, q0, nq, 0, lane, whole, slot);
 }
 
-template <int G, int NT>
+template <int G, int NT, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_reg_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -541,35 +580,41 @@ void mq_reg_kernel(MqParams p) {
   const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
   const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_reg_segment<G, NT>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
+    mq_reg_segment<G, NT, kFp8>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
 // ---------------------------------------------------------------------------
 // shared kernel: 4 waves per KV head share each K/V block through LDS
 
-template <int G, int NT>
-__device__ void mq_shared_segment(const MqParams& p, char* kv, int lane, int wave, int g, int i,
+template <int G, int NT, bool kFp8>
+__device__ __forceinline__ void mq_shared_segment(const MqParams& p, char* kv, int lane, int wave, int g, int i,
                                   int tok_lo, int tok_hi, bool whole, int slot) {
+  using Fmt = KvFmt<kFp8>;
+  using VRow = typename Fmt::VRow;
+  using Chunk = VRow;                               // 8 elements: 16 bytes fp16, 8 bytes FP8
+  constexpr int E = Fmt::kElemBytes;
+  constexpr int KL = Fmt::kKLoads;
+  constexpr int kRow = lds_row<kFp8>();
   constexpr int Qt = 64 * NT / G;
-  constexpr int kStage = 2 * kBS * kLdsRow;        // K rows then V rows of one block
+  constexpr int kStage = 2 * kBS * kRow;            // K rows then V rows of one block
   const int c = lane >> 4, t = lane & 15;
   const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
   const int n = mq_seq_len(p, s);
   const int row0 = wave * 16 * NT;                  // this wave's first row of the tile
   const bool idle = row0 / G >= nq;                 // none of the tile's queries (uniform)
   half8_t qa[NT][4];
-  mq_load_q<G, NT>(p, g, q0, nq, row0, lane, qa);
+  mq_load_q<G, NT, kFp8>(p, g, q0, nq, row0, lane, qa);
   const int causal_base = p.causal ? base : kNoMask;
   const int full_end = p.causal ? min(min(max(base + row0 / G, 0), n), tok_hi) : tok_hi;
 
-  // thread (wave, lane) moves 16 bytes of K and of V of each block: token
-  // tid / 16, bytes 16 * (tid % 16) of the 256-byte row of KV head g
+  // thread (wave, lane) moves 8 elements of K and of V of each block: token
+  // tid / 16, elements 8 * (tid % 16) of the row of KV head g
   const int tid = wave * kWave + lane;
   const int ltok = tid >> 4, lchunk = tid & 15;
-  const unsigned row_bytes = (unsigned)(p.Hkv * kD * 2);
-  const unsigned g_off = (unsigned)((ltok * p.Hkv + g) * kD * 2 + 16 * lchunk);
-  const int s_off = ltok * kLdsRow + 16 * lchunk;
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);
+  const unsigned g_off = (unsigned)((ltok * p.Hkv + g) * kD * E + 8 * E * lchunk);
+  const int s_off = ltok * kRow + 8 * E * lchunk;
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
@@ -579,13 +624,13 @@ __device__ void mq_shared_segment(const MqParams& p, char* kv, int lane, int wav
   MqSeg<NT> st;
   mq_seg_init(st);
   constexpr int NB = kShPrefetch;                  // even: stage = block parity = slot parity
-  u32x4 pk[NB], pv[NB];
+  Chunk pk[NB], pv[NB];
 #pragma unroll
   for (int ii = 0; ii < NB - 1; ++ii)
     if (ii < nblk) {
       const long long off = win.offset(ii);
-      pk[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + g_off);
-      pv[ii] = *reinterpret_cast<const u32x4*>(vbytes + off + g_off);
+      pk[ii] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
+      pv[ii] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
     }
   for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
 #pragma unroll
@@ -595,48 +640,49 @@ __device__ void mq_shared_segment(const MqParams& p, char* kv, int lane, int wav
       const int nxt = cur + NB - 1;
       if (nxt < nblk) {
         const long long off = win.offset(nxt);
-        pk[(sl + NB - 1) % NB] = *reinterpret_cast<const u32x4*>(kbytes + off + g_off);
-        pv[(sl + NB - 1) % NB] = *reinterpret_cast<const u32x4*>(vbytes + off + g_off);
+        pk[(sl + NB - 1) % NB] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
+        pv[(sl + NB - 1) % NB] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
       }
       // stage block cur; every wave finished the block that last used this
       // stage before the previous barrier
       char* stage = kv + (sl & 1) * kStage;
-      *reinterpret_cast<u32x4*>(stage + s_off) = pk[sl];
-      *reinterpret_cast<u32x4*>(stage + kBS * kLdsRow + s_off) = pv[sl];
+      *reinterpret_cast<Chunk*>(stage + s_off) = pk[sl];
+      *reinterpret_cast<Chunk*>(stage + kBS * kRow + s_off) = pv[sl];
       __syncthreads();
       if (!idle) {
-        u32x4 kr[4], vr[4];
+        u32x4 kr[KL];
+        VRow vr[4];
+#pragma unroll
+        for (int ii = 0; ii < KL; ++ii)
+          kr[ii] = *reinterpret_cast<const u32x4*>(stage + t * kRow + 16 * c + 64 * ii);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          kr[ii] = *reinterpret_cast<const u32x4*>(stage + t * kLdsRow + 16 * c + 64 * ii);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          vr[ii] = *reinterpret_cast<const u32x4*>(stage + kBS * kLdsRow +
-                                                   (4 * c + ii) * kLdsRow + 16 * t);
+          vr[ii] = *reinterpret_cast<const VRow*>(stage + kBS * kRow + (4 * c + ii) * kRow +
+                                                  8 * E * t);
         const int t0 = tok_lo + cur * kBS;
         if (t0 + kBS > full_end)
-          mq_fold<G, NT, true>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, tok_hi - t0,
-                               causal_base, n, nq, tok_hi);
+          mq_fold<G, NT, true, kFp8>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, tok_hi - t0,
+                                     causal_base, n, nq, tok_hi);
         else
-          mq_fold<G, NT, false>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, kBS, causal_base, n,
-                                nq, tok_hi);
+          mq_fold<G, NT, false, kFp8>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, kBS,
+                                      causal_base, n, nq, tok_hi);
       }
     }
   }
   __syncthreads();                                  // the stages are free for the next segment
-  if (!idle) mq_store<G, NT, Qt>(p, st, g, q0, nq, row0, lane, whole, slot);
+  if (!idle) mq_store<G, NT, Qt, kFp8>(p, st, g, q0, nq, row0, lane, whole, slot);
 }
 
-template <int G, int NT>
+template <int G, int NT, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_shared_kernel(MqParams p) {
-  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kBS * kLdsRow];   // 2 stages of K, V
+  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kBS * lds_row<kFp8>()];   // 2 stages: K, V
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
   const int g = blockIdx.x % p.Hkv;                 // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_shared_segment<G, NT>(p, kv, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+    mq_shared_segment<G, NT, kFp8>(p, kv, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
@@ -691,29 +737,34 @@ constexpr int kMqVariants = 4;
 struct MqDeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMqVariants][kMqWaves + 1] = {};   // [log2 G][variant][waves per group]
+  int wg_per_cu[4][kMqVariants][2][kMqWaves + 1] = {};   // [log2 G][variant][fp8][waves]
 };
 MqDeviceFacts g_mq_dev[kMaxDevices];
 
 int mq_log2(int x) { return x == 1 ? 0 : x == 2 ? 1 : x == 4 ? 2 : 3; }
 
-template <int G>
+template <int G, bool kFp8>
 const void* mq_kernel_ptr_g(int variant) {
   switch (variant) {
-    case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 1>);
-    case 1: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 2>);
-    case 2: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1>);
-    default: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 2>);
+    case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 1, kFp8>);
+    case 1: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 2, kFp8>);
+    case 2: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1, kFp8>);
+    default: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 2, kFp8>);
   }
 }
 
-const void* mq_kernel_ptr(int G, int variant) {
+template <bool kFp8>
+const void* mq_kernel_ptr_f(int G, int variant) {
   switch (G) {
-    case 1: return mq_kernel_ptr_g<1>(variant);
-    case 2: return mq_kernel_ptr_g<2>(variant);
-    case 4: return mq_kernel_ptr_g<4>(variant);
-    default: return mq_kernel_ptr_g<8>(variant);
+    case 1: return mq_kernel_ptr_g<1, kFp8>(variant);
+    case 2: return mq_kernel_ptr_g<2, kFp8>(variant);
+    case 4: return mq_kernel_ptr_g<4, kFp8>(variant);
+    default: return mq_kernel_ptr_g<8, kFp8>(variant);
   }
+}
+
+const void* mq_kernel_ptr(int G, int variant, bool fp8) {
+  return fp8 ? mq_kernel_ptr_f<true>(G, variant) : mq_kernel_ptr_f<false>(G, variant);
 }
 
 int mq_head_group(int Hkv) {
@@ -747,7 +798,7 @@ bool mq_is_shared(int variant) { return variant >= 2; }
 
 // Runs of the unit stream: as many work-groups as fit on all CUs at once,
 // divided by the work-groups one run has (its head groups, or its KV heads).
-int mq_run_count(int G, int variant, int Hkv) {
+int mq_run_count(int G, int variant, int Hkv, bool fp8) {
   const int waves = mq_is_shared(variant) ? kMqWaves : mq_head_group(Hkv);
   const int per_run = mq_is_shared(variant) ? Hkv : Hkv / mq_head_group(Hkv);
   int dev = 0;
@@ -761,16 +812,17 @@ int mq_run_count(int G, int variant, int Hkv) {
     f.cus = cus;
     for (int lg = 0; lg < 4; ++lg)
       for (int v = 0; v < kMqVariants; ++v)
-        for (int w = 1; w <= kMqWaves; ++w) {
-          int n = 0;
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mq_kernel_ptr(1 << lg, v),
-                                                           w * kWave, 0) != hipSuccess ||
-              n <= 0)
-            n = 1;
-          f.wg_per_cu[lg][v][w] = n;
-        }
+        for (int f8 = 0; f8 < 2; ++f8)
+          for (int w = 1; w <= kMqWaves; ++w) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &n, mq_kernel_ptr(1 << lg, v, f8 != 0), w * kWave, 0) != hipSuccess ||
+                n <= 0)
+              n = 1;
+            f.wg_per_cu[lg][v][f8][w] = n;
+          }
   });
-  return std::max(1, f.cus * f.wg_per_cu[mq_log2(G)][variant][waves] / per_run);
+  return std::max(1, f.cus * f.wg_per_cu[mq_log2(G)][variant][fp8 ? 1 : 0][waves] / per_run);
 }
 
 struct MqPlan {
@@ -807,13 +859,14 @@ int mq_check(int S, int T, int Hq, int Hkv, int D, int block_size, int max_block
   return PDA_OK;
 }
 
-MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition_tokens) {
+MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition_tokens,
+                    bool fp8) {
   MqPlan pl;
   const int G = Hq / Hkv;
   pl.variant = mq_variant(S, T, G);
   pl.Qt = mq_tile_queries(pl.variant, G);
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_runs = mq_run_count(G, pl.variant, Hkv);
+  pl.n_runs = mq_run_count(G, pl.variant, Hkv, fp8);
   pl.hg = mq_head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
   pl.tiles_max = (T + pl.Qt - 1) / pl.Qt + S;
@@ -841,27 +894,38 @@ void mq_launch_aux(bool plan, const MqParams& mp, const MqPlan& pl, hipStream_t 
                      dim3(256), 0, stream, mp);
 }
 
-template <int G, int V>
+template <int G, int V, bool kFp8>
 void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   constexpr int Qt = (16 << V) / G;
   mq_launch_aux<Qt>(true, mp, pl, stream);
   if constexpr (V >= 2) {
-    hipLaunchKernelGGL((mq_shared_kernel<G, V - 1>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+    hipLaunchKernelGGL((mq_shared_kernel<G, V - 1, kFp8>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
                        dim3(kMqWaves * kWave), 0, stream, mp);
   } else {
-    hipLaunchKernelGGL((mq_reg_kernel<G, V + 1>), dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
+    hipLaunchKernelGGL((mq_reg_kernel<G, V + 1, kFp8>),
+                       dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
                        dim3((unsigned)(pl.hg * kWave)), 0, stream, mp);
   }
   mq_launch_aux<Qt>(false, mp, pl, stream);
 }
 
-template <int G>
+template <int G, bool kFp8>
 void mq_launch(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   switch (pl.variant) {
-    case 0: mq_launch_v<G, 0>(mp, pl, stream); break;
-    case 1: mq_launch_v<G, 1>(mp, pl, stream); break;
-    case 2: mq_launch_v<G, 2>(mp, pl, stream); break;
-    default: mq_launch_v<G, 3>(mp, pl, stream); break;
+    case 0: mq_launch_v<G, 0, kFp8>(mp, pl, stream); break;
+    case 1: mq_launch_v<G, 1, kFp8>(mp, pl, stream); break;
+    case 2: mq_launch_v<G, 2, kFp8>(mp, pl, stream); break;
+    default: mq_launch_v<G, 3, kFp8>(mp, pl, stream); break;
+  }
+}
+
+template <bool kFp8>
+void mq_launch_f(int G, const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
+  switch (G) {
+    case 1: mq_launch<1, kFp8>(mp, pl, stream); break;
+    case 2: mq_launch<2, kFp8>(mp, pl, stream); break;
+    case 4: mq_launch<4, kFp8>(mp, pl, stream); break;
+    default: mq_launch<8, kFp8>(mp, pl, stream); break;
   }
 }
 
@@ -869,8 +933,9 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
                     const int32_t* query_start, int T, const void* k_cache, const void* v_cache,
                     const int32_t* bt, int64_t bt_stride, const int32_t* ctx, int S, int Hq,
                     int Hkv, int D, int block_size, int64_t num_blocks, int max_blocks,
-                    float scale, int causal, int partition_tokens, void* workspace,
-                    size_t workspace_bytes, void* stream_ptr) {
+                    float scale, bool fp8, float k_scale, float v_scale, int causal,
+                    int partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream_ptr) {
   int rc = mq_check(S, T, Hq, Hkv, D, block_size, max_blocks, partition_tokens);
   if (rc != PDA_OK) return rc;
   if (S == 0 || T == 0) return ok();
@@ -880,9 +945,10 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
     return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
                 (long long)bt_stride, max_blocks);
   if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
-  if (!finite_f32(scale)) return fail(PDA_EINVAL, "scale must be finite");
+  if (!finite_f32(scale) || !finite_f32(k_scale) || !finite_f32(v_scale))
+    return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
-  const MqPlan pl = mq_make_plan(S, T, Hq, Hkv, max_blocks, partition_tokens);
+  const MqPlan pl = mq_make_plan(S, T, Hq, Hkv, max_blocks, partition_tokens, fp8);
   if (workspace_bytes < pl.total)
     return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
                 pl.total);
@@ -894,8 +960,8 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
   MqParams mp;
   mp.q = static_cast<const _Float16*>(q);
   mp.qs = query_start;
-  mp.k = static_cast<const _Float16*>(k_cache);
-  mp.v = static_cast<const _Float16*>(v_cache);
+  mp.k = k_cache;
+  mp.v = v_cache;
   mp.bt = bt;
   mp.ctx = ctx;
   mp.bt_stride = bt_stride;
@@ -909,8 +975,10 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
   mp.n_runs = pl.n_runs;
   mp.hg = pl.hg;
   mp.causal = causal ? 1 : 0;
-  mp.qk_scale = std::fabs(scale) * kLog2e;
-  mp.q_sign = std::signbit(scale) ? 0x80008000u : 0u;
+  const float score_scale = scale * k_scale;      // k = k_scale * decoded code for FP8
+  mp.qk_scale = std::fabs(score_scale) * kLog2e;
+  mp.q_sign = std::signbit(score_scale) ? 0x80008000u : 0u;
+  mp.v_scale = v_scale;
   mp.hdr = reinterpret_cast<int32_t*>(ws + pl.hdr_offset);
   mp.t_seq = tiles;
   mp.t_q0 = tiles + 1 * (size_t)pl.tiles_max;
@@ -926,12 +994,10 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
   mp.lse_out = lse_out;
   mp.out_f16 = out_f16 ? 1 : 0;
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  switch (Hq / Hkv) {
-    case 1: mq_launch<1>(mp, pl, stream); break;
-    case 2: mq_launch<2>(mp, pl, stream); break;
-    case 4: mq_launch<4>(mp, pl, stream); break;
-    default: mq_launch<8>(mp, pl, stream); break;
-  }
+  if (fp8)
+    mq_launch_f<true>(Hq / Hkv, mp, pl, stream);
+  else
+    mq_launch_f<false>(Hq / Hkv, mp, pl, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PDA_EHIP, "multi-query launch: %s", hipGetErrorString(e));
   return ok();
@@ -948,7 +1014,10 @@ int pda_multi_query_workspace_size(int S, int num_queries, int Hq, int Hkv, int 
   if (rc != PDA_OK) return rc;
   *bytes = (S == 0 || num_queries == 0)
                ? 0
-               : mq_make_plan(S, num_queries, Hq, Hkv, max_blocks_per_seq, partition_tokens).total;
+               : std::max(mq_make_plan(S, num_queries, Hq, Hkv, max_blocks_per_seq,
+                                       partition_tokens, false).total,
+                          mq_make_plan(S, num_queries, Hq, Hkv, max_blocks_per_seq,
+                                       partition_tokens, true).total);
   return ok();
 }
 
@@ -961,8 +1030,8 @@ int paged_multi_query_attn(void* out, float* lse_out, const void* q, const int32
                            size_t workspace_bytes, void* stream) {
   return run_multi_query(true, out, lse_out, q, query_start, num_queries, k_cache, v_cache,
                          block_table, block_table_stride, context_lens, S, Hq, Hkv, D, block_size,
-                         num_blocks, max_blocks_per_seq, scale, causal, partition_tokens,
-                         workspace, workspace_bytes, stream);
+                         num_blocks, max_blocks_per_seq, scale, false, 1.0f, 1.0f, causal,
+                         partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int paged_multi_query_attn_partial(float* o, float* lse, const void* q,
@@ -976,8 +1045,38 @@ int paged_multi_query_attn_partial(float* o, float* lse, const void* q,
   if (S > 0 && num_queries > 0 && !lse) return fail(PDA_EINVAL, "lse is null");
   return run_multi_query(false, o, lse, q, query_start, num_queries, k_cache, v_cache,
                          block_table, block_table_stride, context_lens, S, Hq, Hkv, D, block_size,
-                         num_blocks, max_blocks_per_seq, scale, causal, partition_tokens,
-                         workspace, workspace_bytes, stream);
+                         num_blocks, max_blocks_per_seq, scale, false, 1.0f, 1.0f, causal,
+                         partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int paged_multi_query_attn_fp8(void* out, float* lse_out, const void* q,
+                               const int32_t* query_start, int num_queries, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               int64_t block_table_stride, const int32_t* context_lens, int S,
+                               int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
+                               int max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                               int causal, int partition_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return run_multi_query(true, out, lse_out, q, query_start, num_queries, k_cache, v_cache,
+                         block_table, block_table_stride, context_lens, S, Hq, Hkv, D, block_size,
+                         num_blocks, max_blocks_per_seq, scale, true, k_scale, v_scale, causal,
+                         partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int paged_multi_query_attn_partial_fp8(float* o, float* lse, const void* q,
+                                       const int32_t* query_start, int num_queries,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, int64_t block_table_stride,
+                                       const int32_t* context_lens, int S, int Hq, int Hkv, int D,
+                                       int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                                       float scale, float k_scale, float v_scale, int causal,
+                                       int partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (S > 0 && num_queries > 0 && !lse) return fail(PDA_EINVAL, "lse is null");
+  return run_multi_query(false, o, lse, q, query_start, num_queries, k_cache, v_cache,
+                         block_table, block_table_stride, context_lens, S, Hq, Hkv, D, block_size,
+                         num_blocks, max_blocks_per_seq, scale, true, k_scale, v_scale, causal,
+                         partition_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

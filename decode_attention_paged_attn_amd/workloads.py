@@ -367,6 +367,13 @@ class MqCase:
     block_table_host: np.ndarray
     causal: bool
     seed: int
+    kv_dtype: str = "fp16"       # "fp16", or "fp8": E4M3 codes (uint8) with per-tensor scales
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    def attn_kwargs(self):
+        """The scale arguments the attention calls need for this cache."""
+        return {"k_scale": self.k_scale, "v_scale": self.v_scale} if self.kv_dtype == "fp8" else {}
 
     @property
     def S(self):
@@ -394,10 +401,11 @@ def _queries(T, Hq, D, seed, device):
 
 
 def build_mq_case(lens, n_queries, Hq, Hkv, *, causal=True, seed=0, device="cpu",
-                  rng_backend="numpy", name="mq_custom", pool_blocks=None) -> MqCase:
+                  rng_backend="numpy", name="mq_custom", pool_blocks=None,
+                  kv_dtype="fp16") -> MqCase:
     """Pool and tables as build_case draws them, then sum(n_queries) query rows."""
     base = build_case(lens, Hq, Hkv, seed=seed, device=device, rng_backend=rng_backend,
-                      name=name, pool_blocks=pool_blocks)
+                      name=name, pool_blocks=pool_blocks, kv_dtype=kv_dtype)
     n_queries = np.asarray(n_queries, dtype=np.int64)
     qs = np.concatenate([[0], np.cumsum(n_queries)]).astype(np.int32)
     q = _queries(int(qs[-1]), Hq, base.D, seed, device)
@@ -405,10 +413,11 @@ def build_mq_case(lens, n_queries, Hq, Hkv, *, causal=True, seed=0, device="cpu"
                   block_table=base.block_table, context_lens=base.context_lens,
                   query_start=torch.from_numpy(qs).to(device), scale=base.scale,
                   lens=base.lens, n_queries=n_queries, block_table_host=base.block_table_host,
-                  causal=causal, seed=seed)
+                  causal=causal, seed=seed, kv_dtype=kv_dtype, k_scale=base.k_scale,
+                  v_scale=base.v_scale)
 
 
-def spec_verify(seed=0, device="cpu", rng_backend="torch"):
+def spec_verify(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Speculative verification: 32 sequences of 4096 tokens, 6 query tokens each.
 
     The 5 proposed tokens of a draft model (5 to 6 in the speculative-decoding
@@ -416,10 +425,11 @@ def spec_verify(seed=0, device="cpu", rng_backend="torch"):
     checked causally in one pass; batches above ~32 requests gain little there.
     """
     return build_mq_case([4096] * 32, [6] * 32, 32, 8, causal=True, seed=seed, device=device,
-                         rng_backend=rng_backend, name="spec_verify_b32_ctx4096_q6")
+                         rng_backend=rng_backend, kv_dtype=kv_dtype,
+                         name="spec_verify_b32_ctx4096_q6" + _suffix(kv_dtype))
 
 
-def chunked_prefill(seed=0, device="cpu", rng_backend="torch"):
+def chunked_prefill(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Chunked prefill: 4 prompts, each at a 1024-token chunk (chunks 1, 3, 7, 15).
 
     The chunk attends to the earlier chunks unmasked and to itself causally
@@ -429,7 +439,8 @@ def chunked_prefill(seed=0, device="cpu", rng_backend="torch"):
     chunks = [1, 3, 7, 15]
     lens = [(c + 1) * K1 for c in chunks]
     return build_mq_case(lens, [K1] * 4, 32, 8, causal=True, seed=seed, device=device,
-                         rng_backend=rng_backend, name="prefill_s4_chunk1024_at_1_3_7_15")
+                         rng_backend=rng_backend, kv_dtype=kv_dtype,
+                         name="prefill_s4_chunk1024_at_1_3_7_15" + _suffix(kv_dtype))
 
 
 @dataclasses.dataclass
@@ -451,6 +462,13 @@ class CascadeCase:
     prefix_table_host: np.ndarray
     suffix_table_host: np.ndarray
     seed: int
+    kv_dtype: str = "fp16"
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    def attn_kwargs(self):
+        """The scale arguments the attention calls need for this cache."""
+        return {"k_scale": self.k_scale, "v_scale": self.v_scale} if self.kv_dtype == "fp8" else {}
 
     @property
     def B(self):
@@ -486,13 +504,14 @@ class CascadeCase:
 
 
 def build_cascade_case(prefix_lens, group_sizes, suffix_lens, Hq, Hkv, *, seed=0, device="cpu",
-                       rng_backend="numpy", name="cascade_custom") -> CascadeCase:
+                       rng_backend="numpy", name="cascade_custom",
+                       kv_dtype="fp16") -> CascadeCase:
     """One pool dealt to R prefix rows then B suffix rows, then B query rows."""
     prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
     suffix_lens = np.asarray(suffix_lens, dtype=np.int64)
     R = len(prefix_lens)
     base = build_case(np.concatenate([prefix_lens, suffix_lens]), Hq, Hkv, seed=seed,
-                      device=device, rng_backend=rng_backend, name=name)
+                      device=device, rng_backend=rng_backend, name=name, kv_dtype=kv_dtype)
     gs = np.concatenate([[0], np.cumsum(group_sizes)]).astype(np.int64)
     B = int(gs[-1])
     assert B == len(suffix_lens)
@@ -505,10 +524,11 @@ def build_cascade_case(prefix_lens, group_sizes, suffix_lens, Hq, Hkv, *, seed=0
                        prefix_lens_host=prefix_lens, group_start_host=gs,
                        suffix_lens_host=suffix_lens,
                        prefix_table_host=base.block_table_host[:R].copy(),
-                       suffix_table_host=base.block_table_host[R:].copy(), seed=seed)
+                       suffix_table_host=base.block_table_host[R:].copy(), seed=seed,
+                       kv_dtype=kv_dtype, k_scale=base.k_scale, v_scale=base.v_scale)
 
 
-def shared_prefix(seed=0, device="cpu", rng_backend="torch"):
+def shared_prefix(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
     """Cascade decode: 4 groups of 50 requests, each group sharing a 16K-token prefix.
 
     50 requests per shared prefix as in the worked example of "What
@@ -519,7 +539,8 @@ def shared_prefix(seed=0, device="cpu", rng_backend="torch"):
     rng = np.random.Generator(np.random.PCG64(seed + 7))
     suffix = rng.integers(1, K1, size=200, endpoint=True)
     return build_cascade_case([16 * K1] * 4, [50] * 4, suffix, 32, 8, seed=seed, device=device,
-                              rng_backend=rng_backend, name="cascade_g4x50_prefix16k_suffix1k")
+                              rng_backend=rng_backend, kv_dtype=kv_dtype,
+                              name="cascade_g4x50_prefix16k_suffix1k" + _suffix(kv_dtype))
 
 
 CONFIGS = {

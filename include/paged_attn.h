@@ -286,8 +286,9 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
  *              multiple of 16) by which the work is balanced over the GPU.
  * workspace    device memory of at least pda_multi_query_workspace_size()
  *              bytes, 256-byte aligned; it holds the schedule and partials.
- * Shapes as for paged_decode_attn (fp16 caches, D = 128, block_size = 16,
- * Hq / Hkv in {1, 2, 4, 8}, Hkv <= 8), and S <= 4000.
+ * Shapes as for paged_decode_attn (D = 128, block_size = 16, Hq / Hkv in
+ * {1, 2, 4, 8}, Hkv <= 8), and S <= 4000.  pda_multi_query_workspace_size
+ * covers both cache formats.
  *
  * Cascade attention for B decode requests in R groups that share a prefix
  * (requests group_start[r] .. group_start[r+1]-1 share prefix r): call
@@ -321,6 +322,33 @@ int paged_multi_query_attn_partial(float* o, float* lse, const void* q,
                                    float scale, int causal, int partition_tokens,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * The same over an FP8 (E4M3) cache: k_cache / v_cache hold one E4M3 code per
+ * element (uint8, same layout), decoded as k = k_scale * e4m3(code) and
+ * v = v_scale * e4m3(code), as for paged_decode_attn_fp8.
+ */
+int paged_multi_query_attn_fp8(void* out, float* lse_out, const void* q,
+                               const int32_t* query_start, int num_queries,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int64_t block_table_stride,
+                               const int32_t* context_lens, int S, int Hq, int Hkv,
+                               int D, int block_size, int64_t num_blocks,
+                               int max_blocks_per_seq, float scale, float k_scale,
+                               float v_scale, int causal, int partition_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+int paged_multi_query_attn_partial_fp8(float* o, float* lse, const void* q,
+                                       const int32_t* query_start, int num_queries,
+                                       const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table,
+                                       int64_t block_table_stride,
+                                       const int32_t* context_lens, int S, int Hq,
+                                       int Hkv, int D, int block_size,
+                                       int64_t num_blocks, int max_blocks_per_seq,
+                                       float scale, float k_scale, float v_scale,
+                                       int causal, int partition_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pda_last_error(void);

@@ -34,18 +34,27 @@ def _say(msg):
 
 def run_mq(case, P=0, **kw):
     _say(f"[mq] {case.name} S={case.S} T={case.T} Hq={case.Hq} Hkv={case.Hkv} "
-         f"causal={case.causal} P={P}")
+         f"causal={case.causal} P={P} kv={case.kv_dtype}")
     out, lse = pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                           case.context_lens, case.query_start, case.scale,
                                           causal=case.causal, return_lse=True,
-                                          partition_tokens=P, **kw)
+                                          partition_tokens=P, **case.attn_kwargs(), **kw)
     torch.cuda.synchronize()
     return out, lse
 
 
+def host_kv(case, k, v):
+    """Host copies of (a gather of) the pools as the values they hold: an FP8
+    pool's codes decoded by the oracle and multiplied by the tensor's scale."""
+    k, v = k.cpu().numpy(), v.cpu().numpy()
+    if case.kv_dtype == "fp8":
+        return (case.k_scale * O.fp8_e4m3_decode(k), case.v_scale * O.fp8_e4m3_decode(v))
+    return k, v
+
+
 def host_mq(case):
-    return (case.q.cpu().numpy(), case.k_cache.cpu().numpy(), case.v_cache.cpu().numpy(),
-            case.block_table_host.copy(), case.lens.copy(),
+    k, v = host_kv(case, case.k_cache, case.v_cache)
+    return (case.q.cpu().numpy(), k, v, case.block_table_host.copy(), case.lens.copy(),
             case.query_start.cpu().numpy().astype(np.int64))
 
 
@@ -183,19 +192,76 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(out, eager) and torch.equal(lse, eager_lse), f"replay {i}"
 
 
+# --- FP8 (E4M3) cache -------------------------------------------------------------
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_small_all_group_sizes(G, Hkv, causal):
+    case = W.build_mq_case(SMALL_LENS, SMALL_NQ, G * Hkv, Hkv, causal=causal, seed=140 + G,
+                           device="cuda", name=f"mq_small_fp8_G{G}", kv_dtype="fp8")
+    for P in (0, 32):
+        out, lse = run_mq(case, P)
+        ref, ref_lse = oracle_mq(case)
+        compare_out(to_np(out), ref)
+        compare_lse(to_np(lse), ref_lse)
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("variant", sorted(VARIANT_ROWS))
+def test_fp8_tile_kernel_variants(G, Hkv, variant):
+    per_seq = max(1, VARIANT_ROWS[variant] // G)
+    lens = [per_seq + 3, 700, 95, per_seq]
+    case = W.build_mq_case(lens, [per_seq] * len(lens), G * Hkv, Hkv, causal=True,
+                           seed=160 + G, device="cuda", name=f"mq_{variant}_fp8_G{G}",
+                           kv_dtype="fp8")
+    for P in (0, 48):
+        out, lse = run_mq(case, P)
+        ref, ref_lse = oracle_mq(case)
+        compare_out(to_np(out), ref)
+        compare_lse(to_np(lse), ref_lse)
+
+
+def test_fp8_partial_and_one_query_is_decode():
+    lens = [1, 2, 15, 16, 17, 100, 511, 1537]
+    case = W.build_mq_case(lens, [1] * len(lens), 32, 8, causal=True, seed=141, device="cuda",
+                           name="mq_one_query_fp8", kv_dtype="fp8")
+    out, lse = run_mq(case)
+    o, l = pda.paged_multi_query_attn_partial(case.q, case.k_cache, case.v_cache,
+                                              case.block_table, case.context_lens,
+                                              case.query_start, case.scale, causal=True,
+                                              **case.attn_kwargs())
+    dec = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                case.context_lens, case.scale, **case.attn_kwargs())
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_mq(case)
+    compare_out(to_np(out), ref)
+    compare_out(to_np(dec), ref)
+    compare_lse(to_np(lse), ref_lse)
+    _, _, v, *_ = host_mq(case)
+    compare_out(to_np(o), ref, abs_tol=p_rounding_bound(v))
+    compare_lse(to_np(l), ref_lse)
+
+
+def test_fp8_needs_scales():
+    case = W.build_mq_case([40], [2], 8, 2, seed=142, device="cuda", kv_dtype="fp8")
+    with pytest.raises(ValueError):
+        pda.paged_multi_query_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                   case.context_lens, case.query_start, case.scale)
+
+
 # --- cascade (shared prefix) ----------------------------------------------------
 
 def host_cascade(c):
-    return (c.q.cpu().numpy(), c.k_cache.cpu().numpy(), c.v_cache.cpu().numpy(),
-            c.prefix_table_host, c.prefix_lens_host, c.group_start_host, c.suffix_table_host,
-            c.suffix_lens_host)
+    k, v = host_kv(c, c.k_cache, c.v_cache)
+    return (c.q.cpu().numpy(), k, v, c.prefix_table_host, c.prefix_lens_host, c.group_start_host,
+            c.suffix_table_host, c.suffix_lens_host)
 
 
 def run_cascade(c):
-    _say(f"[cascade] {c.name} B={c.B} groups={len(c.prefix_lens_host)}")
+    _say(f"[cascade] {c.name} B={c.B} groups={len(c.prefix_lens_host)} kv={c.kv_dtype}")
     out, lse = pda.cascade_decode_attn(c.q, c.k_cache, c.v_cache, c.prefix_table, c.prefix_lens,
                                        c.group_start, c.suffix_table, c.suffix_lens, c.scale,
-                                       return_lse=True)
+                                       return_lse=True, **c.attn_kwargs())
     torch.cuda.synchronize()
     return out, lse
 
@@ -217,6 +283,17 @@ def test_cascade_groups_and_edges(G, Hkv):
     # group 2 has an empty prefix; some requests have no suffix
     c = W.build_cascade_case([64, 37, 0, 16], [3, 5, 2, 1], [5, 0, 17, 16, 1, 40, 0, 3, 9, 0, 2],
                              G * Hkv, Hkv, seed=48 + G, device="cuda", name=f"cascade_G{G}")
+    out, lse = run_cascade(c)
+    ref, ref_lse = MQ.cascade_attention(*host_cascade(c), c.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+def test_cascade_fp8(G, Hkv):
+    c = W.build_cascade_case([64, 37, 0, 16], [3, 5, 2, 1], [5, 0, 17, 16, 1, 40, 0, 3, 9, 0, 2],
+                             G * Hkv, Hkv, seed=148 + G, device="cuda",
+                             name=f"cascade_fp8_G{G}", kv_dtype="fp8")
     out, lse = run_cascade(c)
     ref, ref_lse = MQ.cascade_attention(*host_cascade(c), c.scale)
     compare_out(to_np(out), ref)
@@ -250,8 +327,8 @@ def sampled_mq_oracle(case, picks):
         nb = -(-vis // 16)
         idx = torch.tensor([int(x) for x in case.block_table_host[s, :nb]], dtype=torch.int64,
                            device=case.k_cache.device)
-        kp = case.k_cache.index_select(0, idx).cpu().numpy()
-        vp = case.v_cache.index_select(0, idx).cpu().numpy()
+        kp, vp = host_kv(case, case.k_cache.index_select(0, idx),
+                         case.v_cache.index_select(0, idx))
         qrow = case.q[int(qs[s]) + i].cpu().numpy()
         o = np.zeros((Hq, 128))
         l = np.zeros(Hq)
@@ -264,9 +341,10 @@ def sampled_mq_oracle(case, picks):
     return res
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
 @pytest.mark.parametrize("config", ["spec_verify", "chunked_prefill"])
-def test_full_size_sampled(config):
-    case = W.MQ_CONFIGS[config](device="cuda")
+def test_full_size_sampled(config, kv_dtype):
+    case = W.MQ_CONFIGS[config](device="cuda", kv_dtype=kv_dtype)
     out, lse = run_mq(case)
     rng = np.random.default_rng(51)
     picks = []
@@ -285,8 +363,9 @@ def test_full_size_sampled(config):
     torch.cuda.empty_cache()
 
 
-def test_full_size_cascade_sampled():
-    c = W.shared_prefix(device="cuda")
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+def test_full_size_cascade_sampled(kv_dtype):
+    c = W.shared_prefix(device="cuda", kv_dtype=kv_dtype)
     out, lse = run_cascade(c)
     o, l = to_np(out), to_np(lse)
     assert np.all(np.isfinite(o))
@@ -298,8 +377,7 @@ def test_full_size_cascade_sampled():
         frames = (list(c.prefix_table_host[r, :-(-pl // 16)]) +
                   list(c.suffix_table_host[b, :-(-sl // 16)]))
         idx = torch.tensor([int(x) for x in frames], dtype=torch.int64, device="cuda")
-        kp = c.k_cache.index_select(0, idx).cpu().numpy()
-        vp = c.v_cache.index_select(0, idx).cpu().numpy()
+        kp, vp = host_kv(c, c.k_cache.index_select(0, idx), c.v_cache.index_select(0, idx))
         npb = -(-pl // 16)
         ref, ref_l = MQ.cascade_attention(
             c.q[b:b + 1].cpu().numpy(), kp, vp, np.arange(npb)[None], [pl], [0, 1],
