@@ -27,22 +27,21 @@
 // the merge kernel combines by log-sum-exp, one wave per row.  Tiles that see
 // no token are written as 0 with lse -inf by the merge kernel.
 //
-// Two tile kernels, picked by the average query rows per sequence:
-//   * register kernel (up to 16 rows): one work-group per (run, group of up to
-//     4 KV heads), one wave per KV head, a 16-row tile per wave; each wave
-//     streams its own K/V through a ring of register buffers, as the decode
-//     kernel does;
-//   * shared kernel (more rows): one work-group of 4 waves per (run, KV head)
-//     and a tile of 64 * NT rows, 16 * NT per wave; the 256 threads load each
+// Three tile kernels, picked by the average query rows per sequence:
+//   * register kernel (up to 32 rows): one work-group per (run, group of up to
+//     4 KV heads), one wave per KV head, a tile of one or two 16-row blocks per
+//     wave; each wave streams its own K/V through a ring of register buffers,
+//     as the decode kernel does;
+//   * shared kernel (up to 64 rows): one work-group of 4 waves per (run, KV
+//     head) and a 64-row tile, 16 rows per wave; the 256 threads load each
 //     16-token block of K and V once (16 bytes of each per thread, a few blocks
 //     ahead in registers) into a double-buffered LDS stage, and every wave
 //     folds its rows from there, so the tile's K/V is read once for all its
-//     rows.
-// Per block a wave runs the decode kernel's QK^T and p.V MFMAs; the running
-// max and sum of the softmax are per row and live in the lanes that hold the
-// row (lane group c holds rows 16b + 4c .. 16b + 4c + 3 of row block b), each
-// row has its own last visible token, and blocks every row sees in full skip
-// the mask.
+//     rows;
+//   * wide kernel (more rows): the shared kernel's staging with 128-row tiles,
+//     32 rows per wave on 32x32 MFMAs and 32 tokens per step.
+// The running max and sum of the softmax are per row, each row has its own
+// last visible token, and steps every row sees in full skip the mask.
 
 #include <hip/hip_runtime.h>
 
@@ -687,6 +686,359 @@ void mq_shared_kernel(MqParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// wide kernel: 4 waves x 32 rows per tile on v_mfma_f32_32x32x16_f16, two
+// blocks (32 tokens) per step
+//
+// On gfx950 a 32x32x16 f16 MFMA does twice the work of a 16x16x32 one and four
+// times that of a 16x16x16 one in about the same issue time (measured: 2.28,
+// 1.26 and 0.66 PFLOP/s with independent accumulators), so a tile of 32 rows x
+// 32 tokens takes 16 MFMAs here where 16-row blocks over 16-token blocks take 48.
+//   * S^T = K Q^T: A = K (32 tokens x 16 dims), B = Q^T, 8 MFMAs over D = 128.
+//     Lane l (half hf = l >> 5, n = l & 31) holds query row n at tokens
+//     8j + 4hf + i of the step (register 4j + i).  MFMA chunk kk covers head
+//     dims 64hf + 8kk .. 64hf + 8kk + 7 in both operands.
+//   * p.V: A = p (32 rows x 16 tokens), the lane's registers 8c .. 8c+7 for
+//     token chunk c, whose contraction index 8hf + t maps to token
+//     16c + 8(t >> 2) + 4hf + (t & 3); B = V at those tokens.  Output tile u
+//     holds, in register r of lane l, row 8(r >> 2) + 4hf + (r & 3) at head dim
+//     4n + u, so lane l reads V's dims 4n .. 4n+3 (8 bytes fp16, 4 FP8) of its
+//     8 tokens and builds the operand of tile u from element u of each.
+
+constexpr int kWideRows = 32;         // query rows per wave
+constexpr int kWideStep = 2 * kBS;    // tokens per step
+
+__device__ __forceinline__ int wide_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct WideSeg {
+  float m;                  // running reference max of row n (base 2), same in both halves
+  float lp;                 // running sum of p over this lane's tokens of row n
+  f32x16 acc[4];            // p.V tiles u = 0..3
+};
+
+// Q^T as the B operands of the wave's 32 rows: lane l loads row row0 + n, head
+// dims 64hf .. 64hf + 63; rows past the tile's queries are zero.
+template <int G>
+__device__ __forceinline__ void wide_load_q(const MqParams& p, int g, int q0, int nq, int row0,
+                                            int lane, half8_t (&qb)[8]) {
+  const int n = lane & 31, hf = lane >> 5;
+  const int m = row0 + n;
+  const int qi = m / G, j = m % G;
+  const int row = q0 + min(qi, nq - 1);
+  const _Float16* qrow = p.q + ((long long)row * p.Hq + (long long)g * G + j) * kD + 64 * hf;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * kk) ^ p.q_sign;
+    if (qi >= nq) x = u32x4{0u, 0u, 0u, 0u};
+    qb[kk] = __builtin_bit_cast(half8_t, x);
+  }
+}
+
+// B operands of the 4 p.V tiles for token chunk c from the step's V rows in
+// LDS (row stride kRow).  Tokens at or past `valid` (relative to the step) are
+// exact zeros, selected so that stale or poisoned rows cannot leak NaN.
+template <bool kMasked, bool kFp8>
+__device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int hf, int n,
+                                                int valid, half8_t (&vb)[4]) {
+  constexpr int kRow = lds_row<kFp8>();
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      unsigned w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * c + 8 * jj + 4 * hf + i;
+        w[i] = *reinterpret_cast<const unsigned*>(vstage + tok * kRow + 4 * n);
+        if (kMasked && tok >= valid) w[i] = 0u;                      // code 0 = +0
+      }
+      // 4x4 byte transpose: col[u] = byte u (dim 4n + u) of the 4 tokens
+      const unsigned ab_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+      const unsigned ab_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+      const unsigned cd_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+      const unsigned cd_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+      const unsigned col[4] = {__builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),
+                               __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),
+                               __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),
+                               __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(col[u], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(col[u], 1.0f, true);
+        vb[u][4 * jj + 0] = lo[0];
+        vb[u][4 * jj + 1] = lo[1];
+        vb[u][4 * jj + 2] = hi[0];
+        vb[u][4 * jj + 3] = hi[1];
+      }
+    }
+  } else {
+    u32x2 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tok = 16 * c + 8 * (t >> 2) + 4 * hf + (t & 3);
+      v[t] = *reinterpret_cast<const u32x2*>(vstage + tok * kRow + 8 * n);
+      if (kMasked && tok >= valid) v[t] = u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int comp = u >> 1;
+      const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+      u32x4 x;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[w] = __builtin_amdgcn_perm(v[2 * w + 1][comp], v[2 * w][comp], sel);
+      vb[u] = __builtin_bit_cast(half8_t, x);
+    }
+  }
+}
+
+// S^T of one step for the wave's 32 rows: the K rows of the step from LDS
+// against the query rows held as B operands.
+template <bool kFp8>
+__device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* kstage, int lane) {
+  constexpr int kRow = lds_row<kFp8>();
+  const int n = lane & 31, hf = lane >> 5;
+  f32x16 sc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+  const char* krow = kstage + n * kRow + 64 * hf * KvFmt<kFp8>::kElemBytes;
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(krow + 16 * j);
+      half8_t kop[2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[e], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[e], 1.0f, true);
+        kop[e / 2][4 * (e % 2) + 0] = lo[0];
+        kop[e / 2][4 * (e % 2) + 1] = lo[1];
+        kop[e / 2][4 * (e % 2) + 2] = hi[0];
+        kop[e / 2][4 * (e % 2) + 3] = hi[1];
+      }
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[0], qb[2 * j], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[1], qb[2 * j + 1], sc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const half8_t kop = *reinterpret_cast<const half8_t*>(krow + 16 * kk);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qb[kk], sc, 0, 0, 0);
+    }
+  }
+  return sc;
+}
+
+// The rest of a step of 32 tokens from t0 once its scores sc are known: the
+// online softmax and p.V with the step's V rows from LDS.  In a masked step
+// row row0 + n (query qi of the tile) sees tokens before min(base + qi, n_seq,
+// tok_hi) when causal, before tok_hi otherwise; rows past the tile's queries
+// see everything and are never stored.
+template <int G, bool kMasked, bool kFp8>
+__device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16& sc, const char* vstage,
+                                          float qk_scale, int lane, int row0, int t0,
+                                          int causal_base, int n_seq, int nq, int tok_hi) {
+  const int n = lane & 31, hf = lane >> 5;
+  float sv[16];
+  if (kMasked) {
+    const int qi = (row0 + n) / G;
+    int e = tok_hi;
+    if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n_seq), tok_hi);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = t0 + wide_row(r, hf) < e ? sc[r] : -INFINITY;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sc[r];
+  }
+  // lazy reference max, as in the 16-row fold: the 2 halves of a row combine
+  // only when a score exceeds the reference by more than kLazyMax
+  float xl = sv[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) xl = fmaxf(xl, sv[r]);
+  if (__ballot(xl * qk_scale > st.m + kLazyMax) != 0) {   // uniform branch
+    const float x = fmaxf(xl, __shfl_xor(xl, 32, kWave));
+    float mb = x * qk_scale;
+    if (kMasked) mb = x == -INFINITY ? -INFINITY : mb;   // a fully masked row stays -inf
+    const float mn = fmaxf(st.m, mb);
+    const float a = mn == st.m ? 1.0f : fast_exp2(st.m - mn);   // 0 on a first token
+    st.m = mn;
+    st.lp *= a;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float ar = __shfl(a, wide_row(r, hf), kWave);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st.acc[u][r] *= ar;
+    }
+  }
+  float pr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    pr[r] = fast_exp2(fmaf(sv[r], qk_scale, -st.m));
+    if (kMasked) pr[r] = sv[r] == -INFINITY ? 0.0f : pr[r];   // -inf - (-inf) would be NaN
+  }
+  float ps = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 4) ps += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+  st.lp += ps;
+  const int valid = tok_hi - t0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    half8_t pa;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) pa[t] = static_cast<_Float16>(pr[8 * c + t]);
+    half8_t vb[4];
+    wide_v_operands<kMasked, kFp8>(vstage, c, hf, n, valid, vb);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[u], st.acc[u], 0, 0, 0);
+  }
+}
+
+// Normalise and store the wave's rows: register r of lane l holds row
+// row0 + wide_row(r, hf) at head dims 4n .. 4n+3 (tiles 0..3).
+template <int G, bool kFp8>
+__device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g, int q0, int nq,
+                                           int row0, int lane, bool whole, int slot) {
+  constexpr int Qt = kMqWaves * kWideRows / G;
+  const int n = lane & 31;
+  int hf = lane >> 5;
+  // opaque: otherwise the row indices below are hoisted out of the token loop
+  // and their registers spill
+  asm volatile("" : "+v"(hf));
+  const float lrow = st.lp + __shfl_xor(st.lp, 32, kWave);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int R = wide_row(r, hf);
+    const float l = __shfl(lrow, R, kWave);
+    const float mr = __shfl(st.m, R, kWave);
+    const int row = row0 + R;
+    const int qi = row / G, j = row % G;
+    if (qi >= nq) continue;
+    float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if constexpr (kFp8) inv *= p.v_scale;
+    const float lse = l > 0.0f ? (mr + __builtin_log2f(l)) * kLn2 : -INFINITY;
+    const f32x4 o = {st.acc[0][r] * inv, st.acc[1][r] * inv, st.acc[2][r] * inv,
+                     st.acc[3][r] * inv};
+    const int h = g * G + j;
+    if (whole) {
+      const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 4 * n;
+      if (p.out_f16) {
+        const half4_t hv = {static_cast<_Float16>(o[0]), static_cast<_Float16>(o[1]),
+                            static_cast<_Float16>(o[2]), static_cast<_Float16>(o[3])};
+        *reinterpret_cast<half4_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + dst) = o;
+      }
+      if (p.lse_out && n == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse;
+    } else {
+      const long long sl = ((long long)slot * Qt + qi) * p.Hq + h;
+      *reinterpret_cast<f32x4*>(p.ws_o + sl * kD + 4 * n) = o;
+      if (n == 0) p.ws_lse[sl] = lse;
+    }
+  }
+}
+
+template <int G, bool kFp8>
+__device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int lane, int wave,
+                                                int g, int i, int tok_lo, int tok_hi, bool whole,
+                                                int slot) {
+  using Chunk = typename KvFmt<kFp8>::VRow;         // 8 elements: 16 bytes fp16, 8 bytes FP8
+  constexpr int E = KvFmt<kFp8>::kElemBytes;
+  constexpr int kRow = lds_row<kFp8>();
+  constexpr int kHalf = kWideStep * kRow;           // the K (or V) rows of one stage
+  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
+  const int n_seq = mq_seq_len(p, s);
+  const int row0 = wave * kWideRows;
+  const bool idle = row0 / G >= nq;                 // none of the tile's queries (uniform)
+  half8_t qb[8];
+  wide_load_q<G>(p, g, q0, nq, row0, lane, qb);
+  const int causal_base = p.causal ? base : kNoMask;
+  const int full_end = p.causal ? min(min(max(base + row0 / G, 0), n_seq), tok_hi) : tok_hi;
+
+  // thread (wave, lane) moves 8 elements of K and of V of each block: token
+  // tid / 16 of the block, elements 8 * (tid % 16) of the row of KV head g
+  const int tid = wave * kWave + lane;
+  const int ltok = tid >> 4, lchunk = tid & 15;
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);
+  const unsigned g_off = (unsigned)((ltok * p.Hkv + g) * kD * E + 8 * E * lchunk);
+  const int s_off = ltok * kRow + 8 * E * lchunk;
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
+  const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
+  const int nstep = (nblk + 1) / 2;
+  BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
+                  (long long)kBS * row_bytes);
+
+  WideSeg st;
+  st.m = -INFINITY;
+  st.lp = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[u][r] = 0.0f;
+
+  // Two LDS stages, one barrier per step; each thread holds the next step's
+  // K/V in registers while the step before it is folded.
+  Chunk rk[2][2], rv[2][2];
+  // blocks in increasing order (the window advances by 64 blocks)
+  auto fetch = [&](int step, Chunk (&k2)[2], Chunk (&v2)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      if (2 * step + b < nblk) {
+        const long long off = win.offset(2 * step + b);
+        k2[b] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
+        v2[b] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
+      }
+  };
+  fetch(0, rk[0], rv[0]);
+  for (int s0 = 0; s0 < nstep; s0 += 2) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int cur = s0 + sl;
+      if (cur >= nstep) break;
+      if (cur + 1 < nstep) fetch(cur + 1, rk[sl ^ 1], rv[sl ^ 1]);
+      // stage the step; every wave finished the step that last used this
+      // stage before the previous barrier.  A missing second block leaves
+      // stale rows, which lie past tok_hi: the softmax masks them and their V
+      // rows are selected to zero.
+      char* kstage = kv + sl * 2 * kHalf;
+      char* vstage = kstage + kHalf;
+      *reinterpret_cast<Chunk*>(kstage + s_off) = rk[sl][0];
+      *reinterpret_cast<Chunk*>(vstage + s_off) = rv[sl][0];
+      if (2 * cur + 1 < nblk) {
+        *reinterpret_cast<Chunk*>(kstage + kBS * kRow + s_off) = rk[sl][1];
+        *reinterpret_cast<Chunk*>(vstage + kBS * kRow + s_off) = rv[sl][1];
+      }
+      __syncthreads();
+      if (!idle) {
+        const f32x16 sc = wide_qk<kFp8>(qb, kstage, lane);
+        const int t0 = tok_lo + cur * kWideStep;
+        if (t0 + kWideStep > full_end)
+          wide_tail<G, true, kFp8>(st, sc, vstage, p.qk_scale, lane, row0, t0, causal_base, n_seq,
+                                   nq, tok_hi);
+        else
+          wide_tail<G, false, kFp8>(st, sc, vstage, p.qk_scale, lane, row0, t0, causal_base,
+                                    n_seq, nq, tok_hi);
+      }
+    }
+  }
+  __syncthreads();                                  // the stages are free for the next segment
+  if (!idle) wide_store<G, kFp8>(p, st, g, q0, nq, row0, lane, whole, slot);
+}
+
+template <int G, bool kFp8>
+__global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void mq_wide_kernel(MqParams p) {
+  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kWideStep * lds_row<kFp8>()];   // 2 stages
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
+  const int g = blockIdx.x % p.Hkv;                 // KV head
+  for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
+    mq_wide_segment<G, kFp8>(p, kv, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+  });
+}
+
+// ---------------------------------------------------------------------------
 // merge: the rows of tiles cut by run boundaries, and of tiles that see no
 // token; one wave per (listed tile, row), spread over the grid
 
@@ -732,7 +1084,7 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
 
 constexpr int kMaxDevices = 64;
 // tile kernel variants: 0, 1 = register kernel with NT = 1, 2 (16- and 32-row
-// tiles); 2, 3 = shared kernel with NT = 1, 2 (64- and 128-row tiles)
+// tiles); 2 = shared kernel (64-row tiles); 3 = wide kernel (128-row tiles)
 constexpr int kMqVariants = 4;
 struct MqDeviceFacts {
   std::once_flag once;
@@ -749,7 +1101,7 @@ const void* mq_kernel_ptr_g(int variant) {
     case 0: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 1, kFp8>);
     case 1: return reinterpret_cast<const void*>(&mq_reg_kernel<G, 2, kFp8>);
     case 2: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 1, kFp8>);
-    default: return reinterpret_cast<const void*>(&mq_shared_kernel<G, 2, kFp8>);
+    default: return reinterpret_cast<const void*>(&mq_wide_kernel<G, kFp8>);
   }
 }
 
@@ -779,13 +1131,14 @@ int mq_head_group(int Hkv) {
 
 // Tile kernel for the average query rows per sequence (query tokens x G): the
 // register kernel with one or two 16-row blocks per wave up to 16 or 32 rows
-// (no barrier per block; each wave streams its own K/V), above that the
-// shared kernel with 64 (NT = 1) or 128 (NT = 2) rows per tile, so that a
-// sequence's K/V is read by few tiles.  Measured on MI355X: a 24-row workload
-// (speculative verification) ran faster on 16-row register tiles than on one
-// shared 64-row tile (144 vs 218 us); chunked prefill (4096 rows per
-// sequence) took 1.72 ms with 128-row shared tiles, 1.84 ms with 64-row ones
-// and 3.76 ms with 16-row register tiles (before the transposed-score fold).
+// (no barrier per block; each wave streams its own K/V), the shared kernel
+// with 64-row tiles up to 64 rows, above that the wide kernel with 128-row
+// tiles, so that a sequence's K/V is read by few tiles.  Measured on MI355X: a
+// 24-row workload (speculative verification) ran faster on 16-row register
+// tiles than on one shared 64-row tile (144 vs 218 us); chunked prefill (4096
+// rows per sequence) took 1.72 ms with 128-row shared tiles, 1.84 ms with
+// 64-row ones and 3.76 ms with 16-row register tiles (before the
+// transposed-score fold), 0.80 ms on the wide kernel.
 int mq_variant(int S, int T, int G) {
   const long long rows = (long long)((T + S - 1) / std::max(S, 1)) * G;
   const int v = rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 64 ? 2 : 3;
@@ -898,8 +1251,11 @@ template <int G, int V, bool kFp8>
 void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   constexpr int Qt = (16 << V) / G;
   mq_launch_aux<Qt>(true, mp, pl, stream);
-  if constexpr (V >= 2) {
-    hipLaunchKernelGGL((mq_shared_kernel<G, V - 1, kFp8>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+  if constexpr (V == 3) {
+    hipLaunchKernelGGL((mq_wide_kernel<G, kFp8>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
+                       dim3(kMqWaves * kWave), 0, stream, mp);
+  } else if constexpr (V == 2) {
+    hipLaunchKernelGGL((mq_shared_kernel<G, 1, kFp8>), dim3((unsigned)(pl.n_runs * mp.Hkv)),
                        dim3(kMqWaves * kWave), 0, stream, mp);
   } else {
     hipLaunchKernelGGL((mq_reg_kernel<G, V + 1, kFp8>),
