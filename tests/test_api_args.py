@@ -30,7 +30,10 @@ def test_header_declares_the_api():
     names = set(declared_functions())
     assert {"paged_decode_attn", "paged_decode_attn_partial", "merge_partials",
             "pda_workspace_size", "pda_workspace_layout", "pda_last_error",
-            "pda_version"} <= names
+            "pda_version", "paged_decode_attn_fp8", "paged_decode_attn_partial_fp8",
+            "paged_kv_append", "pda_multi_query_workspace_size", "paged_multi_query_attn",
+            "paged_multi_query_attn_partial", "paged_multi_query_attn_fp8",
+            "paged_multi_query_attn_partial_fp8"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -159,3 +162,91 @@ def test_kv_append_rejects(lib):
     empty = list(args)
     empty[7] = 0
     assert lib.paged_kv_append(*empty) == 0
+
+
+# --- multi-query ------------------------------------------------------------------
+
+def _mq_ws(S=3, T=9, Hq=8, Hkv=2, D=128, bs=16, mb=32, P=0):
+    n = ctypes.c_size_t(0)
+    rc = pda.load_library().pda_multi_query_workspace_size(S, T, Hq, Hkv, D, bs, mb, P,
+                                                           ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=4001), 2),             # more sequences than the plan kernel holds
+    (dict(S=-1), 1),
+    (dict(T=-1), 1),
+    (dict(Hq=12, Hkv=4), 2),       # G = 3 not built
+    (dict(Hq=7, Hkv=2), 1),        # Hq % Hkv != 0
+    (dict(Hq=16, Hkv=16), 2),      # more than 8 KV heads
+    (dict(Hq=0), 1),
+    (dict(D=64), 2),
+    (dict(bs=32), 2),
+    (dict(P=24), 1),
+    (dict(P=-16), 1),
+    (dict(P=1 << 21), 2),
+    (dict(mb=-1), 1),
+])
+def test_multi_query_workspace_size_rejects(lib, kw, code):
+    rc, _ = _mq_ws(**kw)
+    assert rc == code
+    assert lib.pda_last_error()
+
+
+def test_multi_query_workspace_size_empty_and_limit(lib):
+    assert _mq_ws(S=0) == (0, 0)
+    assert _mq_ws(T=0) == (0, 0)
+    rc, n = _mq_ws(S=4000, T=12000)
+    assert rc == 0 and n > 0 and n % 256 == 0
+    assert pda.multi_query_workspace_size(4000, 12000, 8, 2, 32) == n
+
+
+def _call_mq(lib, fp8=False, **over):
+    a = dict(out=1, lse=None, q=1, qs=1, T=9, k=1, v=1, bt=1, bt_stride=4, ctx=1, S=3, Hq=8,
+             Hkv=2, D=128, bs=16, nblocks=10, mb=4, scale=0.1, k_scale=0.5, v_scale=0.5,
+             causal=1, P=0, ws=256, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)   # noqa: E731
+    head = (vp(a["out"]), vp(a["lse"]), vp(a["q"]), vp(a["qs"]), a["T"], vp(a["k"]), vp(a["v"]),
+            vp(a["bt"]), a["bt_stride"], vp(a["ctx"]), a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+            a["nblocks"], a["mb"], a["scale"])
+    tail = (a["causal"], a["P"], vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+    if fp8:
+        return lib.paged_multi_query_attn_fp8(*head, a["k_scale"], a["v_scale"], *tail)
+    return lib.paged_multi_query_attn(*head, *tail)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(qs=None), 1),
+    (dict(k=None), 1),
+    (dict(bt=None), 1),
+    (dict(ctx=None), 1),
+    (dict(S=4001), 2),
+    (dict(Hq=12, Hkv=4), 2),
+    (dict(D=96), 2),
+    (dict(P=40), 1),
+    (dict(bt_stride=3), 1),        # narrower than max_blocks_per_seq
+    (dict(nblocks=0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(ws=None), 1),
+    (dict(ws_bytes=16), 1),        # too small
+    (dict(ws=257), 1),             # misaligned
+])
+def test_multi_query_rejects_before_launch(lib, fp8, over, code):
+    assert _call_mq(lib, fp8=fp8, **over) == code
+    assert lib.pda_last_error()
+
+
+@pytest.mark.parametrize("over", [dict(k_scale=float("inf")), dict(v_scale=float("nan"))])
+def test_multi_query_fp8_rejects_bad_scales(lib, over):
+    assert _call_mq(lib, fp8=True, **over) == 1
+
+
+def test_multi_query_empty_is_a_no_op(lib):
+    assert _call_mq(lib, S=0, out=None, q=None, ws=None) == 0
+    assert _call_mq(lib, T=0, out=None, q=None, ws=None) == 0
+    assert _call_mq(lib, fp8=True, S=0, out=None, q=None, ws=None) == 0

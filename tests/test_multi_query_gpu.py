@@ -386,3 +386,21 @@ def test_full_size_cascade_sampled(kv_dtype):
         compare_lse(l[b:b + 1], ref_l, what=f"lse request {b}")
     del c
     torch.cuda.empty_cache()
+
+
+def test_most_sequences_per_call():
+    """4000 sequences, the most one call takes, with 0 .. 4 causal queries each."""
+    rng = np.random.default_rng(53)
+    S = 4000
+    lens = rng.integers(1, 200, size=S)
+    nq = np.minimum(rng.integers(0, 5, size=S), lens)
+    case = W.build_mq_case(lens, nq, 8, 2, causal=True, seed=53, device="cuda",
+                           rng_backend="torch", name="mq_s4000")
+    out, lse = run_mq(case)
+    o, l = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(o))
+    seqs = [s for s in rng.choice(S, size=40, replace=False) if nq[s] > 0]
+    picks = [(int(s), int(i)) for s in seqs for i in range(int(nq[s]))]
+    for row, ref, ref_l in sampled_mq_oracle(case, picks):
+        compare_out(o[row], ref, what=f"row {row}")
+        compare_lse(l[row], ref_l, what=f"lse row {row}")

@@ -447,3 +447,40 @@ def test_fp8_partial_api_and_merge():
     ref, ref_lse = oracle_full(case)
     compare_out(to_np(merged), ref)
     compare_lse(to_np(mlse), ref_lse)
+
+
+# --- the largest sizes tested ------------------------------------------------------
+
+def test_longest_context_one_million_tokens():
+    """One sequence of 2^20 tokens (4 GiB of fp16 K/V, the whole GPU's runs
+    splitting it, hundreds of partials per row for the merge).  The oracle
+    checks two of the eight KV heads (it gathers 2^20 rows per head)."""
+    case = W.build_case([1 << 20], 32, 8, seed=22, device="cuda", rng_backend="torch",
+                        name="ctx_1m")
+    out, lse = run(case)
+    assert torch.isfinite(out.float()).all()
+    q, k, v, table, lens = W.host_sequences(case, [0])
+    kv_heads = [0, 7]
+    q_heads = [h for g in kv_heads for h in range(4 * g, 4 * g + 4)]
+    ref, ref_lse = O.paged_decode_attention(q[:, q_heads], k[:, :, kv_heads], v[:, :, kv_heads],
+                                            table, lens, case.scale)
+    compare_out(to_np(out)[0, q_heads], ref[0], what="ctx 2^20")
+    compare_lse(to_np(lse)[0, q_heads], ref_lse[0], what="ctx 2^20")
+    del case, k, v
+    torch.cuda.empty_cache()
+
+
+def test_many_sequences():
+    """8192 sequences of 0 .. 299 tokens (every 97th empty) in one call."""
+    rng = np.random.default_rng(23)
+    lens = rng.integers(0, 300, size=8192)
+    lens[::97] = 0
+    case = W.build_case(lens, 32, 8, seed=23, device="cuda", rng_backend="torch", name="b8192")
+    out, lse = run(case)
+    o, l = to_np(out), to_np(lse)
+    empty = np.flatnonzero(case.lens == 0)
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
+    ids = sorted(set(_sample(case.lens, np.random.default_rng(3), k=8)) | {int(empty[1])})
+    _check_sampled(case, out, lse, ids)
+    del case
+    torch.cuda.empty_cache()
