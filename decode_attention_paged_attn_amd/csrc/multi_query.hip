@@ -72,6 +72,20 @@ constexpr int lds_row() { return 128 * KvFmt<kFp8>::kElemBytes + 16; }
 constexpr int kNoMask = -(1 << 30);   // causal base of a tile without the causal mask
 constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a row's reference max
 
+#ifndef PDA_MQ_NT_REG
+#define PDA_MQ_NT_REG 1
+#endif
+#ifndef PDA_MQ_NT_STAGE
+#define PDA_MQ_NT_STAGE 0
+#endif
+// K/V loads: non-temporal where a tile streams its own K/V (register kernel),
+// or ordinary where tiles of one sequence read the same K/V again
+template <bool kNt, typename T>
+__device__ __forceinline__ T kv_load(const char* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
 struct MqParams {
   const _Float16* q;        // [T, Hq, D]
   const int32_t* qs;        // [S + 1]: queries of sequence s are rows qs[s] .. qs[s+1]-1
@@ -540,10 +554,10 @@ __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int 
   auto load = [&](long long off, u32x4 (&kr)[KL], VRow (&vr)[4]) {
 #pragma unroll
     for (int ii = 0; ii < KL; ++ii)
-      kr[ii] = *reinterpret_cast<const u32x4*>(kbytes + off + k_lane + 64 * ii);
+      kr[ii] = kv_load<PDA_MQ_NT_REG != 0, u32x4>(kbytes + off + k_lane + 64 * ii);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-      vr[ii] = *reinterpret_cast<const VRow*>(vbytes + off + v_lane + ii * row_bytes);
+      vr[ii] = kv_load<PDA_MQ_NT_REG != 0, VRow>(vbytes + off + v_lane + ii * row_bytes);
   };
   constexpr int NB = kRegRing;
   u32x4 kbuf[NB][KL];
@@ -628,8 +642,8 @@ __device__ __forceinline__ void mq_shared_segment(const MqParams& p, char* kv, i
   for (int ii = 0; ii < NB - 1; ++ii)
     if (ii < nblk) {
       const long long off = win.offset(ii);
-      pk[ii] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
-      pv[ii] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
+      pk[ii] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(kbytes + off + g_off);
+      pv[ii] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(vbytes + off + g_off);
     }
   for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
 #pragma unroll
@@ -639,8 +653,8 @@ __device__ __forceinline__ void mq_shared_segment(const MqParams& p, char* kv, i
       const int nxt = cur + NB - 1;
       if (nxt < nblk) {
         const long long off = win.offset(nxt);
-        pk[(sl + NB - 1) % NB] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
-        pv[(sl + NB - 1) % NB] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
+        pk[(sl + NB - 1) % NB] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(kbytes + off + g_off);
+        pv[(sl + NB - 1) % NB] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(vbytes + off + g_off);
       }
       // stage block cur; every wave finished the block that last used this
       // stage before the previous barrier
@@ -985,8 +999,8 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
     for (int b = 0; b < 2; ++b)
       if (2 * step + b < nblk) {
         const long long off = win.offset(2 * step + b);
-        k2[b] = *reinterpret_cast<const Chunk*>(kbytes + off + g_off);
-        v2[b] = *reinterpret_cast<const Chunk*>(vbytes + off + g_off);
+        k2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(kbytes + off + g_off);
+        v2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(vbytes + off + g_off);
       }
   };
   fetch(0, rk[0], rv[0]);
