@@ -82,9 +82,10 @@ def test_small_all_group_sizes(G, Hkv, causal, P):
 # The library picks its tile kernel from the average query rows per sequence
 # (query tokens x G): up to 16 and 32 rows the register kernel with one or two
 # 16-row blocks per wave, up to 64 the shared kernel with 64-row tiles, above
-# that 128-row tiles.  Each pattern lands in one of the four, at every group
-# size.
-VARIANT_ROWS = {"register16": 12, "register32": 28, "shared64": 48, "shared128": 200}
+# that 128-row tiles (the wide kernel).  Each pattern lands in one of the four,
+# at every group size.
+VARIANT_ROWS = {"register16": 12, "register32": 28, "shared64": 48, "wide128": 200,
+                "wide128_part": 100}   # 100 rows: the last wave of a tile is partly used
 
 
 @pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1)])
