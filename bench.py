@@ -40,6 +40,26 @@ KERNEL_SOURCES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def input_fingerprint(case):
+    """SHA-256 of the small inputs (q, block table, context lengths) and a
+    checksum of each K/V pool computed on the device (the sum of its 16-bit
+    words as int64), so that a run's synthetic inputs can be compared."""
+    import torch
+
+    def sha(t):
+        return hashlib.sha256(t.contiguous().cpu().numpy().tobytes()).hexdigest()[:16]
+
+    def pool_sum(t):
+        words = t.contiguous().view(torch.int16) if t.element_size() == 2 else \
+            t.contiguous().view(torch.uint8)
+        return int(words.to(torch.int64).sum().item()) if words.numel() < (1 << 28) else \
+            int(sum(int(c.to(torch.int64).sum().item()) for c in words.view(-1).split(1 << 28)))
+
+    return {"q_sha256_16": sha(case.q), "block_table_sha256_16": sha(case.block_table),
+            "context_lens_sha256_16": sha(case.context_lens),
+            "k_pool_word_sum": pool_sum(case.k_cache), "v_pool_word_sum": pool_sum(case.v_cache)}
+
+
 def source_hash(op="attention"):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[op]:
@@ -503,6 +523,7 @@ def main():
             "traffic": traffic,
         },
         "kernel_source_sha256_16": source_hash(),
+        "inputs": input_fingerprint(case),
     }
     if args.flush_mib:
         rec["flush_mib_between_steps"] = args.flush_mib
