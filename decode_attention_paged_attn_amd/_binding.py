@@ -161,6 +161,24 @@ def is_fp8_cache(k_cache):
     return k_cache.dtype in FP8_DTYPES
 
 
+def _check_buffer(t, dtype, shape, dev, what):
+    """A caller-given output: dtype, shape, contiguity and device, before any launch."""
+    if (t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or t.device != dev):
+        raise ValueError(f"{what} must be contiguous {dtype} {list(shape)} on {dev}")
+
+
+def _workspace(workspace, nbytes, dev):
+    """The caller's workspace (checked), or a new one of nbytes."""
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer on {dev}")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace
+
+
 def _check_inputs(q, k_cache, v_cache, block_table, context_lens):
     if q.dtype != torch.float16:
         raise TypeError("q must be float16")
@@ -201,21 +219,16 @@ def _run(partial, q, k_cache, v_cache, block_table, context_lens, scale, out, ls
     if mb > width:
         raise ValueError("max_blocks_per_seq exceeds the block table width")
     bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
-    ws_bytes = workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs, dev.index)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < ws_bytes:
-        raise ValueError(f"workspace needs {ws_bytes} bytes")
+    workspace = _workspace(workspace,
+                           workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs, dev.index), dev)
     out_dtype = torch.float32 if partial else torch.float16
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
-    if out.dtype != out_dtype or out.shape != (B, Hq, D) or not out.is_contiguous():
-        raise ValueError(f"output must be contiguous {out_dtype} [B, Hq, D]")
+    _check_buffer(out, out_dtype, (B, Hq, D), dev, "the output")
     if lse is None and need_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B, Hq)
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [B, Hq]")
+    if lse is not None:
+        _check_buffer(lse, torch.float32, (B, Hq), dev, "lse")
     lib = load_library()
     ws_n = workspace.numel() * workspace.element_size()
     if is_fp8_cache(k_cache):
@@ -281,10 +294,11 @@ def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
     dev = o_parts.device
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
-    if out.dtype != torch.float16 or out.shape != (B, Hq, D) or not out.is_contiguous():
-        raise ValueError("out must be contiguous float16 [B, Hq, D]")
+    _check_buffer(out, torch.float16, (B, Hq, D), dev, "out")
     if lse_out is None and return_lse:
         lse_out = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _check_buffer(lse_out, torch.float32, (B, Hq), dev, "lse_out")
     _check(load_library().merge_partials(_ptr(out), _ptr(lse_out), _ptr(o_parts),
                                          _ptr(lse_parts), R, B, Hq, D, _stream(dev)))
     return (out, lse_out) if return_lse else out
@@ -367,21 +381,17 @@ def _run_mq(partial, q, k_cache, v_cache, block_table, context_lens, query_start
     if mb > width:
         raise ValueError("max_blocks_per_seq exceeds the block table width")
     bt_stride = block_table.stride(0) if S > 0 else max(mb, 1)
-    ws_bytes = multi_query_workspace_size(S, T, Hq, Hkv, mb, partition_tokens, D, bs, dev.index)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < ws_bytes:
-        raise ValueError(f"workspace needs {ws_bytes} bytes")
+    workspace = _workspace(
+        workspace, multi_query_workspace_size(S, T, Hq, Hkv, mb, partition_tokens, D, bs,
+                                              dev.index), dev)
     out_dtype = torch.float32 if partial else torch.float16
     if out is None:
         out = torch.empty((T, Hq, D), dtype=out_dtype, device=dev)
-    if out.dtype != out_dtype or out.shape != (T, Hq, D) or not out.is_contiguous():
-        raise ValueError(f"output must be contiguous {out_dtype} [T, Hq, D]")
+    _check_buffer(out, out_dtype, (T, Hq, D), dev, "the output")
     if lse is None and need_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
-    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (T, Hq)
-                            or not lse.is_contiguous()):
-        raise ValueError("lse must be contiguous float32 [T, Hq]")
+    if lse is not None:
+        _check_buffer(lse, torch.float32, (T, Hq), dev, "lse")
     lib = load_library()
     head = (_ptr(out), _ptr(lse), _ptr(q), _ptr(query_start), T, _ptr(k_cache), _ptr(v_cache),
             _ptr(block_table), bt_stride, _ptr(context_lens), S, Hq, Hkv, D, bs, num_blocks, mb,

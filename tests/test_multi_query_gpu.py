@@ -405,3 +405,21 @@ def test_most_sequences_per_call():
     for row, ref, ref_l in sampled_mq_oracle(case, picks):
         compare_out(o[row], ref, what=f"row {row}")
         compare_lse(l[row], ref_l, what=f"lse row {row}")
+
+
+def test_binding_rejects_bad_buffers_before_a_launch():
+    case = W.build_mq_case([40, 9], [3, 2], 8, 2, seed=54, device="cuda")
+    args = (case.q, case.k_cache, case.v_cache, case.block_table, case.context_lens,
+            case.query_start, case.scale)
+    T, Hq = case.T, case.Hq
+    bad = [
+        dict(out=torch.empty((T + 1, Hq, 128), dtype=torch.float16, device="cuda")),
+        dict(out=torch.empty((T, Hq, 128), dtype=torch.float16)),                  # host memory
+        dict(lse_out=torch.empty((T, Hq), dtype=torch.float16, device="cuda")),
+        dict(workspace=torch.empty(16, dtype=torch.uint8, device="cuda")),          # too small
+        dict(workspace=torch.empty(1 << 22, dtype=torch.uint8)),                    # host memory
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            pda.paged_multi_query_attn(*args, **kw)
+    torch.cuda.synchronize()

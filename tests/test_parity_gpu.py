@@ -484,3 +484,28 @@ def test_many_sequences():
     _check_sampled(case, out, lse, ids)
     del case
     torch.cuda.empty_cache()
+
+
+def test_binding_rejects_bad_buffers_before_a_launch():
+    case = W.tiny(device="cuda")
+    args = (case.q, case.k_cache, case.v_cache, case.block_table, case.context_lens, case.scale)
+    B, Hq = case.B, case.Hq
+    bad = [
+        dict(out=torch.empty((B, Hq, 64), dtype=torch.float16, device="cuda")),
+        dict(out=torch.empty((B, Hq, 128), dtype=torch.float32, device="cuda")),
+        dict(out=torch.empty((B, Hq, 128), dtype=torch.float16)),                 # host memory
+        dict(lse_out=torch.empty((B, Hq + 1), dtype=torch.float32, device="cuda")),
+        dict(workspace=torch.empty(16, dtype=torch.uint8, device="cuda")),         # too small
+        dict(workspace=torch.empty(1 << 20, dtype=torch.uint8)),                   # host memory
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            pda.paged_decode_attn(*args, **kw)
+    o = torch.zeros((2, B, Hq, 128), dtype=torch.float32, device="cuda")
+    l = torch.zeros((2, B, Hq), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        pda.merge_partials(o, l, lse_out=torch.empty((B,), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        pda.merge_partials(o, l, out=torch.empty((B, Hq, 128), dtype=torch.float32,
+                                                 device="cuda"))
+    torch.cuda.synchronize()
