@@ -391,34 +391,48 @@ def bench_partial_merge(case, steps, warmup):
 
 
 def bench_append(case, steps, warmup):
-    """Time paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16)."""
+    """paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16),
+    and a decode step both ways: append then attention (two launches) against
+    paged_decode_attn_append (one launch)."""
     import torch
     import decode_attention_paged_attn_amd as pda
     g = torch.Generator(device="cuda").manual_seed(1)
     kn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
     vn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
+    ws = torch.empty(max(pda.workspace_size(case.B, case.Hq, case.Hkv, case.block_table.shape[1]),
+                         1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, case.Hq, 128), dtype=torch.float16, device="cuda")
 
-    def step():
+    def append():
         pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table,
                             case.context_lens)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) / steps * 1e3
-    ev_ms = e0.elapsed_time(e1) / steps
+    def separate():
+        append()
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                              case.context_lens, case.scale, out=out, workspace=ws)
+
+    def fused():
+        pda.paged_decode_attn_append(case.q, kn, vn, case.k_cache, case.v_cache,
+                                     case.block_table, case.context_lens, case.scale, out=out,
+                                     workspace=ws)
+
+    a_wall, a_ev, _ = _time_events(append, steps, warmup)
+    s_wall, s_ev, _ = _time_events(separate, steps, warmup)
+    f_wall, f_ev, _ = _time_events(fused, steps, warmup)
     nbytes = 2 * 2 * case.B * case.Hkv * 128 * 2          # K and V rows, read + write
-    print(json.dumps({"metric": "KV append GB/s", "op": "paged_kv_append", "unit": "GB/s",
-                      "value": round(nbytes / (wall_ms / 1e3) / 1e9, 2),
-                      "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
-                      "us_per_call_events": round(ev_ms * 1e3, 3), "bytes_per_call": nbytes,
+    kvb = kv_bytes(case.lens, case.Hkv)
+    print(json.dumps({"metric": "KV append GB/s; decode step with the append fused",
+                      "op": "paged_kv_append / paged_decode_attn_append", "unit": "GB/s",
+                      "value": round(nbytes / (a_wall / 1e3) / 1e9, 2),
+                      "event_GBps": round(nbytes / (a_ev / 1e3) / 1e9, 2),
+                      "us_per_call_events": round(a_ev * 1e3, 3), "bytes_per_call": nbytes,
+                      "decode_step": {
+                          "append_then_attend_us": round(s_ev * 1e3, 2),
+                          "fused_us": round(f_ev * 1e3, 2),
+                          "fused_KV_read_GBps": round(kvb / (f_ev / 1e3) / 1e9, 2),
+                          "separate_KV_read_GBps": round(kvb / (s_ev / 1e3) / 1e9, 2),
+                          "fused_over_separate_time": round(f_ev / s_ev, 4)},
                       "steps": steps, "config": {"workload": case.name, "batch": case.B,
                                                  "kv_heads": case.Hkv}}), flush=True)
 

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     merge_partials,
     multi_query_workspace_size,
     paged_decode_attn,
+    paged_decode_attn_append,
     paged_decode_attn_partial,
     paged_kv_append,
     paged_multi_query_attn,
@@ -29,6 +30,7 @@ __all__ = [
     "merge_partials",
     "multi_query_workspace_size",
     "paged_decode_attn",
+    "paged_decode_attn_append",
     "paged_decode_attn_partial",
     "paged_kv_append",
     "paged_multi_query_attn",

@@ -74,6 +74,9 @@ _SIGNATURES = {
                                                     _c_i64, _vp, _c_int, _c_int, _c_int, _c_int,
                                                     _c_int, _c_i64, _c_int, _c_float, _c_float,
                                                     _c_float, _c_int, _c_int, _vp, _c_size, _vp]),
+    "paged_decode_attn_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
+                                          _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
+                                          _c_float, _c_int, _vp, _vp, _c_size, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -302,6 +305,45 @@ def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
     _check(load_library().merge_partials(_ptr(out), _ptr(lse_out), _ptr(o_parts),
                                          _ptr(lse_parts), R, B, Hq, D, _stream(dev)))
     return (out, lse_out) if return_lse else out
+
+
+def paged_decode_attn_append(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
+                             scale, out=None, lse_out=None, return_lse=False, partition_tokens=0,
+                             workspace=None, max_blocks_per_seq=None):
+    """paged_kv_append then paged_decode_attn in one launch (fp16 caches).
+
+    Writes k_new / v_new (fp16 [B, Hkv, D]) into slot context_lens[b] - 1 and
+    attends over context_lens[b] tokens; the caches and results are bit for bit
+    those of the two calls.  Returns ``out`` or ``(out, lse)``.
+    """
+    dev = _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    if k_cache.dtype != torch.float16:
+        raise TypeError("paged_decode_attn_append writes fp16 caches")
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    for t in (k_new, v_new):
+        _check_buffer(t, torch.float16, (B, Hkv, D), dev, "k_new and v_new")
+    width = block_table.shape[1]
+    mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    if mb > width:
+        raise ValueError("max_blocks_per_seq exceeds the block table width")
+    bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
+    workspace = _workspace(workspace,
+                           workspace_size(B, Hq, Hkv, mb, partition_tokens, D, bs, dev.index), dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    _check_buffer(out, torch.float16, (B, Hq, D), dev, "the output")
+    lse = lse_out
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check_buffer(lse, torch.float32, (B, Hq), dev, "lse")
+    _check(load_library().paged_decode_attn_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), bt_stride, _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb,
+        float(scale), int(partition_tokens), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev)))
+    return (out, lse) if (return_lse or lse_out is not None) else out
 
 
 def paged_kv_append(k_cache, v_cache, k_new, v_new, block_table, context_lens,

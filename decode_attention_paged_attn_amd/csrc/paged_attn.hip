@@ -127,6 +127,9 @@ struct SplitParams {
   void* out;                // final output of whole-sequence segments
   float* lse_out;           // may be null
   int out_f16;              // out is fp16 (else fp32)
+  // fused append (fp16 caches): the newest token's K/V rows [B, Hkv, D], or null
+  const _Float16* k_new;
+  const _Float16* v_new;
 };
 
 __device__ __forceinline__ int seq_len(const SplitParams& p, int b) {
@@ -233,7 +236,7 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
 }
 
 // One wave: KV head g of sequence b over tokens [tok_lo, tok_hi).
-template <int G, bool kFp8>
+template <int G, bool kFp8, bool kAppend>
 __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g, int b, int tok_lo,
                             int tok_hi, bool whole, int slot) {
   const int c = lane >> 4, t = lane & 15;
@@ -293,7 +296,27 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   // the block table, q and the partials in the caches
   using VRow = typename Fmt::VRow;
   constexpr int KL = Fmt::kKLoads;
-  auto load = [&](long long off, u32x4 (&kr)[KL], VRow (&vr)[4]) {
+  // Fused append: the segment that holds the sequence's newest token writes
+  // k_new / v_new into that token's cache slot and uses them in place of what
+  // its own loads of the slot return, under the conditions of paged_kv_append
+  // (1 <= ctx <= max tokens, the frame inside the pool).  No other segment of
+  // the call reads the slot: the block lies in the sequence's last unit.
+  static_assert(!(kFp8 && kAppend), "the fused append writes fp16 caches");
+  int kb_new = -1, slot_new = 0;
+  if constexpr (kAppend) {
+    if (p.k_new != nullptr) {
+      const int ctx_b = p.ctx[b];
+      if (ctx_b > 0 && ctx_b <= p.max_tokens && tok_hi == ctx_b) {
+        const unsigned frame = (unsigned)p.bt[(long long)b * p.bt_stride + (ctx_b - 1) / kBS];
+        if (frame < (unsigned long long)p.num_blocks) {
+          kb_new = (ctx_b - 1 - tok_lo) / kBS;     // tok_lo is a multiple of the unit
+          slot_new = (ctx_b - 1) % kBS;
+        }
+      }
+    }
+  }
+  auto load = [&](int kbi, u32x4 (&kr)[KL], VRow (&vr)[4]) {
+    const long long off = block_off(kbi);
     const char* kb = kbytes + off;
     const char* vb = vbytes + off;
 #pragma unroll
@@ -303,6 +326,25 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
     for (int i = 0; i < 4; ++i)
       vr[i] = __builtin_nontemporal_load(
           reinterpret_cast<const VRow*>(vb + v_lane + 4 * i * row_bytes));
+    if constexpr (kAppend) {
+      if (kbi == kb_new) {                           // uniform
+        const long long row = ((long long)b * p.Hkv + g) * kD;
+        if (t == slot_new) {
+#pragma unroll
+          for (int i = 0; i < KL; ++i) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p.k_new + row + 8 * c + 32 * i);
+            kr[i] = x;
+            *reinterpret_cast<u32x4*>(const_cast<char*>(kb) + k_lane + 64 * i) = x;
+          }
+        }
+        if (tg == (slot_new & 3)) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(p.v_new + row + 8 * ds);
+          vr[slot_new >> 2] = x;
+          *reinterpret_cast<u32x4*>(const_cast<char*>(vb) + v_lane +
+                                    4 * (slot_new >> 2) * row_bytes) = x;
+        }
+      }
+    }
   };
   auto fold = [&](const u32x4 (&kr)[KL], const VRow (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
@@ -318,14 +360,14 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   VRow vbuf[NB][4];
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i)
-    if (i < nblk) load(block_off(i), kbuf[i], vbuf[i]);
+    if (i < nblk) load(i, kbuf[i], vbuf[i]);
   for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       const int cur = kb0 + s;
       if (cur >= nblk) break;
       const int nxt = cur + NB - 1;
-      if (nxt < nblk) load(block_off(nxt), kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
+      if (nxt < nblk) load(nxt, kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
       fold(kbuf[s], vbuf[s], cur);
     }
   }
@@ -376,7 +418,7 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   }
 }
 
-template <int G, bool kFp8>
+template <int G, bool kFp8, bool kAppend = false>
 __global__ __launch_bounds__(kWave * kMaxWavesPerWG)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu(G, kFp8))))
 void split_kernel(SplitParams p) {
@@ -434,7 +476,7 @@ void split_kernel(SplitParams p) {
     if (p_hi > p_lo) {
       const int tok_lo = p_lo * p.P;
       const int tok_hi = min(p_hi * p.P, n);
-      run_segment<G, kFp8>(p, lds_p, lane, g, b, tok_lo, tok_hi, p_lo == 0 && p_hi == nu,
+      run_segment<G, kFp8, kAppend>(p, lds_p, lane, g, b, tok_lo, tok_hi, p_lo == 0 && p_hi == nu,
                            w + b);
       u = before + p_hi;
     }
@@ -542,19 +584,31 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // host side
 
 // Per-device launch facts, filled once: CU count and how many split-kernel
-// work-groups of each (G, KV format, waves per work-group) shape fit on a CU.
+// work-groups of each (G, kernel kind, waves per work-group) shape fit on a CU.
+// Kernel kinds: 0 = fp16, 1 = FP8, 2 = fp16 with the fused append.
 constexpr int kMaxDevices = 64;
+constexpr int kKinds = 3;
 struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][2][kMaxWavesPerWG + 1] = {};   // [log2 G][fp8][waves per work-group]
+  int wg_per_cu[4][kKinds][kMaxWavesPerWG + 1] = {};   // [log2 G][kind][waves per work-group]
 };
 DeviceFacts g_dev[kMaxDevices];
 
 int log2_group(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
-const void* split_kernel_ptr(int G, bool fp8) {
-  if (fp8) {
+int kernel_kind(bool fp8, bool append) { return fp8 ? 1 : append ? 2 : 0; }
+
+const void* split_kernel_ptr(int G, int kind) {
+  if (kind == 2) {
+    switch (G) {
+      case 1: return reinterpret_cast<const void*>(&split_kernel<1, false, true>);
+      case 2: return reinterpret_cast<const void*>(&split_kernel<2, false, true>);
+      case 4: return reinterpret_cast<const void*>(&split_kernel<4, false, true>);
+      default: return reinterpret_cast<const void*>(&split_kernel<8, false, true>);
+    }
+  }
+  if (kind == 1) {
     switch (G) {
       case 1: return reinterpret_cast<const void*>(&split_kernel<1, true>);
       case 2: return reinterpret_cast<const void*>(&split_kernel<2, true>);
@@ -577,9 +631,9 @@ int head_group(int Hkv) {
   return 1;
 }
 
-// Runs of the unit stream for (G, Hkv, KV format) on the current device: as
+// Runs of the unit stream for (G, Hkv, kernel kind) on the current device: as
 // many work-groups as fit on all CUs at once, divided by the head groups.
-int run_count(int G, int Hkv, bool fp8) {
+int run_count(int G, int Hkv, int kind) {
   const int hg = head_group(Hkv);
   const int n_hgroups = Hkv / hg;
   int dev = 0;
@@ -593,17 +647,17 @@ int run_count(int G, int Hkv, bool fp8) {
       cus = 256;
     f.cus = cus;
     for (int lg = 0; lg < 4; ++lg)
-      for (int f8 = 0; f8 < 2; ++f8)
+      for (int kd = 0; kd < kKinds; ++kd)
         for (int w = 1; w <= kMaxWavesPerWG; ++w) {
           int n = 0;
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg, f8 != 0),
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg, kd),
                                                            w * kWave, 0) != hipSuccess ||
               n <= 0)
             n = 1;
-          f.wg_per_cu[lg][f8][w] = n;
+          f.wg_per_cu[lg][kd][w] = n;
         }
   });
-  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][fp8 ? 1 : 0][hg] / n_hgroups);
+  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][kind][hg] / n_hgroups);
 }
 
 struct Plan {
@@ -639,10 +693,10 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
   return PDA_OK;
 }
 
-Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens, bool fp8) {
+Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens, int kind) {
   Plan pl;
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_runs = run_count(Hq / Hkv, Hkv, fp8);
+  pl.n_runs = run_count(Hq / Hkv, Hkv, kind);
   pl.hg = head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
   pl.n_slots = pl.n_runs + B;
@@ -686,7 +740,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
                   int B, int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
                   int max_blocks, float scale, bool fp8, float k_scale, float v_scale,
                   int partition_tokens, void* workspace, size_t workspace_bytes,
-                  void* stream_ptr) {
+                  void* stream_ptr, const void* k_new = nullptr, const void* v_new = nullptr) {
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks, partition_tokens);
   if (rc != PDA_OK) return rc;
   if (B == 0) return ok();
@@ -699,7 +753,9 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   if (!finite_f32(scale) || !finite_f32(k_scale) || !finite_f32(v_scale))
     return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, fp8);
+  const bool append = k_new != nullptr;
+  if (append && fp8) return fail(PDA_EUNSUPPORTED, "the fused append writes fp16 caches");
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, kernel_kind(fp8, append));
   if (workspace_bytes < pl.total)
     return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
                 pl.total);
@@ -735,6 +791,8 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.out = out;
   sp.lse_out = lse_out;
   sp.out_f16 = out_f16 ? 1 : 0;
+  sp.k_new = static_cast<const _Float16*>(k_new);
+  sp.v_new = static_cast<const _Float16*>(v_new);
   const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
   if (fp8) {
     switch (Hq / Hkv) {
@@ -742,6 +800,13 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
       case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, 0, stream, sp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, true>), grid, block, 0, stream, sp); break;
       default: hipLaunchKernelGGL((split_kernel<8, true>), grid, block, 0, stream, sp); break;
+    }
+  } else if (append) {
+    switch (Hq / Hkv) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, false, true>), grid, block, 0, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, false, true>), grid, block, 0, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, false, true>), grid, block, 0, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, false, true>), grid, block, 0, stream, sp); break;
     }
   } else {
     switch (Hq / Hkv) {
@@ -782,9 +847,10 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size, int max_bl
   if (!bytes) return fail(PDA_EINVAL, "bytes is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  *bytes = B == 0 ? 0
-                  : std::max(make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, false).total,
-                             make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, true).total);
+  size_t need = 0;
+  for (int kind = 0; B > 0 && kind < kKinds; ++kind)   // one size serves every entry point
+    need = std::max(need, make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, kind).total);
+  *bytes = need;
   return ok();
 }
 
@@ -793,7 +859,8 @@ int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size, int max_
   if (!layout) return fail(PDA_EINVAL, "layout is null");
   int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
   if (rc != PDA_OK) return rc;
-  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, kv_fp8 != 0);
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens,
+                            kernel_kind(kv_fp8 != 0, false));
   layout->header_offset = pl.hdr_offset;
   layout->lse_offset = pl.lse_offset;
   layout->o_offset = pl.o_offset;
@@ -814,6 +881,20 @@ int paged_decode_attn(void* out, const void* q, const void* k_cache, const void*
                        context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
                        scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
                        stream);
+}
+
+int paged_decode_attn_append(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* context_lens, int B,
+                             int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
+                             int max_blocks_per_seq, float scale, int partition_tokens,
+                             float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return fail(PDA_EINVAL, "k_new or v_new is null");
+  return run_attention(true, out, lse_out, q, k_cache, v_cache, block_table, block_table_stride,
+                       context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                       scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
+                       stream, k_new, v_new);
 }
 
 int paged_decode_attn_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,

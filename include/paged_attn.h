@@ -254,6 +254,30 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
                     int max_blocks_per_seq, void* stream);
 
 /*
+ * paged_kv_append and paged_decode_attn in one call, for fp16 caches (the
+ * append before the attention of the same passages of the KernelFlume paper,
+ * fused into the attention's launch): the newest token of every sequence
+ * (position context_lens[b] - 1, which the context length already counts)
+ * gets k_new[b] / v_new[b] (fp16 [B, Hkv, D]) in its cache slot, and the
+ * attention uses those rows for that token.  Sequences must own distinct
+ * tail slots, as for paged_kv_append.  The
+ * cache is left as paged_kv_append leaves it and out / lse_out are bit for
+ * bit those of paged_decode_attn after paged_kv_append; sequences whose
+ * length is 0 or above max_blocks_per_seq * block_size, or whose frame lies
+ * outside the pool, get no append (as in paged_kv_append).  One launch fewer
+ * per decode step.  Other arguments, the workspace and the errors are those of
+ * paged_decode_attn; k_new / v_new null with B > 0 -> PDA_EINVAL.  The caches
+ * are written: they must not be read by other work on the GPU meanwhile.
+ */
+int paged_decode_attn_append(void* out, const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* context_lens, int B,
+                             int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
+                             int max_blocks_per_seq, float scale, int partition_tokens,
+                             float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Multi-query attention: several query tokens of each sequence at once, the
  * last n_q tokens of the sequence, over its paged K/V.  Covers a prefill
  * chunk, whose queries see the earlier chunks unmasked and the current chunk

@@ -250,3 +250,20 @@ def test_multi_query_empty_is_a_no_op(lib):
     assert _call_mq(lib, S=0, out=None, q=None, ws=None) == 0
     assert _call_mq(lib, T=0, out=None, q=None, ws=None) == 0
     assert _call_mq(lib, fp8=True, S=0, out=None, q=None, ws=None) == 0
+
+
+def test_fused_append_rejects(lib):
+    vp = ctypes.c_void_p
+
+    def call(**over):
+        a = dict(out=1, q=1, kn=1, vn=1, B=2, ws=256)
+        a.update(over)
+        f = lambda x: None if x is None else vp(x)   # noqa: E731
+        return lib.paged_decode_attn_append(f(a["out"]), f(a["q"]), f(a["kn"]), f(a["vn"]), vp(1),
+                                            vp(1), vp(1), 4, vp(1), a["B"], 8, 2, 128, 16, 10, 4,
+                                            0.1, 0, None, f(a["ws"]), 1 << 30, None)
+    assert call(kn=None) == 1
+    assert call(vn=None) == 1
+    assert call(out=None) == 1
+    assert call(ws=257) == 1
+    assert call(B=0, out=None, q=None, kn=None, vn=None, ws=None) == 0

@@ -509,3 +509,67 @@ def test_binding_rejects_bad_buffers_before_a_launch():
         pda.merge_partials(o, l, out=torch.empty((B, Hq, 128), dtype=torch.float32,
                                                  device="cuda"))
     torch.cuda.synchronize()
+
+
+# --- append fused into the attention call --------------------------------------------
+
+def _new_rows(case, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    kn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
+    vn = torch.randn((case.B, case.Hkv, 128), generator=g, device="cuda").half()
+    return kn, vn
+
+
+def _fused_vs_separate(case, kn, vn, P=0, **kw):
+    """paged_decode_attn_append on a copy of the caches against paged_kv_append +
+    paged_decode_attn on the original: results and whole pools bit for bit."""
+    k2, v2 = case.k_cache.clone(), case.v_cache.clone()
+    _say(f"[fused append] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={P} {kw}")
+    out_f, lse_f = pda.paged_decode_attn_append(case.q, kn, vn, k2, v2, case.block_table,
+                                                case.context_lens, case.scale, return_lse=True,
+                                                partition_tokens=P, **kw)
+    pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table, case.context_lens,
+                        **kw)
+    out_s, lse_s = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                         case.context_lens, case.scale, return_lse=True,
+                                         partition_tokens=P, **kw)
+    torch.cuda.synchronize()
+    # bitwise: the pools' unowned slots hold NaN
+    assert torch.equal(k2.view(torch.int16), case.k_cache.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), case.v_cache.view(torch.int16))
+    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+    return out_f, lse_f
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("P", [0, 32, 512])
+def test_fused_append_equals_append_then_attend(G, Hkv, P):
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257, 1000]
+    case = W.build_case(lens, G * Hkv, Hkv, seed=300 + G, device="cuda",
+                        pool_blocks=sum(-(-n // 16) for n in lens) + 5)
+    kn, vn = _new_rows(case, 301 + G)
+    q, k, v, table, ln = W.host_full(case)
+    out, lse = _fused_vs_separate(case, kn, vn, P)
+    k_ref, v_ref = O.kv_append(k, v, kn.cpu().numpy(), vn.cpu().numpy(), table, ln)
+    ref, ref_lse = O.paged_decode_attention(q, k_ref, v_ref, table, ln, case.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_fused_append_skips_what_append_skips():
+    # max_blocks_per_seq = 2 clamps the 40- and 33-token sequences (no append,
+    # 32 tokens attended); sequence 3's tail frame lies outside the pool
+    case = W.build_case([40, 5, 33, 20], 8, 2, seed=310, device="cuda")
+    bt = case.block_table.clone()
+    bt[3, 1] = case.k_cache.shape[0] + 7
+    case.block_table = bt
+    kn, vn = _new_rows(case, 311)
+    _fused_vs_separate(case, kn, vn, 0, max_blocks_per_seq=2)
+
+
+def test_fused_append_full_size():
+    case = W.llama8b_4k(device="cuda")
+    kn, vn = _new_rows(case, 312)
+    _fused_vs_separate(case, kn, vn)
+    del case
+    torch.cuda.empty_cache()
