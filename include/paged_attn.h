@@ -47,8 +47,9 @@
  * - Ownership: the caller allocates and owns every buffer, the workspace
  *   included.  The library never allocates or frees memory on these calls,
  *   never synchronises, and only enqueues kernels on `stream`, so the calls
- *   may be captured into a HIP graph.  Inputs are read-only; outputs must not
- *   alias inputs.
+ *   may be captured into a HIP graph.  Inputs are read-only (the KV pools
+ *   too, except in paged_kv_append and paged_decode_attn_append, which write
+ *   one slot per sequence); outputs must not alias inputs.
  * - Errors: a non-zero pda_status is returned and pda_last_error() gives a
  *   message for the calling thread.  Argument errors are detected on the host
  *   before anything is enqueued.  Device-side contract violations (a block
@@ -81,8 +82,9 @@ typedef enum {
 
 /*
  * Bytes of device workspace paged_decode_attn and paged_decode_attn_partial
- * need for these sizes (*bytes; 0 when B == 0), enough for both the fp16 and
- * the FP8 entry points.  partition_tokens as in paged_decode_attn.  The size
+ * need for these sizes (*bytes; 0 when B == 0), enough for every decode entry
+ * point: fp16, FP8 and paged_decode_attn_append.  partition_tokens as in
+ * paged_decode_attn.  The size
  * depends on the device (its CU count sets the number of work-groups), so
  * query it on the device that will run the call.
  */
