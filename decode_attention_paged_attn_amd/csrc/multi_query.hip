@@ -39,7 +39,7 @@
 //     folds its rows from there, so the tile's K/V is read once for all its
 //     rows;
 //   * wide kernel (more rows): the shared kernel's staging with 128-row tiles,
-//     32 rows per wave on 32x32 MFMAs and 32 tokens per step.
+//     32 rows per wave on 32x32 MFMAs and 32 tokens per step (64 for FP8).
 // The running max and sum of the softmax are per row, each row has its own
 // last visible token, and steps every row sees in full skip the mask.
 
@@ -701,7 +701,7 @@ void mq_shared_kernel(MqParams p) {
 
 // ---------------------------------------------------------------------------
 // wide kernel: 4 waves x 32 rows per tile on v_mfma_f32_32x32x16_f16, two
-// blocks (32 tokens) per step
+// blocks (32 tokens) per sub-step, one or two sub-steps per step
 //
 // On gfx950 a 32x32x16 f16 MFMA does twice the work of a 16x16x32 one and four
 // times that of a 16x16x16 one in about the same issue time (measured: 2.28,
@@ -719,7 +719,13 @@ void mq_shared_kernel(MqParams p) {
 //     8 tokens and builds the operand of tile u from element u of each.
 
 constexpr int kWideRows = 32;         // query rows per wave
-constexpr int kWideStep = 2 * kBS;    // tokens per step
+// 32-token sub-steps per step: two for FP8 (half the staging registers per
+// token, so twice the tokens fit; chunked prefill 0.84 -> 0.75 ms), one for
+// fp16 (two spill)
+template <bool kFp8>
+constexpr int wide_ns() { return kFp8 ? 2 : 1; }
+template <bool kFp8>
+constexpr int wide_step() { return 2 * kBS * wide_ns<kFp8>(); }   // tokens per step
 
 __device__ __forceinline__ int wide_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
@@ -848,26 +854,36 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
 // tok_hi) when causal, before tok_hi otherwise; rows past the tile's queries
 // see everything and are never stored.
 template <int G, bool kMasked, bool kFp8>
-__device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16& sc, const char* vstage,
-                                          float qk_scale, int lane, int row0, int t0,
-                                          int causal_base, int n_seq, int nq, int tok_hi) {
+__device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[wide_ns<kFp8>()],
+                                          const char* vstage, float qk_scale, int lane, int row0,
+                                          int t0, int causal_base, int n_seq, int nq,
+                                          int tok_hi) {
+  constexpr int kNS = wide_ns<kFp8>();
+  constexpr int kRow = lds_row<kFp8>();
   const int n = lane & 31, hf = lane >> 5;
-  float sv[16];
+  float sv[kNS][16];
   if (kMasked) {
     const int qi = (row0 + n) / G;
     int e = tok_hi;
     if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n_seq), tok_hi);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = t0 + wide_row(r, hf) < e ? sc[r] : -INFINITY;
+    for (int j = 0; j < kNS; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sv[j][r] = t0 + 32 * j + wide_row(r, hf) < e ? sc[j][r] : -INFINITY;
   } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = sc[r];
+    for (int j = 0; j < kNS; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[j][r] = sc[j][r];
   }
   // lazy reference max, as in the 16-row fold: the 2 halves of a row combine
   // only when a score exceeds the reference by more than kLazyMax
-  float xl = sv[0];
+  float xl = sv[0][0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) xl = fmaxf(xl, sv[r]);
+  for (int j = 0; j < kNS; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xl = fmaxf(xl, sv[j][r]);
   if (__ballot(xl * qk_scale > st.m + kLazyMax) != 0) {   // uniform branch
     const float x = fmaxf(xl, __shfl_xor(xl, 32, kWave));
     float mb = x * qk_scale;
@@ -883,28 +899,31 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16& sc, const c
       for (int u = 0; u < 4; ++u) st.acc[u][r] *= ar;
     }
   }
-  float pr[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    pr[r] = fast_exp2(fmaf(sv[r], qk_scale, -st.m));
-    if (kMasked) pr[r] = sv[r] == -INFINITY ? 0.0f : pr[r];   // -inf - (-inf) would be NaN
-  }
   float ps = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; r += 4) ps += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
-  st.lp += ps;
-  const int valid = tok_hi - t0;
+  for (int j = 0; j < kNS; ++j) {
+    float pr[16];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    half8_t pa;
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = fast_exp2(fmaf(sv[j][r], qk_scale, -st.m));
+      if (kMasked) pr[r] = sv[j][r] == -INFINITY ? 0.0f : pr[r];   // -inf - (-inf) would be NaN
+    }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) pa[t] = static_cast<_Float16>(pr[8 * c + t]);
-    half8_t vb[4];
-    wide_v_operands<kMasked, kFp8>(vstage, c, hf, n, valid, vb);
+    for (int r = 0; r < 16; r += 4) ps += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
+    const int valid = tok_hi - t0 - 32 * j;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[u], st.acc[u], 0, 0, 0);
+    for (int c = 0; c < 2; ++c) {
+      half8_t pa;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pa[t] = static_cast<_Float16>(pr[8 * c + t]);
+      half8_t vb[4];
+      wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, c, hf, n, valid, vb);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[u], st.acc[u], 0, 0, 0);
+    }
   }
+  st.lp += ps;
 }
 
 // Normalise and store the wave's rows: register r of lane l holds row
@@ -958,7 +977,9 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
   using Chunk = typename KvFmt<kFp8>::VRow;         // 8 elements: 16 bytes fp16, 8 bytes FP8
   constexpr int E = KvFmt<kFp8>::kElemBytes;
   constexpr int kRow = lds_row<kFp8>();
-  constexpr int kHalf = kWideStep * kRow;           // the K (or V) rows of one stage
+  constexpr int kNS = wide_ns<kFp8>();
+  constexpr int kStepTok = wide_step<kFp8>();
+  constexpr int kHalf = kStepTok * kRow;            // the K (or V) rows of one stage
   const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
   const int n_seq = mq_seq_len(p, s);
   const int row0 = wave * kWideRows;
@@ -978,7 +999,7 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
-  const int nstep = (nblk + 1) / 2;
+  const int nstep = (nblk + 2 * kNS - 1) / (2 * kNS);
   BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
                   (long long)kBS * row_bytes);
 
@@ -992,13 +1013,13 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
 
   // Two LDS stages, one barrier per step; each thread holds the next step's
   // K/V in registers while the step before it is folded.
-  Chunk rk[2][2], rv[2][2];
+  Chunk rk[2][2 * kNS], rv[2][2 * kNS];
   // blocks in increasing order (the window advances by 64 blocks)
-  auto fetch = [&](int step, Chunk (&k2)[2], Chunk (&v2)[2]) {
+  auto fetch = [&](int step, Chunk (&k2)[2 * kNS], Chunk (&v2)[2 * kNS]) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      if (2 * step + b < nblk) {
-        const long long off = win.offset(2 * step + b);
+    for (int b = 0; b < 2 * kNS; ++b)
+      if (2 * kNS * step + b < nblk) {
+        const long long off = win.offset(2 * kNS * step + b);
         k2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(kbytes + off + g_off);
         v2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(vbytes + off + g_off);
       }
@@ -1011,22 +1032,24 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
       if (cur >= nstep) break;
       if (cur + 1 < nstep) fetch(cur + 1, rk[sl ^ 1], rv[sl ^ 1]);
       // stage the step; every wave finished the step that last used this
-      // stage before the previous barrier.  A missing second block leaves
-      // stale rows, which lie past tok_hi: the softmax masks them and their V
-      // rows are selected to zero.
+      // stage before the previous barrier.  Blocks past the segment's end
+      // leave stale rows, which lie past tok_hi: the softmax masks them and
+      // their V rows are selected to zero.
       char* kstage = kv + sl * 2 * kHalf;
       char* vstage = kstage + kHalf;
-      *reinterpret_cast<Chunk*>(kstage + s_off) = rk[sl][0];
-      *reinterpret_cast<Chunk*>(vstage + s_off) = rv[sl][0];
-      if (2 * cur + 1 < nblk) {
-        *reinterpret_cast<Chunk*>(kstage + kBS * kRow + s_off) = rk[sl][1];
-        *reinterpret_cast<Chunk*>(vstage + kBS * kRow + s_off) = rv[sl][1];
-      }
+#pragma unroll
+      for (int bb = 0; bb < 2 * kNS; ++bb)
+        if (2 * kNS * cur + bb < nblk) {
+          *reinterpret_cast<Chunk*>(kstage + bb * kBS * kRow + s_off) = rk[sl][bb];
+          *reinterpret_cast<Chunk*>(vstage + bb * kBS * kRow + s_off) = rv[sl][bb];
+        }
       __syncthreads();
       if (!idle) {
-        const f32x16 sc = wide_qk<kFp8>(qb, kstage, lane);
-        const int t0 = tok_lo + cur * kWideStep;
-        if (t0 + kWideStep > full_end)
+        f32x16 sc[kNS];
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) sc[j] = wide_qk<kFp8>(qb, kstage + 32 * j * kRow, lane);
+        const int t0 = tok_lo + cur * kStepTok;
+        if (t0 + kStepTok > full_end)
           wide_tail<G, true, kFp8>(st, sc, vstage, p.qk_scale, lane, row0, t0, causal_base, n_seq,
                                    nq, tok_hi);
         else
@@ -1042,7 +1065,7 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
 template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_wide_kernel(MqParams p) {
-  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * kWideStep * lds_row<kFp8>()];   // 2 stages
+  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * wide_step<kFp8>() * lds_row<kFp8>()];   // 2 stages
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
