@@ -1079,20 +1079,67 @@ void mq_wide_kernel(MqParams p) {
 // merge: the rows of tiles cut by run boundaries, and of tiles that see no
 // token; one wave per (listed tile, row), spread over the grid
 
+// R consecutive rows of one listed tile, all with nseg <= kSmallSeg partials
+// in slots slot0 .. slot0 + nseg - 1: every load of the R rows is issued at
+// once (the lse values as broadcast loads), and each lane merges its two
+// dims of every row on its own (the same arithmetic as merge_row, with the
+// weights summed in each lane).
+constexpr int kMergeRows = 4;
+constexpr int kSmallSeg = 8;
+__device__ __forceinline__ void merge_rows_small(const float* o, const float* lse, long long slot0,
+                                                 int nseg, long long rows, long long row0,
+                                                 int lane, f32x2 (&res)[kMergeRows],
+                                                 float (&lse_res)[kMergeRows]) {
+  float lv[kMergeRows][kSmallSeg];
+  f32x2 ov[kMergeRows][kSmallSeg];
+#pragma unroll
+  for (int r = 0; r < kMergeRows; ++r)
+#pragma unroll
+    for (int sg = 0; sg < kSmallSeg; ++sg) {
+      const long long at = (slot0 + sg) * rows + row0 + r;
+      lv[r][sg] = sg < nseg ? lse[at] : -INFINITY;
+      ov[r][sg] = sg < nseg ? *reinterpret_cast<const f32x2*>(o + at * kD + 2 * lane)
+                            : f32x2{0.0f, 0.0f};
+    }
+#pragma unroll
+  for (int r = 0; r < kMergeRows; ++r) {
+    float L = lv[r][0];
+#pragma unroll
+    for (int sg = 1; sg < kSmallSeg; ++sg) L = fmaxf(L, lv[r][sg]);
+    res[r] = f32x2{0.0f, 0.0f};
+    lse_res[r] = -INFINITY;
+    if (L == -INFINITY) continue;
+    float wsum = 0.0f;
+    f32x2 acc = {0.0f, 0.0f};
+#pragma unroll
+    for (int sg = 0; sg < kSmallSeg; ++sg) {
+      const float w = sg < nseg ? fast_exp2((lv[r][sg] - L) * kLog2e) : 0.0f;
+      wsum += w;
+      acc.x = fmaf(w, ov[r][sg].x, acc.x);
+      acc.y = fmaf(w, ov[r][sg].y, acc.y);
+    }
+    const float inv = 1.0f / wsum;
+    res[r] = f32x2{acc.x * inv, acc.y * inv};
+    lse_res[r] = L + __builtin_logf(wsum);
+  }
+}
+
 template <int Qt>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4], n_fix = p.hdr[5];
+  // rows of a tile: Qt * Hq = (16 << variant) * Hkv, a multiple of kMergeRows
   const long long rows = (long long)Qt * p.Hq;
-  const long long total = (long long)n_fix * rows;
+  const long long groups = rows / kMergeRows;
+  const long long total = (long long)n_fix * groups;
   for (long long idx = (long long)blockIdx.x * 4 + wave; idx < total;
        idx += (long long)gridDim.x * 4) {
-    const int f = (int)(idx / rows);
-    const int row = (int)(idx % rows);
+    const int f = (int)(idx / groups);
+    const long long row0 = (idx % groups) * kMergeRows;
     const int i = p.t_fix[f];
-    const int qi = row / p.Hq, h = row % p.Hq;
-    if (qi >= p.t_nq[i]) continue;
+    const int nq = p.t_nq[i];
+    if (row0 / p.Hq >= nq) continue;                 // every row past the tile's queries
     const int ub = p.t_ub[i];
     const int nu = (i + 1 < n_tiles ? p.t_ub[i + 1] : U) - ub;
     int nseg = 0;
@@ -1102,17 +1149,29 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
       nseg = w1 - w0 + 1;
       slot0 = (long long)w0 + p.t_rank[i];
     }
-    f32x2 res;
-    float lse_res;
-    merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, rows, row, lane, res, lse_res);
-    const long long dst = ((long long)(p.t_q0[i] + qi) * p.Hq + h) * kD + 2 * lane;
-    if (p.out_f16) {
-      half2_t hv = {static_cast<_Float16>(res.x), static_cast<_Float16>(res.y)};
-      *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+    f32x2 res[kMergeRows];
+    float lse_res[kMergeRows];
+    if (nseg <= kSmallSeg) {
+      merge_rows_small(p.ws_o, p.ws_lse, slot0, nseg, rows, row0, lane, res, lse_res);
     } else {
-      *reinterpret_cast<f32x2*>(static_cast<float*>(p.out) + dst) = res;
+#pragma unroll
+      for (int r = 0; r < kMergeRows; ++r)
+        merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, rows, row0 + r, lane, res[r], lse_res[r]);
     }
-    if (p.lse_out && lane == 0) p.lse_out[(long long)(p.t_q0[i] + qi) * p.Hq + h] = lse_res;
+#pragma unroll
+    for (int r = 0; r < kMergeRows; ++r) {
+      const long long row = row0 + r;
+      const int qi = (int)(row / p.Hq), h = (int)(row % p.Hq);
+      if (qi >= nq) continue;
+      const long long dst = ((long long)(p.t_q0[i] + qi) * p.Hq + h) * kD + 2 * lane;
+      if (p.out_f16) {
+        half2_t hv = {static_cast<_Float16>(res[r].x), static_cast<_Float16>(res[r].y)};
+        *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+      } else {
+        *reinterpret_cast<f32x2*>(static_cast<float*>(p.out) + dst) = res[r];
+      }
+      if (p.lse_out && lane == 0) p.lse_out[(long long)(p.t_q0[i] + qi) * p.Hq + h] = lse_res[r];
+    }
   }
 }
 
@@ -1276,11 +1335,12 @@ void mq_launch_aux(bool plan, const MqParams& mp, const MqPlan& pl, hipStream_t 
     hipLaunchKernelGGL((mq_plan_kernel<Qt>), dim3(1), dim3(kWave), 0, stream, mp);
     return;
   }
-  // one wave per row of the at most n_runs - 1 cut tiles (the rows of empty
-  // tiles, rare, are covered by the grid-stride loop)
-  const long long merge_rows = (long long)std::max(pl.n_runs - 1, 1) * Qt * mp.Hq;
+  // one wave per kMergeRows rows of the at most n_runs - 1 cut tiles (the rows
+  // of empty tiles, rare, are covered by the grid-stride loop)
+  const long long merge_groups =
+      (long long)std::max(pl.n_runs - 1, 1) * Qt * mp.Hq / kMergeRows;
   hipLaunchKernelGGL((mq_merge_kernel<Qt>),
-                     dim3((unsigned)std::min<long long>((merge_rows + 3) / 4, 1 << 20)),
+                     dim3((unsigned)std::min<long long>((merge_groups + 3) / 4, 1 << 20)),
                      dim3(256), 0, stream, mp);
 }
 
