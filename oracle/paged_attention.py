@@ -65,6 +65,8 @@ __all__ = [
     "kv_append",
     "fp8_e4m3_value",
     "fp8_e4m3_decode",
+    "fp8_e4m3_encode",
+    "kv_append_fp8",
     "paged_decode_attention_fp8",
     "kv_cache_bytes",
     "kv_read_bytes",
@@ -340,6 +342,42 @@ def fp8_e4m3_decode(codes):
     """Element-wise fp8_e4m3_value of a uint8 array, as float64."""
     table = np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
     return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp8_e4m3_encode(x):
+    """E4M3 code (uint8) of each value: the nearest finite E4M3 value, ties to
+    the even code (the one whose mantissa ends in 0, as in round-to-nearest-
+    even); the sign of zero is kept; NaN gives 0x7F with its sign; magnitudes
+    at or above the largest finite value, 448, saturate to +-448.
+
+    Saturation is a reading: the format leaves out-of-range conversion open,
+    and a NaN written into a KV cache would poison every attention over it.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos = fp8_e4m3_decode(np.arange(0x7F))          # codes 0x00 .. 0x7E: 0 .. 448, increasing
+    a = np.abs(x)
+    i = np.clip(np.searchsorted(pos, a), 1, 0x7E)    # pos[i-1] < a <= pos[i] inside the range
+    lo, hi = pos[i - 1], pos[i]
+    up = (hi - a < a - lo) | ((hi - a == a - lo) & (i % 2 == 0))
+    code = np.where(up, i, i - 1)
+    code = np.where(a >= 448.0, 0x7E, code)
+    sign = np.signbit(x).astype(np.int64) << 7
+    code = np.where(np.isnan(x), 0x7F, code) | sign
+    return code.astype(np.uint8)
+
+
+def kv_append_fp8(k_codes, v_codes, k_new, v_new, block_table, context_lens, k_scale, v_scale,
+                  block_size=16):
+    """kv_append into FP8 E4M3 pools: the new rows are quantised to
+    fp8_e4m3_encode(fp32(x) * fp32(1 / scale)) with the tensor's scale (the
+    product and the reciprocal rounded to fp32), so that scale * value(code)
+    is the stored approximation of x (the FP8 KV cache of "4. Quantised KV
+    cache" in "Optimising decode in vLLM", one scale per tensor)."""
+    inv_k = np.float32(1.0) / np.float32(k_scale)
+    inv_v = np.float32(1.0) / np.float32(v_scale)
+    kq = fp8_e4m3_encode(np.asarray(k_new, dtype=np.float32) * inv_k)
+    vq = fp8_e4m3_encode(np.asarray(v_new, dtype=np.float32) * inv_v)
+    return kv_append(k_codes, v_codes, kq, vq, block_table, context_lens, block_size)
 
 
 def paged_decode_attention_fp8(q, k_codes, v_codes, block_table, context_lens, scale, k_scale,

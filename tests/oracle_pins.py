@@ -422,6 +422,74 @@ def pin_fp8_decode(O):
     assert np.array_equal(got[ok], ref[ok])
 
 
+def pin_fp8_encode(O):
+    codes = np.arange(256)
+    finite = (codes & 0x7F) != 0x7F
+    # the encoder inverts the decoder on every finite code (-0 included)
+    assert np.array_equal(O.fp8_e4m3_encode(O.fp8_e4m3_decode(codes[finite])), codes[finite])
+    # midpoints of adjacent codes go to the even one (exact in float32: 5 bits)
+    pos = O.fp8_e4m3_decode(np.arange(0x7F))
+    mid = (pos[:-1] + pos[1:]) / 2
+    up = np.arange(1, 0x7F)
+    want = np.where(up % 2 == 0, up, up - 1)
+    assert np.array_equal(O.fp8_e4m3_encode(mid), want)
+    assert np.array_equal(O.fp8_e4m3_encode(-mid), want | 0x80)
+    # just off a midpoint goes to the nearer code
+    assert np.array_equal(O.fp8_e4m3_encode(np.nextafter(mid, np.inf)), up)
+    assert np.array_equal(O.fp8_e4m3_encode(np.nextafter(mid, -np.inf)), up - 1)
+    # saturation, infinities, NaN
+    assert O.fp8_e4m3_encode([448.0, 463.9, 464.0, 1e30, np.inf, -np.inf, -1e30]).tolist() == \
+        [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert int(O.fp8_e4m3_encode([np.nan])[0]) & 0x7F == 0x7F
+    # an independent encoder of the same format: torch's float8_e4m3fn
+    # conversion (round to nearest even), below 464 where it does not overflow
+    import torch
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal(4000) * 10.0 ** rng.uniform(-4, 2.6, 4000)
+    x = np.concatenate([x, mid, -mid, [0.0, -0.0, 2.0 ** -10, 2.0 ** -9 * 1.5]]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x), ref)
+
+
+def pin_kv_append_fp8(O):
+    rng = np.random.default_rng(26)
+    Hkv, D = 2, 8
+    lens = [0, 1, 16, 17, 40]
+    _, _, _, table, _ = small_paged(rng, lens, 2, Hkv, D)
+    pool = int(table.max()) + 1
+    k = rng.integers(0, 0x7F, size=(pool, 16, Hkv, D)).astype(np.uint8)
+    v = rng.integers(0, 0x7F, size=(pool, 16, Hkv, D)).astype(np.uint8)
+    kn = (rng.standard_normal((len(lens), Hkv, D)) * 3).astype(np.float16)
+    vn = (rng.standard_normal((len(lens), Hkv, D)) * 0.2).astype(np.float16)
+    ks = float(np.abs(kn.astype(np.float64)).max()) / 400      # in range: no saturation
+    vs = float(np.abs(vn.astype(np.float64)).max()) / 400
+    k2, v2 = O.kv_append_fp8(k, v, kn, vn, table, lens, ks, vs)
+    changed = set()
+    for b, n in enumerate(lens):
+        if n <= 0:
+            continue
+        fr, sl = int(table[b][(n - 1) // 16]), (n - 1) % 16
+        changed.add((fr, sl))
+        for src, codes, s_ in ((kn, k2, ks), (vn, v2, vs)):
+            back = s_ * O.fp8_e4m3_decode(codes[fr, sl])
+            x = src[b].astype(np.float64)
+            # E4M3 keeps 3 mantissa bits: within half a step, 2^-4 relative, or
+            # half the smallest step 2^-10 * scale near zero
+            assert np.all(np.abs(back - x) <= np.maximum(np.abs(x) * 2.0 ** -4, s_ * 2.0 ** -10)
+                          * (1 + 1e-6)), (b, s_)
+    for fr in range(pool):
+        for sl in range(16):
+            if (fr, sl) not in changed:
+                assert np.array_equal(k2[fr, sl], k[fr, sl]) and np.array_equal(v2[fr, sl], v[fr, sl])
+    # beyond the range the codes saturate to +-448
+    big = np.full_like(kn, 1000.0)
+    big[:, :, 1::2] = -1000.0
+    k3, _ = O.kv_append_fp8(k, v, big, vn, table, lens, 1.0, vs)
+    fr, sl = int(table[4][39 // 16]), 39 % 16
+    assert set(k3[fr, sl].ravel().tolist()) == {0x7E, 0xFE}
+
+
 def pin_fp8_attention(O):
     rng = np.random.default_rng(24)
     Hq, Hkv, D = 4, 2, 8
@@ -479,5 +547,7 @@ ALL_PINS = [
     pin_poison_not_read,
     pin_kv_append,
     pin_fp8_decode,
+    pin_fp8_encode,
+    pin_kv_append_fp8,
     pin_fp8_attention,
 ]

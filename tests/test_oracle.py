@@ -25,6 +25,19 @@ _token_location = O.token_location
 _segments = O.balanced_segments
 _append = O.kv_append
 _fp8 = O.fp8_e4m3_value
+_fp8_encode = O.fp8_e4m3_encode
+_append_fp8 = O.kv_append_fp8
+
+
+def _encode_ties_away(x):
+    """Round half away from zero instead of to the even code."""
+    x = np.asarray(x, dtype=np.float64)
+    c = _fp8_encode(x)
+    pos = O.fp8_e4m3_decode(np.arange(0x7F))
+    a = np.abs(x)
+    i = np.clip(np.searchsorted(pos, a), 1, 0x7E)
+    tie = (pos[i] - a == a - pos[i - 1]) & (a < 448)
+    return np.where(tie, (i | (c & 0x80)).astype(np.uint8), c)
 
 
 def _attend_lse_without_max(q_rows, K, V, scale):
@@ -72,6 +85,10 @@ MUTANTS = {
                                  bs)),
     "fp8_bias_8": ("fp8_e4m3_value",
                    lambda code: _fp8(code) / 2.0 if (int(code) >> 3) & 0xF else _fp8(code)),
+    "fp8_encode_ties_away": ("fp8_e4m3_encode", _encode_ties_away),
+    "append_fp8_times_scale": ("kv_append_fp8",
+                               lambda k, v, kn, vn, bt, lens, ks, vs, bs=16: _append_fp8(
+                                   k, v, kn, vn, bt, lens, 1.0 / ks, 1.0 / vs, bs)),
     "partition_end_short": ("partition_ranges",
                             lambda n, P: [(lo, max(lo, hi - 1)) if hi - lo > 1 else (lo, hi)
                                           for lo, hi in _ranges(n, P)]),
