@@ -74,6 +74,8 @@ _SIGNATURES = {
                                                     _c_i64, _vp, _c_int, _c_int, _c_int, _c_int,
                                                     _c_int, _c_i64, _c_int, _c_float, _c_float,
                                                     _c_float, _c_int, _c_int, _vp, _c_size, _vp]),
+    "paged_kv_append_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
+                                     _c_int, _c_i64, _c_int, _c_float, _c_float, _vp]),
     "paged_decode_attn_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
                                           _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                                           _c_float, _c_int, _vp, _vp, _c_size, _vp]),
@@ -347,25 +349,31 @@ def paged_decode_attn_append(q, k_new, v_new, k_cache, v_cache, block_table, con
 
 
 def paged_kv_append(k_cache, v_cache, k_new, v_new, block_table, context_lens,
-                    max_blocks_per_seq=None):
-    """Write token ctx_b - 1 of every sequence (k_new, v_new: fp16 [B, Hkv, D]) in place."""
+                    max_blocks_per_seq=None, k_scale=None, v_scale=None):
+    """Write token ctx_b - 1 of every sequence (k_new, v_new: fp16 [B, Hkv, D]) in place.
+
+    fp16 caches take the rows as they are; FP8 E4M3 caches (uint8 /
+    float8_e4m3fn) store their codes quantised with ``k_scale`` / ``v_scale``.
+    """
     dev = _check_inputs(k_new, k_cache, v_cache, block_table, context_lens)
-    if k_cache.dtype != torch.float16:
-        raise TypeError("paged_kv_append writes fp16 caches")
     B = k_new.shape[0]
     num_blocks, bs, Hkv, D = k_cache.shape
-    if (k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or k_new.dtype != torch.float16
-            or v_new.dtype != torch.float16 or not k_new.is_contiguous()
-            or not v_new.is_contiguous() or k_new.device != dev or v_new.device != dev):
-        raise ValueError("k_new and v_new must be contiguous fp16 [B, Hkv, D] on the caches' GPU")
+    for t in (k_new, v_new):
+        _check_buffer(t, torch.float16, (B, Hkv, D), dev, "k_new and v_new")
     width = block_table.shape[1]
     mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
     if mb > width:
         raise ValueError("max_blocks_per_seq exceeds the block table width")
     bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
-    _check(load_library().paged_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
-                                          _ptr(block_table), bt_stride, _ptr(context_lens), B,
-                                          Hkv, D, bs, num_blocks, mb, _stream(dev)))
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_table), bt_stride,
+            _ptr(context_lens), B, Hkv, D, bs, num_blocks, mb)
+    lib = load_library()
+    if is_fp8_cache(k_cache):
+        if k_scale is None or v_scale is None:
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        _check(lib.paged_kv_append_fp8(*args, float(k_scale), float(v_scale), _stream(dev)))
+    else:
+        _check(lib.paged_kv_append(*args, _stream(dev)))
 
 
 # --- several query tokens per sequence, and cascade attention ------------------

@@ -550,8 +550,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 // KV append: the newest token of each sequence into its tail slot
 
 struct AppendParams {
-  _Float16* k;              // [num_blocks, 16, Hkv, D], written in place
-  _Float16* v;
+  void* k;                  // [num_blocks, 16, Hkv, D] fp16 or E4M3 codes, written in place
+  void* v;
   const _Float16* kn;       // [B, Hkv, D]
   const _Float16* vn;
   const int32_t* bt;
@@ -560,7 +560,27 @@ struct AppendParams {
   long long num_blocks;
   int B, Hkv;
   int max_tokens;
+  float k_inv, v_inv;       // FP8: the codes are e4m3_encode(x * (1 / scale))
 };
+
+// E4M3 code of an fp32 value: the nearest finite E4M3 value, ties to the even
+// code (round to nearest even on the 3-bit mantissa), the sign of zero kept;
+// NaN gives 0x7F with its sign; magnitudes at or above 448, the largest
+// finite value, saturate to +-448 (a NaN written into the cache would poison
+// every attention over it).  Computed exactly: every step below is a scaling
+// by a power of two or a round to integer.
+__device__ __forceinline__ unsigned e4m3_encode(float x) {
+  const unsigned bits = __float_as_uint(x);
+  const unsigned sign = (bits >> 24) & 0x80u;
+  const unsigned mag = bits & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return sign | 0x7Fu;                         // NaN
+  const float a = __uint_as_float(mag);
+  if (a >= 448.0f) return sign | 0x7Eu;                               // saturate
+  if (a < 0.015625f) return sign | (unsigned)rintf(a * 512.0f);       // m * 2^-9, m = 0 .. 8
+  const int e = (int)(mag >> 23) - 127;                               // 2^e <= a < 2^(e+1)
+  const unsigned q = (unsigned)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);  // 0 .. 8 (8 carries)
+  return sign | min(((unsigned)(e + 7) << 3) + q, 0x7Eu);
+}
 
 // One thread per 16-byte chunk of the Hkv * D row of K and of V.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
@@ -576,8 +596,37 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   if (frame >= (unsigned long long)p.num_blocks) return;
   const long long dst = ((long long)frame * kBS + t % kBS) * p.Hkv * kD + (long long)c * 8;
   const long long src = (long long)b * p.Hkv * kD + (long long)c * 8;
-  *reinterpret_cast<u32x4*>(p.k + dst) = *reinterpret_cast<const u32x4*>(p.kn + src);
-  *reinterpret_cast<u32x4*>(p.v + dst) = *reinterpret_cast<const u32x4*>(p.vn + src);
+  *reinterpret_cast<u32x4*>(static_cast<_Float16*>(p.k) + dst) =
+      *reinterpret_cast<const u32x4*>(p.kn + src);
+  *reinterpret_cast<u32x4*>(static_cast<_Float16*>(p.v) + dst) =
+      *reinterpret_cast<const u32x4*>(p.vn + src);
+}
+
+// FP8 pools: one thread per 8 elements (16 bytes of the fp16 row in, 8 bytes
+// of E4M3 codes out) of K and of V.
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams p) {
+  const int chunks = p.Hkv * (kD / 8);
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)p.B * chunks) return;
+  const int b = (int)(i / chunks);
+  const int c = (int)(i % chunks);
+  const int n = p.ctx[b];
+  if (n <= 0 || n > p.max_tokens) return;           // nothing to append / outside the table
+  const int t = n - 1;
+  const unsigned frame = (unsigned)p.bt[(long long)b * p.bt_stride + t / kBS];
+  if (frame >= (unsigned long long)p.num_blocks) return;
+  const long long dst = ((long long)frame * kBS + t % kBS) * p.Hkv * kD + (long long)c * 8;
+  const long long src = (long long)b * p.Hkv * kD + (long long)c * 8;
+  const half8_t kx = *reinterpret_cast<const half8_t*>(p.kn + src);
+  const half8_t vx = *reinterpret_cast<const half8_t*>(p.vn + src);
+  u32x2 kc = {0u, 0u}, vc = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kc[e / 4] |= e4m3_encode(static_cast<float>(kx[e]) * p.k_inv) << (8 * (e % 4));
+    vc[e / 4] |= e4m3_encode(static_cast<float>(vx[e]) * p.v_inv) << (8 * (e % 4));
+  }
+  *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.k) + dst) = kc;
+  *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.v) + dst) = vc;
 }
 
 // ---------------------------------------------------------------------------
@@ -838,6 +887,52 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   return ok();
 }
 
+// Shared body of paged_kv_append and paged_kv_append_fp8.
+int run_append(bool fp8, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+               const int32_t* block_table, int64_t block_table_stride,
+               const int32_t* context_lens, int B, int Hkv, int D, int block_size,
+               int64_t num_blocks, int max_blocks_per_seq, float k_scale, float v_scale,
+               void* stream) {
+  if (B < 0 || Hkv <= 0) return fail(PDA_EINVAL, "B must be >= 0 and Hkv > 0");
+  if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
+  if (block_size != kBS) return fail(PDA_EUNSUPPORTED, "block size %d not built (16 is)", block_size);
+  if (max_blocks_per_seq < 0 || max_blocks_per_seq > (1 << 26))
+    return fail(PDA_EINVAL, "max_blocks_per_seq must be in [0, 2^26]");
+  if (fp8 && (!finite_f32(k_scale) || !finite_f32(v_scale) || k_scale == 0.0f ||
+              v_scale == 0.0f))
+    return fail(PDA_EINVAL, "k_scale and v_scale must be finite and non-zero");
+  if (B == 0 || max_blocks_per_seq == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_table || !context_lens)
+    return fail(PDA_EINVAL, "null pointer");
+  if (block_table_stride < max_blocks_per_seq)
+    return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
+                (long long)block_table_stride, max_blocks_per_seq);
+  if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
+  AppendParams ap;
+  ap.k = k_cache;
+  ap.v = v_cache;
+  ap.kn = static_cast<const _Float16*>(k_new);
+  ap.vn = static_cast<const _Float16*>(v_new);
+  ap.bt = block_table;
+  ap.ctx = context_lens;
+  ap.bt_stride = block_table_stride;
+  ap.num_blocks = num_blocks;
+  ap.B = B;
+  ap.Hkv = Hkv;
+  ap.max_tokens = max_blocks_per_seq * kBS;
+  ap.k_inv = 1.0f / k_scale;
+  ap.v_inv = 1.0f / v_scale;
+  const long long threads = (long long)B * Hkv * (kD / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (fp8)
+    hipLaunchKernelGGL(append_fp8_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ap);
+  else
+    hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), ap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PDA_EHIP, "append kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -966,36 +1061,19 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
                     const int32_t* block_table, int64_t block_table_stride,
                     const int32_t* context_lens, int B, int Hkv, int D, int block_size,
                     int64_t num_blocks, int max_blocks_per_seq, void* stream) {
-  if (B < 0 || Hkv <= 0) return fail(PDA_EINVAL, "B must be >= 0 and Hkv > 0");
-  if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
-  if (block_size != kBS) return fail(PDA_EUNSUPPORTED, "block size %d not built (16 is)", block_size);
-  if (max_blocks_per_seq < 0 || max_blocks_per_seq > (1 << 26))
-    return fail(PDA_EINVAL, "max_blocks_per_seq must be in [0, 2^26]");
-  if (B == 0 || max_blocks_per_seq == 0) return ok();
-  if (!k_cache || !v_cache || !k_new || !v_new || !block_table || !context_lens)
-    return fail(PDA_EINVAL, "null pointer");
-  if (block_table_stride < max_blocks_per_seq)
-    return fail(PDA_EINVAL, "block_table_stride (%lld) < max_blocks_per_seq (%d)",
-                (long long)block_table_stride, max_blocks_per_seq);
-  if (num_blocks <= 0) return fail(PDA_EINVAL, "num_blocks must be > 0");
-  AppendParams ap;
-  ap.k = static_cast<_Float16*>(k_cache);
-  ap.v = static_cast<_Float16*>(v_cache);
-  ap.kn = static_cast<const _Float16*>(k_new);
-  ap.vn = static_cast<const _Float16*>(v_new);
-  ap.bt = block_table;
-  ap.ctx = context_lens;
-  ap.bt_stride = block_table_stride;
-  ap.num_blocks = num_blocks;
-  ap.B = B;
-  ap.Hkv = Hkv;
-  ap.max_tokens = max_blocks_per_seq * kBS;
-  const long long threads = (long long)B * Hkv * (kD / 8);
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), ap);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PDA_EHIP, "append kernel launch: %s", hipGetErrorString(e));
-  return ok();
+  return run_append(false, k_cache, v_cache, k_new, v_new, block_table, block_table_stride,
+                    context_lens, B, Hkv, D, block_size, num_blocks, max_blocks_per_seq, 1.0f,
+                    1.0f, stream);
+}
+
+int paged_kv_append_fp8(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                        const int32_t* block_table, int64_t block_table_stride,
+                        const int32_t* context_lens, int B, int Hkv, int D, int block_size,
+                        int64_t num_blocks, int max_blocks_per_seq, float k_scale,
+                        float v_scale, void* stream) {
+  return run_append(true, k_cache, v_cache, k_new, v_new, block_table, block_table_stride,
+                    context_lens, B, Hkv, D, block_size, num_blocks, max_blocks_per_seq, k_scale,
+                    v_scale, stream);
 }
 
 const char* pda_last_error(void) { return pda::t_last_error.c_str(); }

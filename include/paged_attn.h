@@ -256,6 +256,24 @@ int paged_kv_append(void* k_cache, void* v_cache, const void* k_new,
                     int max_blocks_per_seq, void* stream);
 
 /*
+ * paged_kv_append into FP8 (E4M3) pools, one code per element in the layout
+ * of paged_decode_attn_fp8: the new rows (fp16 [B, Hkv, D]) are quantised with
+ * the tensors' scales, code = E4M3 value nearest to fp32(x) * fp32(1 / scale)
+ * (ties to the even code, the sign of zero kept, magnitudes at or above 448
+ * saturate to +-448, NaN stays NaN), so that scale * value(code) is the stored
+ * approximation of x, as paged_decode_attn_fp8 reads it (the FP8 KV cache of
+ * "4. Quantised KV cache" in "Optimising decode in vLLM: squeezing every
+ * token out of small hardware").  Slots, skip rules and errors as
+ * paged_kv_append; k_scale / v_scale not finite or 0 -> PDA_EINVAL.
+ */
+int paged_kv_append_fp8(void* k_cache, void* v_cache, const void* k_new,
+                        const void* v_new, const int32_t* block_table,
+                        int64_t block_table_stride, const int32_t* context_lens,
+                        int B, int Hkv, int D, int block_size, int64_t num_blocks,
+                        int max_blocks_per_seq, float k_scale, float v_scale,
+                        void* stream);
+
+/*
  * paged_kv_append and paged_decode_attn in one call, for fp16 caches (the
  * append before the attention of the same passages of the KernelFlume paper,
  * fused into the attention's launch): the newest token of every sequence

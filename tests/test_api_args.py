@@ -267,3 +267,17 @@ def test_fused_append_rejects(lib):
     assert call(out=None) == 1
     assert call(ws=257) == 1
     assert call(B=0, out=None, q=None, kn=None, vn=None, ws=None) == 0
+
+
+def test_fp8_append_rejects(lib):
+    vp = ctypes.c_void_p
+
+    def call(ks=0.5, vs=0.5, ptr=1, B=2):
+        p = None if ptr is None else vp(ptr)
+        return lib.paged_kv_append_fp8(p, vp(1), vp(1), vp(1), vp(1), 4, vp(1), B, 2, 128, 16, 10,
+                                       4, ks, vs, None)
+    assert call(ks=float("inf")) == 1
+    assert call(vs=float("nan")) == 1
+    assert call(ks=0.0) == 1
+    assert call(ptr=None) == 1
+    assert call(B=0, ptr=None) == 0

@@ -573,3 +573,33 @@ def test_fused_append_full_size():
     _fused_vs_separate(case, kn, vn)
     del case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 2)])
+def test_fp8_kv_append_then_attend(Hq, Hkv):
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257]   # counts the appended token
+    case = W.build_case(lens, Hq, Hkv, seed=320, device="cuda", kv_dtype="fp8",
+                        pool_blocks=sum(-(-n // 16) for n in lens) + 5)
+    g = torch.Generator(device="cuda").manual_seed(321)
+    kn = torch.randn((case.B, Hkv, 128), generator=g, device="cuda").half()
+    vn = torch.randn((case.B, Hkv, 128), generator=g, device="cuda").half()
+    kn[3, 0, :4] = torch.tensor([1e4, -1e4, 60000.0, -0.0], dtype=torch.float16)   # saturate, -0
+    vn[5, 1, :2] = torch.tensor([float("inf"), float("-inf")], dtype=torch.float16)
+    k_host, v_host = case.k_cache.cpu().numpy(), case.v_cache.cpu().numpy()
+    table, ln = case.block_table_host.copy(), case.lens.copy()
+    k_ref, v_ref = O.kv_append_fp8(k_host, v_host, kn.cpu().numpy(), vn.cpu().numpy(), table, ln,
+                                   case.k_scale, case.v_scale)
+    _say(f"[append fp8] B={case.B} Hkv={Hkv}")
+    pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table, case.context_lens,
+                        **case.attn_kwargs())
+    torch.cuda.synchronize()
+    assert np.array_equal(case.k_cache.cpu().numpy(), k_ref)     # every byte of both pools
+    assert np.array_equal(case.v_cache.cpu().numpy(), v_ref)
+    # attention over the appended cache (sequences whose new V row holds +-inf excluded)
+    out, lse = run(case)
+    q = case.q.cpu().numpy()
+    ref, ref_lse = O.paged_decode_attention_fp8(q, k_ref, v_ref, table, ln, case.scale,
+                                                case.k_scale, case.v_scale)
+    keep = [b for b in range(case.B) if b != 5]
+    compare_out(to_np(out)[keep], ref[keep])
+    compare_lse(to_np(lse)[keep], ref_lse[keep])
