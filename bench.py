@@ -391,9 +391,9 @@ def bench_partial_merge(case, steps, warmup):
 
 
 def bench_append(case, steps, warmup):
-    """paged_kv_append of one token per sequence (reads and writes 2*B*Hkv*D fp16),
-    and a decode step both ways: append then attention (two launches) against
-    paged_decode_attn_append (one launch)."""
+    """paged_kv_append of one token per sequence (reads 2*B*Hkv*D fp16 and writes
+    them in the cache's element type), and a decode step both ways: append then
+    attention (two launches) against paged_decode_attn_append (one launch)."""
     import torch
     import decode_attention_paged_attn_amd as pda
     g = torch.Generator(device="cuda").manual_seed(1)
@@ -402,26 +402,28 @@ def bench_append(case, steps, warmup):
     ws = torch.empty(max(pda.workspace_size(case.B, case.Hq, case.Hkv, case.block_table.shape[1]),
                          1), dtype=torch.uint8, device="cuda")
     out = torch.empty((case.B, case.Hq, 128), dtype=torch.float16, device="cuda")
+    sc = case.attn_kwargs()
 
     def append():
         pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table,
-                            case.context_lens)
+                            case.context_lens, **sc)
 
     def separate():
         append()
         pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
-                              case.context_lens, case.scale, out=out, workspace=ws)
+                              case.context_lens, case.scale, out=out, workspace=ws, **sc)
 
     def fused():
         pda.paged_decode_attn_append(case.q, kn, vn, case.k_cache, case.v_cache,
                                      case.block_table, case.context_lens, case.scale, out=out,
-                                     workspace=ws)
+                                     workspace=ws, **sc)
 
     a_wall, a_ev, _ = _time_events(append, steps, warmup)
     s_wall, s_ev, _ = _time_events(separate, steps, warmup)
     f_wall, f_ev, _ = _time_events(fused, steps, warmup)
-    nbytes = 2 * 2 * case.B * case.Hkv * 128 * 2          # K and V rows, read + write
-    kvb = kv_bytes(case.lens, case.Hkv)
+    elem = 1 if case.kv_dtype == "fp8" else 2
+    nbytes = 2 * case.B * case.Hkv * 128 * (2 + elem)     # K and V rows, read + write
+    kvb = kv_bytes(case.lens, case.Hkv, elem=case.kv_bytes_per_elem)
     print(json.dumps({"metric": "KV append GB/s; decode step with the append fused",
                       "op": "paged_kv_append / paged_decode_attn_append", "unit": "GB/s",
                       "value": round(nbytes / (a_wall / 1e3) / 1e9, 2),
@@ -433,8 +435,9 @@ def bench_append(case, steps, warmup):
                           "fused_KV_read_GBps": round(kvb / (f_ev / 1e3) / 1e9, 2),
                           "separate_KV_read_GBps": round(kvb / (s_ev / 1e3) / 1e9, 2),
                           "fused_over_separate_time": round(f_ev / s_ev, 4)},
-                      "steps": steps, "config": {"workload": case.name, "batch": case.B,
-                                                 "kv_heads": case.Hkv}}), flush=True)
+                      "steps": steps, "dtype": case.kv_dtype,
+                      "config": {"workload": case.name, "batch": case.B, "kv_heads": case.Hkv,
+                                 "kv_dtype": case.kv_dtype}}), flush=True)
 
 
 def main():

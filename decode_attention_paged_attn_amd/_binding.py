@@ -79,6 +79,10 @@ _SIGNATURES = {
     "paged_decode_attn_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
                                           _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                                           _c_float, _c_int, _vp, _vp, _c_size, _vp]),
+    "paged_decode_attn_append_fp8": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
+                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
+                                              _c_int, _c_float, _c_float, _c_float, _c_int, _vp,
+                                              _vp, _c_size, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -311,16 +315,18 @@ def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):
 
 def paged_decode_attn_append(q, k_new, v_new, k_cache, v_cache, block_table, context_lens,
                              scale, out=None, lse_out=None, return_lse=False, partition_tokens=0,
-                             workspace=None, max_blocks_per_seq=None):
-    """paged_kv_append then paged_decode_attn in one launch (fp16 caches).
+                             workspace=None, max_blocks_per_seq=None, k_scale=None, v_scale=None):
+    """paged_kv_append then paged_decode_attn in one launch.
 
-    Writes k_new / v_new (fp16 [B, Hkv, D]) into slot context_lens[b] - 1 and
-    attends over context_lens[b] tokens; the caches and results are bit for bit
-    those of the two calls.  Returns ``out`` or ``(out, lse)``.
+    Writes k_new / v_new (fp16 [B, Hkv, D]) into slot context_lens[b] - 1
+    (quantised with ``k_scale`` / ``v_scale`` for an FP8 cache) and attends over
+    context_lens[b] tokens; the caches and results are bit for bit those of the
+    two calls.  Returns ``out`` or ``(out, lse)``.
     """
     dev = _check_inputs(q, k_cache, v_cache, block_table, context_lens)
-    if k_cache.dtype != torch.float16:
-        raise TypeError("paged_decode_attn_append writes fp16 caches")
+    fp8 = is_fp8_cache(k_cache)
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("an FP8 cache needs k_scale and v_scale")
     B, Hq, D = q.shape
     num_blocks, bs, Hkv, _ = k_cache.shape
     for t in (k_new, v_new):
@@ -340,11 +346,16 @@ def paged_decode_attn_append(q, k_new, v_new, k_cache, v_cache, block_table, con
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     if lse is not None:
         _check_buffer(lse, torch.float32, (B, Hq), dev, "lse")
-    _check(load_library().paged_decode_attn_append(
-        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-        _ptr(block_table), bt_stride, _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb,
-        float(scale), int(partition_tokens), _ptr(lse), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(dev)))
+    head = (_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), bt_stride, _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb,
+            float(scale))
+    tail = (int(partition_tokens), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    lib = load_library()
+    if fp8:
+        _check(lib.paged_decode_attn_append_fp8(*head, float(k_scale), float(v_scale), *tail))
+    else:
+        _check(lib.paged_decode_attn_append(*head, *tail))
     return (out, lse) if (return_lse or lse_out is not None) else out
 
 

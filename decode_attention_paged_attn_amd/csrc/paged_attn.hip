@@ -102,6 +102,25 @@ constexpr int waves_per_eu(int G, bool fp8) { return fp8 && G <= 4 ? PDA_WAVES_P
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kHdrInts = 4;           // k, U, n_runs, P, then units_before[b]
 
+// E4M3 code of an fp32 value: the nearest finite E4M3 value, ties to the even
+// code (round to nearest even on the 3-bit mantissa), the sign of zero kept;
+// NaN gives 0x7F with its sign; magnitudes at or above 448, the largest
+// finite value, saturate to +-448 (a NaN written into the cache would poison
+// every attention over it).  Computed exactly: every step below is a scaling
+// by a power of two or a round to integer.
+__device__ __forceinline__ unsigned e4m3_encode(float x) {
+  const unsigned bits = __float_as_uint(x);
+  const unsigned sign = (bits >> 24) & 0x80u;
+  const unsigned mag = bits & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return sign | 0x7Fu;                         // NaN
+  const float a = __uint_as_float(mag);
+  if (a >= 448.0f) return sign | 0x7Eu;                               // saturate
+  if (a < 0.015625f) return sign | (unsigned)rintf(a * 512.0f);       // m * 2^-9, m = 0 .. 8
+  const int e = (int)(mag >> 23) - 127;                               // 2^e <= a < 2^(e+1)
+  const unsigned q = (unsigned)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);  // 0 .. 8 (8 carries)
+  return sign | min(((unsigned)(e + 7) << 3) + q, 0x7Eu);
+}
+
 // ---------------------------------------------------------------------------
 // split kernel
 
@@ -127,9 +146,11 @@ struct SplitParams {
   void* out;                // final output of whole-sequence segments
   float* lse_out;           // may be null
   int out_f16;              // out is fp16 (else fp32)
-  // fused append (fp16 caches): the newest token's K/V rows [B, Hkv, D], or null
+  // fused append: the newest token's K/V rows [B, Hkv, D] fp16, or null; an
+  // FP8 cache stores e4m3_encode(x * inv) with these reciprocals of its scales
   const _Float16* k_new;
   const _Float16* v_new;
+  float k_inv, v_inv;
 };
 
 __device__ __forceinline__ int seq_len(const SplitParams& p, int b) {
@@ -236,9 +257,10 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
 }
 
 // One wave: KV head g of sequence b over tokens [tok_lo, tok_hi).
+// Forced inline: a call would pass the parameters through the stack.
 template <int G, bool kFp8, bool kAppend>
-__device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g, int b, int tok_lo,
-                            int tok_hi, bool whole, int slot) {
+__device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
+                                            int b, int tok_lo, int tok_hi, bool whole, int slot) {
   const int c = lane >> 4, t = lane & 15;
   const int tg = lane >> 4, ds = lane & 15;
 
@@ -301,7 +323,6 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
   // its own loads of the slot return, under the conditions of paged_kv_append
   // (1 <= ctx <= max tokens, the frame inside the pool).  No other segment of
   // the call reads the slot: the block lies in the sequence's last unit.
-  static_assert(!(kFp8 && kAppend), "the fused append writes fp16 caches");
   int kb_new = -1, slot_new = 0;
   if constexpr (kAppend) {
     if (p.k_new != nullptr) {
@@ -328,20 +349,44 @@ __device__ void run_segment(const SplitParams& p, float* lds_p, int lane, int g,
           reinterpret_cast<const VRow*>(vb + v_lane + 4 * i * row_bytes));
     if constexpr (kAppend) {
       if (kbi == kb_new) {                           // uniform
-        const long long row = ((long long)b * p.Hkv + g) * kD;
+        const long long row = ((long long)b * p.Hkv + g) * kD;   // element index in k_new
         if (t == slot_new) {
 #pragma unroll
           for (int i = 0; i < KL; ++i) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(p.k_new + row + 8 * c + 32 * i);
+            u32x4 x;
+            if constexpr (kFp8) {                    // elements 16c + 64i .. +15 as codes
+              const half8_t h0 = *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i);
+              const half8_t h1 =
+                  *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i + 8);
+              x = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                x[e / 4] |= e4m3_encode(static_cast<float>(h0[e]) * p.k_inv) << (8 * (e % 4));
+                x[2 + e / 4] |= e4m3_encode(static_cast<float>(h1[e]) * p.k_inv) << (8 * (e % 4));
+              }
+            } else {
+              x = *reinterpret_cast<const u32x4*>(p.k_new + row + 8 * c + 32 * i);
+            }
             kr[i] = x;
             *reinterpret_cast<u32x4*>(const_cast<char*>(kb) + k_lane + 64 * i) = x;
           }
         }
         if (tg == (slot_new & 3)) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(p.v_new + row + 8 * ds);
-          vr[slot_new >> 2] = x;
-          *reinterpret_cast<u32x4*>(const_cast<char*>(vb) + v_lane +
-                                    4 * (slot_new >> 2) * row_bytes) = x;
+          VRow x;
+          if constexpr (kFp8) {                      // elements 8ds .. 8ds+7 as codes
+            const half8_t h = *reinterpret_cast<const half8_t*>(p.v_new + row + 8 * ds);
+            x = VRow{0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              x[e / 4] |= e4m3_encode(static_cast<float>(h[e]) * p.v_inv) << (8 * (e % 4));
+          } else {
+            x = *reinterpret_cast<const VRow*>(p.v_new + row + 8 * ds);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)                // a constant index keeps vr in registers
+            if (r == (slot_new >> 2)) vr[r] = x;
+          *reinterpret_cast<VRow*>(const_cast<char*>(vb) + v_lane +
+                                   4 * (slot_new >> 2) * row_bytes) = x;
         }
       }
     }
@@ -563,24 +608,6 @@ struct AppendParams {
   float k_inv, v_inv;       // FP8: the codes are e4m3_encode(x * (1 / scale))
 };
 
-// E4M3 code of an fp32 value: the nearest finite E4M3 value, ties to the even
-// code (round to nearest even on the 3-bit mantissa), the sign of zero kept;
-// NaN gives 0x7F with its sign; magnitudes at or above 448, the largest
-// finite value, saturate to +-448 (a NaN written into the cache would poison
-// every attention over it).  Computed exactly: every step below is a scaling
-// by a power of two or a round to integer.
-__device__ __forceinline__ unsigned e4m3_encode(float x) {
-  const unsigned bits = __float_as_uint(x);
-  const unsigned sign = (bits >> 24) & 0x80u;
-  const unsigned mag = bits & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return sign | 0x7Fu;                         // NaN
-  const float a = __uint_as_float(mag);
-  if (a >= 448.0f) return sign | 0x7Eu;                               // saturate
-  if (a < 0.015625f) return sign | (unsigned)rintf(a * 512.0f);       // m * 2^-9, m = 0 .. 8
-  const int e = (int)(mag >> 23) - 127;                               // 2^e <= a < 2^(e+1)
-  const unsigned q = (unsigned)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);  // 0 .. 8 (8 carries)
-  return sign | min(((unsigned)(e + 7) << 3) + q, 0x7Eu);
-}
 
 // One thread per 16-byte chunk of the Hkv * D row of K and of V.
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
@@ -634,9 +661,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams p) {
 
 // Per-device launch facts, filled once: CU count and how many split-kernel
 // work-groups of each (G, kernel kind, waves per work-group) shape fit on a CU.
-// Kernel kinds: 0 = fp16, 1 = FP8, 2 = fp16 with the fused append.
+// Kernel kinds: 0 = fp16, 1 = FP8, 2 = fp16 and 3 = FP8 with the fused append.
 constexpr int kMaxDevices = 64;
-constexpr int kKinds = 3;
+constexpr int kKinds = 4;
 struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
@@ -646,9 +673,17 @@ DeviceFacts g_dev[kMaxDevices];
 
 int log2_group(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
 
-int kernel_kind(bool fp8, bool append) { return fp8 ? 1 : append ? 2 : 0; }
+int kernel_kind(bool fp8, bool append) { return (fp8 ? 1 : 0) + (append ? 2 : 0); }
 
 const void* split_kernel_ptr(int G, int kind) {
+  if (kind == 3) {
+    switch (G) {
+      case 1: return reinterpret_cast<const void*>(&split_kernel<1, true, true>);
+      case 2: return reinterpret_cast<const void*>(&split_kernel<2, true, true>);
+      case 4: return reinterpret_cast<const void*>(&split_kernel<4, true, true>);
+      default: return reinterpret_cast<const void*>(&split_kernel<8, true, true>);
+    }
+  }
   if (kind == 2) {
     switch (G) {
       case 1: return reinterpret_cast<const void*>(&split_kernel<1, false, true>);
@@ -803,7 +838,8 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
     return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
   if (!workspace) return fail(PDA_EINVAL, "workspace is null");
   const bool append = k_new != nullptr;
-  if (append && fp8) return fail(PDA_EUNSUPPORTED, "the fused append writes fp16 caches");
+  if (append && (k_scale == 0.0f || v_scale == 0.0f))
+    return fail(PDA_EINVAL, "the fused append needs non-zero k_scale and v_scale");
   const Plan pl = make_plan(B, Hq, Hkv, max_blocks, partition_tokens, kernel_kind(fp8, append));
   if (workspace_bytes < pl.total)
     return fail(PDA_EINVAL, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
@@ -842,8 +878,17 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.out_f16 = out_f16 ? 1 : 0;
   sp.k_new = static_cast<const _Float16*>(k_new);
   sp.v_new = static_cast<const _Float16*>(v_new);
+  sp.k_inv = 1.0f / k_scale;
+  sp.v_inv = 1.0f / v_scale;
   const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
-  if (fp8) {
+  if (fp8 && append) {
+    switch (Hq / Hkv) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, true, true>), grid, block, 0, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, true, true>), grid, block, 0, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, true, true>), grid, block, 0, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, true, true>), grid, block, 0, stream, sp); break;
+    }
+  } else if (fp8) {
     switch (Hq / Hkv) {
       case 1: hipLaunchKernelGGL((split_kernel<1, true>), grid, block, 0, stream, sp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, 0, stream, sp); break;
@@ -990,6 +1035,20 @@ int paged_decode_attn_append(void* out, const void* q, const void* k_new, const 
                        context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
                        scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
                        stream, k_new, v_new);
+}
+
+int paged_decode_attn_append_fp8(void* out, const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_table,
+                                 int64_t block_table_stride, const int32_t* context_lens, int B,
+                                 int Hq, int Hkv, int D, int block_size, int64_t num_blocks,
+                                 int max_blocks_per_seq, float scale, float k_scale,
+                                 float v_scale, int partition_tokens, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return fail(PDA_EINVAL, "k_new or v_new is null");
+  return run_attention(true, out, lse_out, q, k_cache, v_cache, block_table, block_table_stride,
+                       context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                       scale, true, k_scale, v_scale, partition_tokens, workspace,
+                       workspace_bytes, stream, k_new, v_new);
 }
 
 int paged_decode_attn_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,

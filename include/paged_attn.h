@@ -83,7 +83,7 @@ typedef enum {
 /*
  * Bytes of device workspace paged_decode_attn and paged_decode_attn_partial
  * need for these sizes (*bytes; 0 when B == 0), enough for every decode entry
- * point: fp16, FP8 and paged_decode_attn_append.  partition_tokens as in
+ * point: fp16, FP8 and the fused appends.  partition_tokens as in
  * paged_decode_attn.  The size
  * depends on the device (its CU count sets the number of work-groups), so
  * query it on the device that will run the call.
@@ -296,6 +296,23 @@ int paged_decode_attn_append(void* out, const void* q, const void* k_new, const 
                              int max_blocks_per_seq, float scale, int partition_tokens,
                              float* lse_out, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * paged_kv_append_fp8 and paged_decode_attn_fp8 in one call: the newest
+ * token's rows are quantised into the FP8 pools exactly as paged_kv_append_fp8
+ * does and attended as paged_decode_attn_fp8 reads them; caches, out and
+ * lse_out are bit for bit those of the two calls.  Arguments, skip rules and
+ * errors as paged_decode_attn_append, with the scales of paged_decode_attn_fp8
+ * (both must be non-zero).
+ */
+int paged_decode_attn_append_fp8(void* out, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, int64_t block_table_stride,
+                                 const int32_t* context_lens, int B, int Hq, int Hkv,
+                                 int D, int block_size, int64_t num_blocks,
+                                 int max_blocks_per_seq, float scale, float k_scale,
+                                 float v_scale, int partition_tokens, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Multi-query attention: several query tokens of each sequence at once, the

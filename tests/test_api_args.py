@@ -281,3 +281,16 @@ def test_fp8_append_rejects(lib):
     assert call(ks=0.0) == 1
     assert call(ptr=None) == 1
     assert call(B=0, ptr=None) == 0
+
+
+def test_fp8_fused_append_rejects(lib):
+    vp = ctypes.c_void_p
+
+    def call(ks=0.5, vs=0.5, kn=1):
+        return lib.paged_decode_attn_append_fp8(vp(1), vp(1), None if kn is None else vp(kn),
+                                                vp(1), vp(1), vp(1), vp(1), 4, vp(1), 2, 8, 2,
+                                                128, 16, 10, 4, 0.1, ks, vs, 0, None, vp(256),
+                                                1 << 30, None)
+    assert call(kn=None) == 1
+    assert call(ks=0.0) == 1
+    assert call(vs=float("inf")) == 1

@@ -524,19 +524,22 @@ def _fused_vs_separate(case, kn, vn, P=0, **kw):
     """paged_decode_attn_append on a copy of the caches against paged_kv_append +
     paged_decode_attn on the original: results and whole pools bit for bit."""
     k2, v2 = case.k_cache.clone(), case.v_cache.clone()
-    _say(f"[fused append] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={P} {kw}")
+    sc = case.attn_kwargs()
+    _say(f"[fused append] {case.name} B={case.B} Hq={case.Hq} Hkv={case.Hkv} P={P} "
+         f"kv={case.kv_dtype} {kw}")
     out_f, lse_f = pda.paged_decode_attn_append(case.q, kn, vn, k2, v2, case.block_table,
                                                 case.context_lens, case.scale, return_lse=True,
-                                                partition_tokens=P, **kw)
+                                                partition_tokens=P, **sc, **kw)
     pda.paged_kv_append(case.k_cache, case.v_cache, kn, vn, case.block_table, case.context_lens,
-                        **kw)
+                        **sc, **kw)
     out_s, lse_s = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                          case.context_lens, case.scale, return_lse=True,
-                                         partition_tokens=P, **kw)
+                                         partition_tokens=P, **sc, **kw)
     torch.cuda.synchronize()
-    # bitwise: the pools' unowned slots hold NaN
-    assert torch.equal(k2.view(torch.int16), case.k_cache.view(torch.int16))
-    assert torch.equal(v2.view(torch.int16), case.v_cache.view(torch.int16))
+    # bitwise (the pools' unowned slots hold NaN): compare the stored words
+    word = torch.int16 if case.k_cache.element_size() == 2 else torch.uint8
+    assert torch.equal(k2.view(word), case.k_cache.view(word))
+    assert torch.equal(v2.view(word), case.v_cache.view(word))
     assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
     return out_f, lse_f
 
@@ -603,3 +606,29 @@ def test_fp8_kv_append_then_attend(Hq, Hkv):
     keep = [b for b in range(case.B) if b != 5]
     compare_out(to_np(out)[keep], ref[keep])
     compare_lse(to_np(lse)[keep], ref_lse[keep])
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("P", [0, 64])
+def test_fp8_fused_append_equals_append_then_attend(G, Hkv, P):
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257, 1000]
+    case = W.build_case(lens, G * Hkv, Hkv, seed=330 + G, device="cuda", kv_dtype="fp8",
+                        pool_blocks=sum(-(-n // 16) for n in lens) + 5)
+    kn, vn = _new_rows(case, 331 + G)
+    kn[2, 0, :3] = torch.tensor([1e4, -1e4, -0.0], dtype=torch.float16)     # saturate, -0
+    q, k, v, table, ln = W.host_full(case)
+    out, lse = _fused_vs_separate(case, kn, vn, P)
+    k_ref, v_ref = O.kv_append_fp8(k, v, kn.cpu().numpy(), vn.cpu().numpy(), table, ln,
+                                   case.k_scale, case.v_scale)
+    ref, ref_lse = O.paged_decode_attention_fp8(q, k_ref, v_ref, table, ln, case.scale,
+                                                case.k_scale, case.v_scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_fp8_fused_append_full_size():
+    case = W.llama8b_4k(device="cuda", kv_dtype="fp8")
+    kn, vn = _new_rows(case, 332)
+    _fused_vs_separate(case, kn, vn)
+    del case
+    torch.cuda.empty_cache()
