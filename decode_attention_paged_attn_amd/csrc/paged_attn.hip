@@ -82,13 +82,16 @@ namespace {
 using namespace pda;
 
 constexpr int kMaxKvHeads = 8;        // one wave per KV head
-constexpr int kMaxWavesPerWG = 4;     // KV heads of one work-group
-// occupancy target of the split kernel and the depth of its ring of K/V
-// register buffers (blocks in flight + 1).  Measured on MI355X: fp16 runs best
-// at 2 waves per SIMD with ring 2 (ring 3 is no faster, 3 waves per SIMD in
-// 168 VGPRs are slower); FP8 blocks are half the bytes and run best at 2
-// waves per SIMD with ring 4 (rings 2, 3, 5, 6 and 8, and 3 or 4 waves per
-// SIMD, are slower).
+#ifndef PDA_MAX_WAVES_PER_WG
+#define PDA_MAX_WAVES_PER_WG 4
+#endif
+constexpr int kMaxWavesPerWG = PDA_MAX_WAVES_PER_WG;   // KV heads of one work-group
+// (1, 2 and 4 heads per work-group measured; 8 is no faster than 4)
+// Occupancy target of the split kernel, held by LDS padding when its registers
+// would allow more, and the depth of its ring of K/V register buffers (blocks
+// in flight + 1).  Measured on MI355X: fp16 runs best at 2 waves per SIMD
+// (3 are 3-4% slower) with ring 2 (3 is no faster); FP8 blocks are half the
+// bytes and run at 2 waves per SIMD with ring 4 (3 is equal, 6 slower).
 #ifndef PDA_WAVES_PER_EU_FP8
 #define PDA_WAVES_PER_EU_FP8 2
 #endif
@@ -302,15 +305,12 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
 #pragma unroll
   for (int r = 0; r < 4; ++r) st.lp[r] = 0.0f;
 
-  // block-id window: lane i holds the id of block (window base + i)
-  int window = lane < nblk ? bt_row[lane] : 0;
-  auto block_off = [&](int kb) -> long long {
-    if ((kb & 63) == 0 && kb > 0) {                  // next window of 64 ids
-      const int idx = kb + lane;
-      window = idx < nblk ? bt_row[idx] : 0;
-    }
+  // Block ids are uniform: each is one scalar load (the table is read-only
+  // here), which the K/V loads in flight never have to wait for.
+  ConstI32* bt_s = (ConstI32*)bt_row;
+  auto block_off = [&](int raw_id) -> long long {
     // ids outside the pool are clamped: a broken table gives wrong numbers, not a fault
-    const unsigned raw = (unsigned)__builtin_amdgcn_readlane(window, kb & 63);
+    const unsigned raw = (unsigned)raw_id;
     const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
     return blk * block_bytes;
   };
@@ -336,8 +336,9 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
       }
     }
   }
-  auto load = [&](int kbi, u32x4 (&kr)[KL], VRow (&vr)[4]) {
-    const long long off = block_off(kbi);
+  // block kbi, whose table entry is id
+  auto load_id = [&](int kbi, int id, u32x4 (&kr)[KL], VRow (&vr)[4]) {
+    const long long off = block_off(id);
     const char* kb = kbytes + off;
     const char* vb = vbytes + off;
 #pragma unroll
@@ -391,30 +392,54 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
       }
     }
   };
+  auto load = [&](int kbi, u32x4 (&kr)[KL], VRow (&vr)[4]) { load_id(kbi, bt_s[kbi], kr, vr); };
   auto fold = [&](const u32x4 (&kr)[KL], const VRow (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
       fold_block<G, true, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, last_valid);
     else
       fold_block<G, false, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
   };
+  auto fold_full = [&](const u32x4 (&kr)[KL], const VRow (&vr)[4]) {
+    fold_block<G, false, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
+  };
 
   // a ring of NB register buffers: blocks kb+1 .. kb+NB-1 are in flight while
-  // block kb is folded (FP8 blocks are half the bytes, so they keep one more)
+  // block kb is folded.  The loop runs whole turns of the ring with no exit
+  // inside, and every step issues its loads (past the last block, the last
+  // block again): with the same loads on every path, the wait before a fold
+  // covers that block's loads only, not the ones behind it.
   constexpr int NB = kFp8 ? PDA_RING_FP8 : PDA_RING_FP16;
   u32x4 kbuf[NB][KL];
   VRow vbuf[NB][4];
 #pragma unroll
-  for (int i = 0; i < NB - 1; ++i)
-    if (i < nblk) load(i, kbuf[i], vbuf[i]);
-  for (int kb0 = 0; kb0 < nblk; kb0 += NB) {
+  for (int i = 0; i < NB - 1; ++i) load(min(i, nblk - 1), kbuf[i], vbuf[i]);
+  // The main loop never holds the last block (the only one that may be
+  // partial), so it folds whole blocks only.
+  // Each turn reads the table entries of the next turn's loads up front, so
+  // no load waits on its id.
+  int kb0 = 0;
+  int ids[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) ids[s] = bt_s[min(s + NB - 1, nblk - 1)];
+  for (; kb0 + NB < nblk; kb0 += NB) {
+    int next_ids[NB];
+#pragma unroll
+    for (int s = 0; s < NB; ++s) next_ids[s] = bt_s[min(kb0 + NB + s + NB - 1, nblk - 1)];
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      const int cur = kb0 + s;
-      if (cur >= nblk) break;
-      const int nxt = cur + NB - 1;
-      if (nxt < nblk) load(nxt, kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
-      fold(kbuf[s], vbuf[s], cur);
+      const int kbi = min(kb0 + s + NB - 1, nblk - 1);
+      load_id(kbi, ids[s], kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
+      fold_full(kbuf[s], vbuf[s]);
     }
+#pragma unroll
+    for (int s = 0; s < NB; ++s) ids[s] = next_ids[s];
+  }
+  // at most NB blocks left, the first NB - 1 of them in flight
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    if (kb0 + s >= nblk) break;
+    if (s == NB - 1) load(nblk - 1, kbuf[s], vbuf[s]);
+    fold(kbuf[s], vbuf[s], kb0 + s);
   }
 
   // epilogue: totals over token slots and token rows, normalise, store
@@ -480,7 +505,7 @@ void split_kernel(SplitParams p) {
   for (int b0 = 0; b0 < p.B; b0 += kWave) {
     const int b = b0 + lane;
     const int nu = b < p.B ? (seq_len(p, b) + p.P - 1) / p.P : 0;
-    U += wave_sum_i32(nu);
+    U += __builtin_amdgcn_readfirstlane(wave_sum_i32(nu));   // equal in every lane
   }
   const int k = U > 0 ? (U + p.n_runs - 1) / p.n_runs : 1;
   const int u_lo = w * k;
@@ -514,7 +539,9 @@ void split_kernel(SplitParams p) {
   float* lds_p = lds[wave];
   int u = u_lo, b = b_start, before = before_start;
   while (u < u_hi && b < p.B) {
-    const int n = seq_len(p, b);
+    // uniform by construction; said so, everything derived from it (the block
+    // index, the table row) stays in scalar registers
+    const int n = __builtin_amdgcn_readfirstlane(seq_len(p, b));
     const int nu = (n + p.P - 1) / p.P;
     const int p_lo = u - before;
     const int p_hi = min(u_hi - before, nu);
@@ -668,6 +695,7 @@ struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
   int wg_per_cu[4][kKinds][kMaxWavesPerWG + 1] = {};   // [log2 G][kind][waves per work-group]
+  int lds_pad[4][kKinds][kMaxWavesPerWG + 1] = {};     // dynamic LDS bytes per launch
 };
 DeviceFacts g_dev[kMaxDevices];
 
@@ -717,31 +745,71 @@ int head_group(int Hkv) {
 
 // Runs of the unit stream for (G, Hkv, kernel kind) on the current device: as
 // many work-groups as fit on all CUs at once, divided by the head groups.
+// Dynamic LDS that holds a split kernel to its measured best occupancy
+// (waves_per_eu waves per SIMD) when its registers would allow more: each
+// work-group takes just over 1 / (target + 1) of the CU's LDS.  0 when the
+// registers already limit it or the padding would not fit.
+int occupancy_pad(int G, int kind, int hg, int lds_cu, int lds_wg_max, int regs_wgs) {
+  const int target = waves_per_eu(G, kind & 1) * 4 / hg;    // 4 SIMDs per CU
+  if (target <= 0 || regs_wgs <= target || lds_cu <= 0) return 0;
+  const int static_lds = (int)sizeof(float) * kMaxWavesPerWG * kBS * 8;
+  const int per_wg = (lds_cu / (target + 1) + 1 + 511) / 512 * 512;
+  if (per_wg * target > lds_cu || per_wg > lds_wg_max) return 0;
+  return std::max(0, per_wg - static_lds);
+}
+
+void device_facts(DeviceFacts& f, int dev) {
+  int cus = 0, lds_cu = 0, lds_wg = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+      hipSuccess)
+    lds_cu = 0;
+  if (hipDeviceGetAttribute(&lds_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+      hipSuccess)
+    lds_wg = 0;
+  f.cus = cus;
+  for (int lg = 0; lg < 4; ++lg)
+    for (int kd = 0; kd < kKinds; ++kd)
+      for (int w = 1; w <= kMaxWavesPerWG; ++w) {
+        const void* fn = split_kernel_ptr(1 << lg, kd);
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, w * kWave, 0) != hipSuccess ||
+            n <= 0)
+          n = 1;
+        const int pad = occupancy_pad(1 << lg, kd, w, lds_cu, lds_wg, n);
+        if (pad > 0) {
+          int m = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, fn, w * kWave, pad) == hipSuccess &&
+              m > 0) {
+            n = m;
+            f.lds_pad[lg][kd][w] = pad;
+          }
+        }
+        f.wg_per_cu[lg][kd][w] = n;
+      }
+}
+
+DeviceFacts* facts() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  DeviceFacts& f = g_dev[dev];
+  std::call_once(f.once, [&f, dev] { device_facts(f, dev); });
+  return &f;
+}
+
 int run_count(int G, int Hkv, int kind) {
   const int hg = head_group(Hkv);
   const int n_hgroups = Hkv / hg;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return 1024 / n_hgroups;        // no device: a fixed size keeps sizing queries usable
-  DeviceFacts& f = g_dev[dev];
-  std::call_once(f.once, [&f, dev] {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    f.cus = cus;
-    for (int lg = 0; lg < 4; ++lg)
-      for (int kd = 0; kd < kKinds; ++kd)
-        for (int w = 1; w <= kMaxWavesPerWG; ++w) {
-          int n = 0;
-          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr(1 << lg, kd),
-                                                           w * kWave, 0) != hipSuccess ||
-              n <= 0)
-            n = 1;
-          f.wg_per_cu[lg][kd][w] = n;
-        }
-  });
-  return std::max(1, f.cus * f.wg_per_cu[log2_group(G)][kind][hg] / n_hgroups);
+  const DeviceFacts* f = facts();
+  if (!f) return 1024 / n_hgroups;  // no device: a fixed size keeps sizing queries usable
+  return std::max(1, f->cus * f->wg_per_cu[log2_group(G)][kind][hg] / n_hgroups);
+}
+
+int lds_pad(int G, int Hkv, int kind) {
+  const DeviceFacts* f = facts();
+  return f ? f->lds_pad[log2_group(G)][kind][head_group(Hkv)] : 0;
 }
 
 struct Plan {
@@ -881,33 +949,34 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.k_inv = 1.0f / k_scale;
   sp.v_inv = 1.0f / v_scale;
   const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
+  const unsigned pad = (unsigned)lds_pad(Hq / Hkv, Hkv, kernel_kind(fp8, append));
   if (fp8 && append) {
     switch (Hq / Hkv) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, true, true>), grid, block, 0, stream, sp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, true, true>), grid, block, 0, stream, sp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, true, true>), grid, block, 0, stream, sp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, true, true>), grid, block, 0, stream, sp); break;
+      case 1: hipLaunchKernelGGL((split_kernel<1, true, true>), grid, block, pad, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, true, true>), grid, block, pad, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, true, true>), grid, block, pad, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, true, true>), grid, block, pad, stream, sp); break;
     }
   } else if (fp8) {
     switch (Hq / Hkv) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, true>), grid, block, 0, stream, sp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, 0, stream, sp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, true>), grid, block, 0, stream, sp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, true>), grid, block, 0, stream, sp); break;
+      case 1: hipLaunchKernelGGL((split_kernel<1, true>), grid, block, pad, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, pad, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, true>), grid, block, pad, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, true>), grid, block, pad, stream, sp); break;
     }
   } else if (append) {
     switch (Hq / Hkv) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, false, true>), grid, block, 0, stream, sp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, false, true>), grid, block, 0, stream, sp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, false, true>), grid, block, 0, stream, sp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, false, true>), grid, block, 0, stream, sp); break;
+      case 1: hipLaunchKernelGGL((split_kernel<1, false, true>), grid, block, pad, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, false, true>), grid, block, pad, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, false, true>), grid, block, pad, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, false, true>), grid, block, pad, stream, sp); break;
     }
   } else {
     switch (Hq / Hkv) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, false>), grid, block, 0, stream, sp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, false>), grid, block, 0, stream, sp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, false>), grid, block, 0, stream, sp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, false>), grid, block, 0, stream, sp); break;
+      case 1: hipLaunchKernelGGL((split_kernel<1, false>), grid, block, pad, stream, sp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, false>), grid, block, pad, stream, sp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, false>), grid, block, pad, stream, sp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, false>), grid, block, pad, stream, sp); break;
     }
   }
   hipError_t e = hipGetLastError();

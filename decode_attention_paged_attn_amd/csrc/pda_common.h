@@ -24,6 +24,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// int32 in the constant address space: a load through it with a uniform
+// address is a scalar load (for tables the kernel never writes)
+typedef const int32_t __attribute__((address_space(4))) ConstI32;
 
 // ---------------------------------------------------------------------------
 // cross-lane helpers
