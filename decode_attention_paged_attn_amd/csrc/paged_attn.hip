@@ -314,85 +314,92 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
     const long long blk = raw < (unsigned long long)p.num_blocks ? (long long)raw : 0;
     return blk * block_bytes;
   };
-  // K/V are read once per call: non-temporal loads keep them from displacing
-  // the block table, q and the partials in the caches
+  // K/V are read once per call: streaming V non-temporally keeps it from
+  // displacing the block table, q and the partials in the caches
   using VRow = typename Fmt::VRow;
   constexpr int KL = Fmt::kKLoads;
   // Fused append: the segment that holds the sequence's newest token writes
   // k_new / v_new into that token's cache slot and uses them in place of what
-  // its own loads of the slot return, under the conditions of paged_kv_append
-  // (1 <= ctx <= max tokens, the frame inside the pool).  No other segment of
-  // the call reads the slot: the block lies in the sequence's last unit.
-  int kb_new = -1, slot_new = 0;
+  // its own loads of the slot returned, under the conditions of
+  // paged_kv_append (1 <= ctx <= max tokens, the frame inside the pool).  The
+  // slot lies in the segment's last block (tok_hi == ctx), which no other
+  // segment of the call reads.
+  bool append_here = false;
+  int slot_new = 0;
   if constexpr (kAppend) {
     if (p.k_new != nullptr) {
       const int ctx_b = p.ctx[b];
       if (ctx_b > 0 && ctx_b <= p.max_tokens && tok_hi == ctx_b) {
         const unsigned frame = (unsigned)p.bt[(long long)b * p.bt_stride + (ctx_b - 1) / kBS];
-        if (frame < (unsigned long long)p.num_blocks) {
-          kb_new = (ctx_b - 1 - tok_lo) / kBS;     // tok_lo is a multiple of the unit
-          slot_new = (ctx_b - 1) % kBS;
-        }
+        append_here = frame < (unsigned long long)p.num_blocks;
+        slot_new = (ctx_b - 1) % kBS;
       }
     }
   }
-  // block kbi, whose table entry is id
-  auto load_id = [&](int kbi, int id, u32x4 (&kr)[KL], VRow (&vr)[4]) {
+  // one block's K and V into registers; a load past the segment's end (its
+  // data never used) reads a single line for the whole wave
+  auto load_id = [&](int id, bool past_end, u32x4 (&kr)[KL], VRow (&vr)[4]) {
     const long long off = block_off(id);
     const char* kb = kbytes + off;
     const char* vb = vbytes + off;
+    const unsigned kl = past_end ? 0u : k_lane, vl = past_end ? 0u : v_lane;
+    // K: each instruction reads 64 of a token row's bytes and the next the
+    // rest of the same lines, so K loads are ordinary (non-temporal ones let
+    // the line go between the halves: 1.5% refetched in FP8, up to 9% slower);
+    // V loads read whole lines and stream non-temporally
 #pragma unroll
-    for (int i = 0; i < KL; ++i)
-      kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + k_lane + 64 * i));
+    for (int i = 0; i < KL; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kb + kl + 64 * i);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       vr[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const VRow*>(vb + v_lane + 4 * i * row_bytes));
-    if constexpr (kAppend) {
-      if (kbi == kb_new) {                           // uniform
-        const long long row = ((long long)b * p.Hkv + g) * kD;   // element index in k_new
-        if (t == slot_new) {
+          reinterpret_cast<const VRow*>(vb + vl + 4 * i * row_bytes));
+  };
+  auto load = [&](int kbi, u32x4 (&kr)[KL], VRow (&vr)[4]) {
+    load_id(bt_s[kbi], false, kr, vr);
+  };
+  // the newest token's rows into the last block's registers and its cache slot
+  auto append_new = [&](u32x4 (&kr)[KL], VRow (&vr)[4]) {
+    const long long off = block_off(bt_s[nblk - 1]);
+    char* kb = const_cast<char*>(kbytes) + off;
+    char* vb = const_cast<char*>(vbytes) + off;
+    const long long row = ((long long)b * p.Hkv + g) * kD;   // element index in k_new
+    if (t == slot_new) {
 #pragma unroll
-          for (int i = 0; i < KL; ++i) {
-            u32x4 x;
-            if constexpr (kFp8) {                    // elements 16c + 64i .. +15 as codes
-              const half8_t h0 = *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i);
-              const half8_t h1 =
-                  *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i + 8);
-              x = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < KL; ++i) {
+        u32x4 x;
+        if constexpr (kFp8) {                    // elements 16c + 64i .. +15 as codes
+          const half8_t h0 = *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i);
+          const half8_t h1 = *reinterpret_cast<const half8_t*>(p.k_new + row + 16 * c + 64 * i + 8);
+          x = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                x[e / 4] |= e4m3_encode(static_cast<float>(h0[e]) * p.k_inv) << (8 * (e % 4));
-                x[2 + e / 4] |= e4m3_encode(static_cast<float>(h1[e]) * p.k_inv) << (8 * (e % 4));
-              }
-            } else {
-              x = *reinterpret_cast<const u32x4*>(p.k_new + row + 8 * c + 32 * i);
-            }
-            kr[i] = x;
-            *reinterpret_cast<u32x4*>(const_cast<char*>(kb) + k_lane + 64 * i) = x;
+          for (int e = 0; e < 8; ++e) {
+            x[e / 4] |= e4m3_encode(static_cast<float>(h0[e]) * p.k_inv) << (8 * (e % 4));
+            x[2 + e / 4] |= e4m3_encode(static_cast<float>(h1[e]) * p.k_inv) << (8 * (e % 4));
           }
+        } else {
+          x = *reinterpret_cast<const u32x4*>(p.k_new + row + 8 * c + 32 * i);
         }
-        if (tg == (slot_new & 3)) {
-          VRow x;
-          if constexpr (kFp8) {                      // elements 8ds .. 8ds+7 as codes
-            const half8_t h = *reinterpret_cast<const half8_t*>(p.v_new + row + 8 * ds);
-            x = VRow{0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              x[e / 4] |= e4m3_encode(static_cast<float>(h[e]) * p.v_inv) << (8 * (e % 4));
-          } else {
-            x = *reinterpret_cast<const VRow*>(p.v_new + row + 8 * ds);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r)                // a constant index keeps vr in registers
-            if (r == (slot_new >> 2)) vr[r] = x;
-          *reinterpret_cast<VRow*>(const_cast<char*>(vb) + v_lane +
-                                   4 * (slot_new >> 2) * row_bytes) = x;
-        }
+        kr[i] = x;
+        *reinterpret_cast<u32x4*>(kb + k_lane + 64 * i) = x;
       }
     }
+    if (tg == (slot_new & 3)) {
+      VRow x;
+      if constexpr (kFp8) {                      // elements 8ds .. 8ds+7 as codes
+        const half8_t h = *reinterpret_cast<const half8_t*>(p.v_new + row + 8 * ds);
+        x = VRow{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e / 4] |= e4m3_encode(static_cast<float>(h[e]) * p.v_inv) << (8 * (e % 4));
+      } else {
+        x = *reinterpret_cast<const VRow*>(p.v_new + row + 8 * ds);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)                // a constant index keeps vr in registers
+        if (r == (slot_new >> 2)) vr[r] = x;
+      *reinterpret_cast<VRow*>(vb + v_lane + 4 * (slot_new >> 2) * row_bytes) = x;
+    }
   };
-  auto load = [&](int kbi, u32x4 (&kr)[KL], VRow (&vr)[4]) { load_id(kbi, bt_s[kbi], kr, vr); };
   auto fold = [&](const u32x4 (&kr)[KL], const VRow (&vr)[4], int kb) {
     if (kb == nblk - 1 && last_valid < kBS)
       fold_block<G, true, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, last_valid);
@@ -412,7 +419,7 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
   u32x4 kbuf[NB][KL];
   VRow vbuf[NB][4];
 #pragma unroll
-  for (int i = 0; i < NB - 1; ++i) load(min(i, nblk - 1), kbuf[i], vbuf[i]);
+  for (int i = 0; i < NB - 1; ++i) load_id(bt_s[min(i, nblk - 1)], i >= nblk, kbuf[i], vbuf[i]);
   // The main loop never holds the last block (the only one that may be
   // partial), so it folds whole blocks only.
   // Each turn reads the table entries of the next turn's loads up front, so
@@ -427,8 +434,7 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
     for (int s = 0; s < NB; ++s) next_ids[s] = bt_s[min(kb0 + NB + s + NB - 1, nblk - 1)];
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
-      const int kbi = min(kb0 + s + NB - 1, nblk - 1);
-      load_id(kbi, ids[s], kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
+      load_id(ids[s], kb0 + s + NB - 1 >= nblk, kbuf[(s + NB - 1) % NB], vbuf[(s + NB - 1) % NB]);
       fold_full(kbuf[s], vbuf[s]);
     }
 #pragma unroll
@@ -439,6 +445,8 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
   for (int s = 0; s < NB; ++s) {
     if (kb0 + s >= nblk) break;
     if (s == NB - 1) load(nblk - 1, kbuf[s], vbuf[s]);
+    if constexpr (kAppend)
+      if (append_here && kb0 + s == nblk - 1) append_new(kbuf[s], vbuf[s]);
     fold(kbuf[s], vbuf[s], kb0 + s);
   }
 
