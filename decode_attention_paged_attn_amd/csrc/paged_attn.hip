@@ -89,19 +89,24 @@ constexpr int kMaxWavesPerWG = PDA_MAX_WAVES_PER_WG;   // KV heads of one work-g
 // (1, 2 and 4 heads per work-group measured; 8 is no faster than 4)
 // Occupancy target of the split kernel, held by LDS padding when its registers
 // would allow more, and the depth of its ring of K/V register buffers (blocks
-// in flight + 1).  Measured on MI355X: fp16 runs best at 2 waves per SIMD
-// (3 are 3-4% slower) with ring 2 (3 is no faster); FP8 blocks are half the
-// bytes and run at 2 waves per SIMD with ring 4 (3 is equal, 6 slower).
+// in flight + 1).  Measured on MI355X: both run best at 2 waves per SIMD
+// (3 are 1-5% slower) with ring 3 (fp16 ring 2 0.1-1% slower; FP8 rings 4
+// and 6 0.7-2% slower).
 #ifndef PDA_WAVES_PER_EU_FP8
 #define PDA_WAVES_PER_EU_FP8 2
 #endif
 #ifndef PDA_RING_FP16
-#define PDA_RING_FP16 2
+#define PDA_RING_FP16 3
 #endif
 #ifndef PDA_RING_FP8
-#define PDA_RING_FP8 4
+#define PDA_RING_FP8 3
 #endif
-constexpr int waves_per_eu(int G, bool fp8) { return fp8 && G <= 4 ? PDA_WAVES_PER_EU_FP8 : 2; }
+#ifndef PDA_WAVES_PER_EU_FP16
+#define PDA_WAVES_PER_EU_FP16 2
+#endif
+constexpr int waves_per_eu(int G, bool fp8) {
+  return fp8 && G <= 4 ? PDA_WAVES_PER_EU_FP8 : G <= 4 ? PDA_WAVES_PER_EU_FP16 : 2;
+}
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kHdrInts = 4;           // k, U, n_runs, P, then units_before[b]
 
