@@ -112,7 +112,14 @@ def cpu_baseline(case, budget_s):
         if spent >= budget_s:
             break
     gbs = kv_bytes([tokens], case.Hkv, elem=case.kv_bytes_per_elem) / spent / 1e9
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu,
             "sample": f"{len(done)} of {case.B} sequences ({tokens} tokens, all {case.Hq} query "
                       f"heads), float64 numpy gather + two-pass softmax, {spent:.1f} s"}
 
@@ -216,6 +223,23 @@ def _time_events(step, steps, warmup):
     wall_ms = (time.perf_counter() - t0) / steps * 1e3
     ev = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     return wall_ms, sum(ev) / len(ev), ev[len(ev) // 2]
+
+
+def stream_read_ceiling(gib=4, steps=10):
+    """Read bandwidth of a plain streaming kernel (pda_stream_read) over ``gib``
+    GiB: ordinary and non-temporal 16-byte loads, the better mean by events."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"bytes": buf.numel()}
+    for name, nt in (("ordinary_GBps", False), ("nontemporal_GBps", True)):
+        _, ev_ms, _ = _time_events(lambda: pda.stream_read(buf, sink, nt), steps, 2)
+        res[name] = round(buf.numel() / (ev_ms / 1e3) / 1e9, 1)
+    res["GBps"] = max(res["ordinary_GBps"], res["nontemporal_GBps"])
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def mq_work(case):
@@ -449,6 +473,8 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read ceiling measured beside the headline")
     ap.add_argument("--also", default="llama8b_4k",
                     help="comma-separated extra workloads reported under 'also'")
     ap.add_argument("--op", default="attention",
@@ -544,6 +570,10 @@ def main():
     }
     if args.flush_mib:
         rec["flush_mib_between_steps"] = args.flush_mib
+    if not args.no_stream_read:
+        ceiling = stream_read_ceiling()
+        rec["stream_read_ceiling"] = ceiling
+        rec["frac_of_stream_read_ceiling"] = round(m["achieved"] / ceiling["GBps"], 4)
     also = {}
     for name in [x for x in args.also.split(",") if x and x != args.config]:
         del case

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     paged_kv_append,
     paged_multi_query_attn,
     paged_multi_query_attn_partial,
+    stream_read,
     workspace_layout,
     workspace_size,
 )
@@ -35,6 +36,7 @@ __all__ = [
     "paged_kv_append",
     "paged_multi_query_attn",
     "paged_multi_query_attn_partial",
+    "stream_read",
     "workspace_layout",
     "workspace_size",
 ]

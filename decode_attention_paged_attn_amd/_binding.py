@@ -83,6 +83,7 @@ _SIGNATURES = {
                                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_i64,
                                               _c_int, _c_float, _c_float, _c_float, _c_int, _vp,
                                               _vp, _c_size, _vp]),
+    "pda_stream_read": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -287,6 +288,19 @@ def paged_decode_attn_partial(q, k_cache, v_cache, block_table, context_lens, sc
     """Normalised partial (o fp32 [B, Hq, D], lse fp32 [B, Hq]) of a token range."""
     return _run(True, q, k_cache, v_cache, block_table, context_lens, scale, o, lse, True,
                 partition_tokens, workspace, max_blocks_per_seq, k_scale, v_scale)
+
+
+def stream_read(buf, sink, nontemporal=True):
+    """Diagnostic: enqueue a read of all of ``buf`` (a contiguous GPU tensor of a
+    multiple of 16 bytes) with the attention kernels' load forms; ``sink`` is a
+    one-element int32 GPU tensor that is not written in practice."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    if sink.device != buf.device or sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("sink is one 4-byte element on buf's GPU")
+    _check(load_library().pda_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                          _ptr(sink), int(bool(nontemporal)),
+                                          _stream(buf.device)))
 
 
 def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):

@@ -411,6 +411,20 @@ int paged_multi_query_attn_partial_fp8(float* o, float* lse, const void* q,
                                        int causal, int partition_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * Diagnostic, no part of the attention path: reads `bytes` (a multiple of 16)
+ * of device memory at `src` (16-byte aligned) with 16-byte loads, ordinary or
+ * (nontemporal != 0) non-temporal, the load forms of the attention kernels,
+ * enqueued on `stream`.  Timed, it gives the read bandwidth a plain streaming
+ * kernel reaches on the device: a measured ceiling to set the decode kernels'
+ * KV-read rate against, beside the HBM peak.  `sink` (one unsigned of device
+ * memory) is written only if the xor of a thread's words hits one fixed
+ * value, which no ordinary buffer does; nothing else is written.  Returns
+ * PDA_EINVAL for null pointers or a misaligned `src` or size.
+ */
+int pda_stream_read(const void* src, size_t bytes, unsigned* sink, int nontemporal,
+                    void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pda_last_error(void);
 

@@ -294,3 +294,13 @@ def test_fp8_fused_append_rejects(lib):
     assert call(kn=None) == 1
     assert call(ks=0.0) == 1
     assert call(vs=float("inf")) == 1
+
+
+def test_stream_read_rejects(lib):
+    vp = ctypes.c_void_p
+    assert lib.pda_stream_read(None, 64, vp(256), 1, None) == 1
+    assert lib.pda_stream_read(vp(256), 64, None, 1, None) == 1
+    assert lib.pda_stream_read(vp(257), 64, vp(256), 1, None) == 1     # misaligned source
+    assert lib.pda_stream_read(vp(256), 60, vp(256), 0, None) == 1     # size not a multiple of 16
+    assert b"16" in lib.pda_last_error()
+    assert lib.pda_stream_read(None, 0, None, 1, None) == 0           # nothing to read

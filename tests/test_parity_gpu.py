@@ -632,3 +632,16 @@ def test_fp8_fused_append_full_size():
     _fused_vs_separate(case, kn, vn)
     del case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes", [16, 4096, (3 << 20) + 48])
+def test_stream_read_reads_without_writing(nbytes):
+    """The diagnostic streaming read (the bench's read ceiling) runs on odd sizes
+    and leaves its sink alone: it writes nothing for an ordinary buffer."""
+    buf = torch.arange(nbytes, dtype=torch.int32, device="cuda").to(torch.uint8)
+    sink = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    for nt in (False, True):
+        pda.stream_read(buf, sink, nt)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == -5
