@@ -86,6 +86,7 @@ constexpr int kMaxKvHeads = 8;        // one wave per KV head
 #define PDA_MAX_WAVES_PER_WG 4
 #endif
 constexpr int kMaxWavesPerWG = PDA_MAX_WAVES_PER_WG;   // KV heads of one work-group
+constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a head's running max
 // (1, 2 and 4 heads per work-group measured; 8 is no faster than 4)
 // Occupancy target of the split kernel, held by LDS padding when its registers
 // would allow more, and the depth of its ring of K/V register buffers (blocks
@@ -197,23 +198,35 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
 #pragma unroll
   for (int r = 0; r < kR; ++r) s[r] = tok_valid ? sc[r] : -INFINITY;
 
-  // block max of every head (base-2 units), uniform over the wave
-  float mb[G];
+  // Lazy reference max: the running max m of a head moves only when one of
+  // its scores (base-2 units) exceeds m by more than kLazyMax, so p stays
+  // below 2^kLazyMax; only then is the exact block max taken (a DPP row
+  // reduction).  The first block always takes it (m = -inf).  Lanes of rows
+  // >= G (zero q rows) take no part.
+  float ts[kR];
+  bool over = false;
 #pragma unroll
   for (int r = 0; r < kR; ++r) {
-    const float x = row16_max(s[r]);
+    float m = st.m[r];
 #pragma unroll
-    for (int cc = 0; cc * 4 + r < G; ++cc) mb[cc * 4 + r] = uniform_f32(x, 16 * cc) * qk_scale;
+    for (int cc = 1; cc * 4 + r < G; ++cc) m = c == cc ? st.m[cc * 4 + r] : m;
+    ts[r] = s[r] * qk_scale;          // NaN for a masked token when scale' = 0: never "over"
+    over |= 4 * c + r < G && ts[r] > m + kLazyMax;
   }
-  bool grow = false;
+  if (__ballot(over) != 0) {        // uniform branch: the running max moves
+    // block max of every head (base-2 units), uniform over the wave
+    float mb[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) grow |= mb[j] > st.m[j];
-  if (grow) {                       // uniform branch: the running max moved
+    for (int r = 0; r < kR; ++r) {
+      const float x = row16_max(s[r]);
+#pragma unroll
+      for (int cc = 0; cc * 4 + r < G; ++cc) mb[cc * 4 + r] = uniform_f32(x, 16 * cc) * qk_scale;
+    }
     float alpha[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const float mn = fmaxf(st.m[j], mb[j]);
-      alpha[j] = fast_exp2(st.m[j] - mn);   // 0 on the first block (m = -inf)
+      alpha[j] = mn == st.m[j] ? 1.0f : fast_exp2(st.m[j] - mn);   // 0 on the first block
       st.m[j] = mn;
     }
 #pragma unroll
@@ -242,7 +255,7 @@ __device__ __forceinline__ void fold_block(Seg<G>& st, const half8_t (&qa)[4],
     float m = st.m[r];
 #pragma unroll
     for (int cc = 1; cc * 4 + r < G; ++cc) m = c == cc ? st.m[cc * 4 + r] : m;
-    pr[r] = fast_exp2(fmaf(s[r], qk_scale, -m));
+    pr[r] = fast_exp2(ts[r] - m);
     if (kMasked) pr[r] = tok_valid ? pr[r] : 0.0f;
     st.lp[r] += pr[r];
   }
