@@ -795,22 +795,30 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
       }
     }
   } else {
-    u32x2 v[8];
+    // Transposed LDS reads (ds_read_b64_tr_b16): in each 16-lane group, lane
+    // 4a + e receives element e of the 8-byte pieces that lanes a, a + 4,
+    // a + 8, a + 12 of the group address.  Lane a + 4b addresses dims
+    // 32u + 16 (n / 16) + 4a .. +3 of token 16c + 8r + 4hf + b, so lane n gets
+    // dim 32u + n of the four tokens k = 8hf + 4r + b: tile u covers dims
+    // 32u .. 32u + 31, column n dim 32u + n.
+    const int a = n & 3, b = (n >> 2) & 3, g16 = n >> 4;
+    typedef __fp16 fp16x4 __attribute__((vector_size(8)));    // the builtin's element type
+    typedef __attribute__((address_space(3))) fp16x4 LdsHalf4;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int tok = 16 * c + 8 * (t >> 2) + 4 * hf + (t & 3);
-      v[t] = *reinterpret_cast<const u32x2*>(vstage + tok * kRow + 8 * n);
-      if (kMasked && tok >= valid) v[t] = u32x2{0u, 0u};
-    }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int comp = u >> 1;
-      const unsigned sel = (u & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-      u32x4 x;
+      for (int r = 0; r < 2; ++r) {
+        const int tok = 16 * c + 8 * r + 4 * hf + b;
+        const char* src = vstage + tok * kRow + 2 * (32 * u + 16 * g16 + 4 * a);
+        half4_t x = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LdsHalf4*)src));
+        if (kMasked) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) x[w] = __builtin_amdgcn_perm(v[2 * w + 1][comp], v[2 * w][comp], sel);
-      vb[u] = __builtin_bit_cast(half8_t, x);
-    }
+          for (int e = 0; e < 4; ++e)   // element e came from token 16c + 8r + 4hf + e
+            if (16 * c + 8 * r + 4 * hf + e >= valid) x[e] = static_cast<_Float16>(0.0f);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vb[u][4 * r + e] = x[e];
+      }
   }
 }
 
@@ -930,7 +938,8 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[wide_n
 }
 
 // Normalise and store the wave's rows: register r of lane l holds row
-// row0 + wide_row(r, hf) at head dims 4n .. 4n+3 (tiles 0..3).
+// row0 + wide_row(r, hf) at head dims 4n .. 4n+3 (tiles 0..3) over an FP8
+// cache, and at dims n, 32 + n, 64 + n, 96 + n over an fp16 one.
 template <int G, bool kFp8>
 __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g, int q0, int nq,
                                            int row0, int lane, bool whole, int slot) {
@@ -955,6 +964,25 @@ __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g
     const f32x4 o = {st.acc[0][r] * inv, st.acc[1][r] * inv, st.acc[2][r] * inv,
                      st.acc[3][r] * inv};
     const int h = g * G + j;
+    if constexpr (!kFp8) {
+      if (whole) {
+        const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + n;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (p.out_f16)
+            static_cast<_Float16*>(p.out)[dst + 32 * u] = static_cast<_Float16>(o[u]);
+          else
+            static_cast<float*>(p.out)[dst + 32 * u] = o[u];
+        }
+        if (p.lse_out && n == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse;
+      } else {
+        const long long sl = ((long long)slot * Qt + qi) * p.Hq + h;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p.ws_o[sl * kD + 32 * u + n] = o[u];
+        if (n == 0) p.ws_lse[sl] = lse;
+      }
+      continue;
+    }
     if (whole) {
       const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 4 * n;
       if (p.out_f16) {
