@@ -225,6 +225,21 @@ def _time_events(step, steps, warmup):
     return wall_ms, sum(ev) / len(ev), ev[len(ev) // 2]
 
 
+def platform_info():
+    """Device and software versions for the record."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rocm = ""
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count, "rocm": rocm,
+            "torch": torch.__version__, "torch_hip": torch.version.hip}
+
+
 def stream_read_ceiling(gib=4, steps=10):
     """Read bandwidth of a plain streaming kernel (pda_stream_read) over ``gib``
     GiB: ordinary and non-temporal 16-byte loads, the better mean by events."""
@@ -567,6 +582,7 @@ def main():
         },
         "kernel_source_sha256_16": source_hash(),
         "inputs": input_fingerprint(case),
+        "platform": platform_info(),
     }
     if args.flush_mib:
         rec["flush_mib_between_steps"] = args.flush_mib
