@@ -658,3 +658,29 @@ def test_split_kernel_runs_at_two_waves_per_simd(fp8, G, Hkv):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     lay = pda.workspace_layout(16, G * Hkv, Hkv, 64, 0, kv_fp8=fp8)
     assert lay["n_runs"] == cus * 8 // Hkv
+
+
+@pytest.mark.parametrize("kv", ["fp16", "fp8"])
+@pytest.mark.parametrize("nblk", list(range(1, 9)))
+@pytest.mark.parametrize("last", [1, 7, 16])
+def test_every_segment_length_of_the_ring(kv, nblk, last):
+    """Sequence 0's partition is its whole context, so its single segment has
+    nblk blocks (1..8 covers the ring's prologue, whole turns and last partial
+    turn for rings of 2 to 4) and a last block with `last` valid tokens; the
+    fused append on the same shapes matches append-then-attend bit for bit."""
+    n = 16 * (nblk - 1) + last
+    lens = [n, 3 * n + 5]
+    case = W.build_case(lens, 8, 2, seed=900 + 10 * nblk + last, device="cuda", kv_dtype=kv,
+                        pool_blocks=sum(-(-x // 16) for x in lens) + 4)
+    P = 16 * nblk
+    q, k, v, table, ln = W.host_full(case)
+    out, lse = run(case, P)
+    if kv == "fp8":
+        ref, ref_lse = O.paged_decode_attention_fp8(q, k, v, table, ln, case.scale, case.k_scale,
+                                                    case.v_scale)
+    else:
+        ref, ref_lse = O.paged_decode_attention(q, k, v, table, ln, case.scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+    kn, vn = _new_rows(case, 950 + nblk)
+    _fused_vs_separate(case, kn, vn, P)
