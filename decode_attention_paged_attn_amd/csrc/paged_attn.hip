@@ -90,8 +90,9 @@ constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a head's runnin
 // (1, 2 and 4 heads per work-group measured; 8 is no faster than 4)
 // Occupancy target of the split kernel, held by LDS padding when its registers
 // would allow more, and the depth of its ring of K/V register buffers (blocks
-// in flight + 1).  Measured on MI355X: both run best at 2 waves per SIMD
-// (3 are 1-5% slower) with ring 3 (fp16 ring 2 0.1-1% slower; FP8 rings 4
+// in flight + 1).  Measured on MI355X, ring 3 for both: fp16 (G <= 4) runs
+// best at 1 wave per SIMD (0.3-1% over 2; rings 4 and 5 equal), FP8 at 2
+// (1 wave is 11% slower on the agentic batch, 3 waves 2-6% slower; rings 4
 // and 6 0.7-2% slower).
 #ifndef PDA_WAVES_PER_EU_FP8
 #define PDA_WAVES_PER_EU_FP8 2
@@ -103,7 +104,7 @@ constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a head's runnin
 #define PDA_RING_FP8 3
 #endif
 #ifndef PDA_WAVES_PER_EU_FP16
-#define PDA_WAVES_PER_EU_FP16 2
+#define PDA_WAVES_PER_EU_FP16 1
 #endif
 constexpr int waves_per_eu(int G, bool fp8) {
   return fp8 && G <= 4 ? PDA_WAVES_PER_EU_FP8 : G <= 4 ? PDA_WAVES_PER_EU_FP16 : 2;
