@@ -189,40 +189,50 @@ __device__ __forceinline__ void pv_mfma(f32x4 (&acc)[8], half4_t pa,
 // and lse = L + ln(sum_s w_s).  Partials with lse = -inf weigh nothing; if
 // every partial is empty the row is 0 with lse -inf.  One wave per row; lane
 // l returns dims 2l and 2l + 1.
-constexpr int kMergeBatch = 16;   // rows with at most this many partials: one round of loads
+// Rows with at most N partials: every load of the row in one round (the lse
+// of partial `lane` and, for each partial u < N, this lane's two dims; a slot
+// past the last re-reads the last with weight 0).
+template <int N>
+__device__ __forceinline__ void merge_row_batch(const float* o, const float* lse, long long slot0,
+                                                long long slot_step, int nseg, long long rows,
+                                                long long row, int lane, f32x2& res,
+                                                float& lse_res) {
+  const int last = max(nseg - 1, 0);
+  const float lv =
+      lane < nseg ? lse[(slot0 + (long long)lane * slot_step) * rows + row] : -INFINITY;
+  f32x2 ov[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    ov[u] = *reinterpret_cast<const f32x2*>(
+        o + ((slot0 + (long long)min(u, last) * slot_step) * rows + row) * kD + 2 * lane);
+  const float L = wave_max_f32(lv);
+  res = f32x2{0.0f, 0.0f};
+  lse_res = -INFINITY;
+  if (nseg == 0 || L == -INFINITY) return;
+  const float wl = lane < nseg ? fast_exp2((lv - L) * kLog2e) : 0.0f;
+  const float wsum = wave_sum_f32(wl);
+  f32x2 acc = {0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const float wj = uniform_f32(wl, u);
+    acc.x = fmaf(wj, ov[u].x, acc.x);
+    acc.y = fmaf(wj, ov[u].y, acc.y);
+  }
+  const float inv = 1.0f / wsum;
+  res = f32x2{acc.x * inv, acc.y * inv};
+  lse_res = L + __builtin_logf(wsum);
+}
+
 __device__ __forceinline__ void merge_row(const float* o, const float* lse, long long slot0,
                                           long long slot_step, int nseg, long long rows,
                                           long long row, int lane, f32x2& res, float& lse_res) {
-  if (nseg <= kMergeBatch) {
-    // every load of the row at once: the lse of partial `lane` and, for each
-    // partial u, this lane's two dims (a partial past the last one reads the
-    // last one again and gets weight 0)
-    const int last = max(nseg - 1, 0);
-    const float lv =
-        lane < nseg ? lse[(slot0 + (long long)lane * slot_step) * rows + row] : -INFINITY;
-    f32x2 ov[kMergeBatch];
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      ov[u] = *reinterpret_cast<const f32x2*>(
-          o + ((slot0 + (long long)min(u, last) * slot_step) * rows + row) * kD + 2 * lane);
-    const float L = wave_max_f32(lv);
-    res = f32x2{0.0f, 0.0f};
-    lse_res = -INFINITY;
-    if (nseg == 0 || L == -INFINITY) return;
-    const float wl = lane < nseg ? fast_exp2((lv - L) * kLog2e) : 0.0f;
-    const float wsum = wave_sum_f32(wl);
-    f32x2 acc = {0.0f, 0.0f};
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const float wj = uniform_f32(wl, u);
-      acc.x = fmaf(wj, ov[u].x, acc.x);
-      acc.y = fmaf(wj, ov[u].y, acc.y);
-    }
-    const float inv = 1.0f / wsum;
-    res = f32x2{acc.x * inv, acc.y * inv};
-    lse_res = L + __builtin_logf(wsum);
-    return;
-  }
+  // nseg is uniform: one round of loads sized to the row
+  if (nseg <= 4)
+    return merge_row_batch<4>(o, lse, slot0, slot_step, nseg, rows, row, lane, res, lse_res);
+  if (nseg <= 8)
+    return merge_row_batch<8>(o, lse, slot0, slot_step, nseg, rows, row, lane, res, lse_res);
+  if (nseg <= 16)
+    return merge_row_batch<16>(o, lse, slot0, slot_step, nseg, rows, row, lane, res, lse_res);
   float L = -INFINITY;
   for (int s = lane; s < nseg; s += kWave) L = fmaxf(L, lse[(slot0 + s * slot_step) * rows + row]);
   L = wave_max_f32(L);
