@@ -124,6 +124,10 @@ struct MqParams {
   // last: inserted before the pointers above, it changed the generated code of
   // the fp16 kernels (up to 30 more VGPRs and spills at 2 row blocks per wave)
   float v_scale;            // multiplies the output (FP8 V scale; 1 for fp16)
+  // the merge's view of fix tile f (16-byte aligned): first query row, queries,
+  // first partial slot, partials (0 for a tile that sees no token)
+  int32_t* t_rec;           // [tiles_max][4]
+  int tiles_max;
 };
 
 __device__ __forceinline__ int mq_seq_len(const MqParams& p, int s) {
@@ -227,7 +231,12 @@ __global__ __launch_bounds__(kWave) void mq_plan_kernel(MqParams p) {
       p.t_ntok[i] = ntok;
       p.t_ub[i] = ub;
       p.t_rank[i] = cut ? rincl - 1 : -1;
-      if (fix) p.t_fix[fincl - 1] = i;
+      if (fix) {
+        p.t_fix[fincl - 1] = i;
+        const int nseg = nu > 0 ? (ub + nu - 1) / k - ub / k + 1 : 0;
+        const int slot0 = nu > 0 ? ub / k + rincl - 1 : 0;    // a listed tile with nu > 0 is cut
+        *reinterpret_cast<int4*>(p.t_rec + 4 * (fincl - 1)) = int4{q0, nq, slot0, nseg};
+      }
     }
     ucarry = __builtin_amdgcn_readlane(incl, kWave - 1);
     rcarry = __builtin_amdgcn_readlane(rincl, kWave - 1);
@@ -1159,27 +1168,19 @@ template <int Qt>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4], n_fix = p.hdr[5];
   // rows of a tile: Qt * Hq = (16 << variant) * Hkv, a multiple of kMergeRows
   const long long rows = (long long)Qt * p.Hq;
   const long long groups = rows / kMergeRows;
-  const long long total = (long long)n_fix * groups;
-  for (long long idx = (long long)blockIdx.x * 4 + wave; idx < total;
-       idx += (long long)gridDim.x * 4) {
-    const int f = (int)(idx / groups);
+  const int n_fix = p.hdr[5];
+  for (long long idx = (long long)blockIdx.x * 4 + wave;; idx += (long long)gridDim.x * 4) {
+    const int f = (int)min(idx / groups, (long long)p.tiles_max - 1);
     const long long row0 = (idx % groups) * kMergeRows;
-    const int i = p.t_fix[f];
-    const int nq = p.t_nq[i];
+    // read with the header, before the bound is known (the index is clamped)
+    const int4 rec = *reinterpret_cast<const int4*>(p.t_rec + 4 * f);
+    if (idx >= (long long)n_fix * groups) break;
+    const int q0 = rec.x, nq = rec.y, nseg = rec.w;
+    const long long slot0 = rec.z;
     if (row0 / p.Hq >= nq) continue;                 // every row past the tile's queries
-    const int ub = p.t_ub[i];
-    const int nu = (i + 1 < n_tiles ? p.t_ub[i + 1] : U) - ub;
-    int nseg = 0;
-    long long slot0 = 0;
-    if (nu > 0) {
-      const int w0 = ub / k, w1 = (ub + nu - 1) / k;
-      nseg = w1 - w0 + 1;
-      slot0 = (long long)w0 + p.t_rank[i];
-    }
     f32x2 res[kMergeRows];
     float lse_res[kMergeRows];
     if (nseg <= kSmallSeg) {
@@ -1194,14 +1195,14 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
       const long long row = row0 + r;
       const int qi = (int)(row / p.Hq), h = (int)(row % p.Hq);
       if (qi >= nq) continue;
-      const long long dst = ((long long)(p.t_q0[i] + qi) * p.Hq + h) * kD + 2 * lane;
+      const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 2 * lane;
       if (p.out_f16) {
         half2_t hv = {static_cast<_Float16>(res[r].x), static_cast<_Float16>(res[r].y)};
         *reinterpret_cast<half2_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
       } else {
         *reinterpret_cast<f32x2*>(static_cast<float*>(p.out) + dst) = res[r];
       }
-      if (p.lse_out && lane == 0) p.lse_out[(long long)(p.t_q0[i] + qi) * p.Hq + h] = lse_res[r];
+      if (p.lse_out && lane == 0) p.lse_out[(long long)(q0 + qi) * p.Hq + h] = lse_res[r];
     }
   }
 }
@@ -1307,7 +1308,8 @@ int mq_run_count(int G, int variant, int Hkv, bool fp8) {
 
 struct MqPlan {
   int variant = 0, Qt = 0, P = 0, n_runs = 0, hg = 0, max_tokens = 0, tiles_max = 0, n_slots = 0;
-  size_t hdr_offset = 0, tiles_offset = 0, lse_offset = 0, o_offset = 0, total = 0;
+  size_t hdr_offset = 0, tiles_offset = 0, rec_offset = 0, lse_offset = 0, o_offset = 0,
+         total = 0;
 };
 
 int mq_check(int S, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
@@ -1353,8 +1355,9 @@ MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition
   pl.n_slots = 2 * pl.n_runs;
   pl.hdr_offset = 0;
   pl.tiles_offset = align256(sizeof(int32_t) * kMqHdrInts);
-  pl.lse_offset =
+  pl.rec_offset =
       pl.tiles_offset + align256(sizeof(int32_t) * (size_t)kMqTileArrays * pl.tiles_max);
+  pl.lse_offset = pl.rec_offset + align256(sizeof(int32_t) * 4 * (size_t)pl.tiles_max);
   pl.o_offset = pl.lse_offset + align256(sizeof(float) * (size_t)pl.n_slots * pl.Qt * Hq);
   pl.total = pl.o_offset + align256(sizeof(float) * (size_t)pl.n_slots * pl.Qt * Hq * kD);
   return pl;
@@ -1472,6 +1475,8 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
   mp.t_ub = tiles + 5 * (size_t)pl.tiles_max;
   mp.t_rank = tiles + 6 * (size_t)pl.tiles_max;
   mp.t_fix = tiles + 7 * (size_t)pl.tiles_max;
+  mp.t_rec = reinterpret_cast<int32_t*>(ws + pl.rec_offset);
+  mp.tiles_max = pl.tiles_max;
   mp.ws_o = reinterpret_cast<float*>(ws + pl.o_offset);
   mp.ws_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   mp.out = out;
