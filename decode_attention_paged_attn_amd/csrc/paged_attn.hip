@@ -429,20 +429,20 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
     fold_block<G, false, kFp8>(st, qa, kr, vr, lds_p, p.qk_scale, lane, kBS);
   };
 
-  // a ring of NB register buffers: blocks kb+1 .. kb+NB-1 are in flight while
-  // block kb is folded.  The loop runs whole turns of the ring with no exit
-  // inside, and every step issues its loads (past the last block, the last
-  // block again): with the same loads on every path, the wait before a fold
-  // covers that block's loads only, not the ones behind it.
+  // A ring of NB register buffers (block kb in buffer kb % NB): blocks kb+1 ..
+  // kb+NB-1 are in flight while block kb is folded.  The main loop runs whole
+  // turns of the ring with no exit inside, and every step issues its loads (a
+  // step past the last block reads one line of it for the whole wave): with
+  // the same loads on every path, the wait before a fold covers that block's
+  // loads only, not the ones behind it.  The main loop never holds the last
+  // block, the only one that may be partial, so it folds whole blocks only;
+  // each turn reads the table entries of the next turn's loads up front, so no
+  // load waits on its id.
   constexpr int NB = kFp8 ? PDA_RING_FP8 : PDA_RING_FP16;
   u32x4 kbuf[NB][KL];
   VRow vbuf[NB][4];
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i) load_id(bt_s[min(i, nblk - 1)], i >= nblk, kbuf[i], vbuf[i]);
-  // The main loop never holds the last block (the only one that may be
-  // partial), so it folds whole blocks only.
-  // Each turn reads the table entries of the next turn's loads up front, so
-  // no load waits on its id.
   int kb0 = 0;
   int ids[NB];
 #pragma unroll
