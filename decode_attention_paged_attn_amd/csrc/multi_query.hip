@@ -731,13 +731,27 @@ void mq_shared_kernel(MqParams p) {
 //     8 tokens and builds the operand of tile u from element u of each.
 
 constexpr int kWideRows = 32;         // query rows per wave
-// 32-token sub-steps per step: two for FP8 (half the staging registers per
-// token, so twice the tokens fit; chunked prefill 0.84 -> 0.75 ms), one for
-// fp16 (two spill)
+// 32-token sub-steps per staged step (one barrier each): two (one for fp16
+// spilled while fp16 was staged through registers)
 template <bool kFp8>
-constexpr int wide_ns() { return kFp8 ? 2 : 1; }
+constexpr int wide_ns() { return 2; }
+// 32-token sub-steps per online-softmax update: two for FP8 (chunked prefill
+// 0.84 -> 0.75 ms against one), one for fp16 (two spill)
+template <bool kFp8>
+constexpr int wide_fold_ns() { return kFp8 ? 2 : 1; }
 template <bool kFp8>
 constexpr int wide_step() { return 2 * kBS * wide_ns<kFp8>(); }   // tokens per step
+// A wide-kernel stage holds whole token rows of one KV head, 256 bytes fp16
+// and 128 FP8, unpadded (the layout the direct global-to-LDS loads write):
+// 16-byte chunk c of row t sits in slot c ^ (t mod chunks per row), so the rows
+// an operand load reads at once fall on distinct banks.
+template <bool kFp8>
+constexpr int wide_row_bytes() { return kD * KvFmt<kFp8>::kElemBytes; }
+template <bool kFp8>
+__device__ __forceinline__ int wide_at(int t, int c) {
+  constexpr int kChunks = wide_row_bytes<kFp8>() / 16;
+  return t * wide_row_bytes<kFp8>() + 16 * (c ^ (t & (kChunks - 1)));
+}
 
 __device__ __forceinline__ int wide_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
@@ -773,7 +787,6 @@ __device__ __forceinline__ void wide_load_q(const MqParams& p, int g, int q0, in
 template <bool kMasked, bool kFp8>
 __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int hf, int n,
                                                 int valid, half8_t (&vb)[4]) {
-  constexpr int kRow = lds_row<kFp8>();
   if constexpr (kFp8) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -781,7 +794,7 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * c + 8 * jj + 4 * hf + i;
-        w[i] = *reinterpret_cast<const unsigned*>(vstage + tok * kRow + 4 * n);
+        w[i] = *reinterpret_cast<const unsigned*>(vstage + wide_at<true>(tok, n >> 2) + 4 * (n & 3));
         if (kMasked && tok >= valid) w[i] = 0u;                      // code 0 = +0
       }
       // 4x4 byte transpose: col[u] = byte u (dim 4n + u) of the 4 tokens
@@ -818,7 +831,7 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int tok = 16 * c + 8 * r + 4 * hf + b;
-        const char* src = vstage + tok * kRow + 2 * (32 * u + 16 * g16 + 4 * a);
+        const char* src = vstage + wide_at<false>(tok, 4 * u + 2 * g16 + (a >> 1)) + 8 * (a & 1);
         half4_t x = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LdsHalf4*)src));
         if (kMasked) {
 #pragma unroll
@@ -835,16 +848,14 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
 // against the query rows held as B operands.
 template <bool kFp8>
 __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* kstage, int lane) {
-  constexpr int kRow = lds_row<kFp8>();
   const int n = lane & 31, hf = lane >> 5;
   f32x16 sc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
-  const char* krow = kstage + n * kRow + 64 * hf * KvFmt<kFp8>::kElemBytes;
   if constexpr (kFp8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(krow + 16 * j);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kstage + wide_at<true>(n, 4 * hf + j));
       half8_t kop[2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -861,7 +872,8 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
   } else {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const half8_t kop = *reinterpret_cast<const half8_t*>(krow + 16 * kk);
+      const half8_t kop =
+          *reinterpret_cast<const half8_t*>(kstage + wide_at<false>(n, 8 * hf + kk));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qb[kk], sc, 0, 0, 0);
     }
   }
@@ -873,13 +885,12 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
 // row row0 + n (query qi of the tile) sees tokens before min(base + qi, n_seq,
 // tok_hi) when causal, before tok_hi otherwise; rows past the tile's queries
 // see everything and are never stored.
-template <int G, bool kMasked, bool kFp8>
-__device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[wide_ns<kFp8>()],
+template <int G, bool kMasked, bool kFp8, int kNS>
+__device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
                                           const char* vstage, float qk_scale, int lane, int row0,
                                           int t0, int causal_base, int n_seq, int nq,
                                           int tok_hi) {
-  constexpr int kNS = wide_ns<kFp8>();
-  constexpr int kRow = lds_row<kFp8>();
+  constexpr int kRow = wide_row_bytes<kFp8>();
   const int n = lane & 31, hf = lane >> 5;
   float sv[kNS][16];
   if (kMasked) {
@@ -1011,16 +1022,17 @@ __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g
 }
 
 template <int G, bool kFp8>
-__device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int lane, int wave,
-                                                int g, int i, int tok_lo, int tok_hi, bool whole,
-                                                int slot) {
-  using Chunk = typename KvFmt<kFp8>::VRow;         // 8 elements: 16 bytes fp16, 8 bytes FP8
+__device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (&stage)[2][2],
+                                                int lane, int wave, int g, int i, int tok_lo,
+                                                int tok_hi, bool whole, int slot) {
   constexpr int E = KvFmt<kFp8>::kElemBytes;
-  constexpr int kRow = lds_row<kFp8>();
+  constexpr int kRow = wide_row_bytes<kFp8>();
   constexpr int kNS = wide_ns<kFp8>();
   constexpr int kStepTok = wide_step<kFp8>();
-  constexpr int kHalf = kStepTok * kRow;            // the K (or V) rows of one stage
-  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
+  const int s = __builtin_amdgcn_readfirstlane(p.t_seq[i]);
+  const int q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
+  tok_lo = __builtin_amdgcn_readfirstlane(tok_lo);
+  tok_hi = __builtin_amdgcn_readfirstlane(tok_hi);
   const int n_seq = mq_seq_len(p, s);
   const int row0 = wave * kWideRows;
   const bool idle = row0 / G >= nq;                 // none of the tile's queries (uniform)
@@ -1029,19 +1041,14 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
   const int causal_base = p.causal ? base : kNoMask;
   const int full_end = p.causal ? min(min(max(base + row0 / G, 0), n_seq), tok_hi) : tok_hi;
 
-  // thread (wave, lane) moves 8 elements of K and of V of each block: token
-  // tid / 16 of the block, elements 8 * (tid % 16) of the row of KV head g
-  const int tid = wave * kWave + lane;
-  const int ltok = tid >> 4, lchunk = tid & 15;
   const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);
-  const unsigned g_off = (unsigned)((ltok * p.Hkv + g) * kD * E + 8 * E * lchunk);
-  const int s_off = ltok * kRow + 8 * E * lchunk;
   const char* kbytes = reinterpret_cast<const char*>(p.k);
   const char* vbytes = reinterpret_cast<const char*>(p.v);
   const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
   const int nstep = (nblk + 2 * kNS - 1) / (2 * kNS);
-  BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
-                  (long long)kBS * row_bytes);
+  // block ids by scalar loads (the table is not written while the kernel runs)
+  ConstI32* bt_s = (ConstI32*)(p.bt + (long long)s * p.bt_stride + tok_lo / kBS);
+  const long long block_bytes = (long long)kBS * row_bytes;
 
   WideSeg st;
   st.m = -INFINITY;
@@ -1051,52 +1058,78 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[u][r] = 0.0f;
 
-  // Two LDS stages, one barrier per step; each thread holds the next step's
-  // K/V in registers while the step before it is folded.
-  Chunk rk[2][2 * kNS], rv[2][2 * kNS];
-  // blocks in increasing order (the window advances by 64 blocks)
-  auto fetch = [&](int step, Chunk (&k2)[2 * kNS], Chunk (&v2)[2 * kNS]) {
+  // the step's sub-steps, kFS at a time; a group wholly past tok_hi would
+  // add exact zeros and is skipped
+  constexpr int kFS = wide_fold_ns<kFp8>();
+  auto fold_step = [&](int cur, const char* kstage, const char* vstage) {
 #pragma unroll
-    for (int b = 0; b < 2 * kNS; ++b)
-      if (2 * kNS * step + b < nblk) {
-        const long long off = win.offset(2 * kNS * step + b);
-        k2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(kbytes + off + g_off);
-        v2[b] = kv_load<PDA_MQ_NT_STAGE != 0, Chunk>(vbytes + off + g_off);
-      }
+    for (int j0 = 0; j0 < kNS; j0 += kFS) {
+      const int t0 = tok_lo + cur * kStepTok + 32 * j0;
+      if (j0 > 0 && t0 >= tok_hi) break;
+      f32x16 sc[kFS];
+#pragma unroll
+      for (int j = 0; j < kFS; ++j)
+        sc[j] = wide_qk<kFp8>(qb, kstage + 32 * (j0 + j) * kRow, lane);
+      const char* vs = vstage + 32 * j0 * kRow;
+      if (t0 + 32 * kFS > full_end)
+        wide_tail<G, true, kFp8, kFS>(st, sc, vs, p.qk_scale, lane, row0, t0, causal_base, n_seq,
+                                      nq, tok_hi);
+      else
+        wide_tail<G, false, kFp8, kFS>(st, sc, vs, p.qk_scale, lane, row0, t0, causal_base,
+                                       n_seq, nq, tok_hi);
+    }
   };
-  fetch(0, rk[0], rv[0]);
-  for (int s0 = 0; s0 < nstep; s0 += 2) {
+  // Direct global-to-LDS staging (global_load_lds_dwordx4, probed on the
+  // device: lane l's 16 bytes land at the wave's LDS base + 16 l).  A step's
+  // K (or V) rows are kLoads pieces of 1024 bytes, kR rows each; wave w moves
+  // pieces w, w + 4, ..., lane l slot l % kC of row l / kC of its piece, so it
+  // fetches chunk (l % kC) ^ row of that token.  The loads of step cur + 1 go
+  // out right after the barrier of step cur into the other stage (last read
+  // in step cur - 1, which every wave has finished); each wave waits for its
+  // own before the next barrier.  Blocks past the segment's end are not
+  // loaded: their stale rows lie past tok_hi, where the softmax masks them and
+  // their V rows are selected to zero.  The two stages are separate LDS
+  // arrays and the step loop is unrolled by two, so that the compiler can
+  // tell a step's operand reads from the loads in flight into the other stage
+  // and puts no wait for those before them.
+  typedef __attribute__((address_space(3))) void LdsVoid;
+  typedef const __attribute__((address_space(1))) void GlobalVoid;
+  constexpr int kC = kRow / 16;                     // 16-byte chunks per row
+  constexpr int kR = kWave / kC;                    // rows per piece
+  constexpr int kLoads = kStepTok / kR / kMqWaves;  // pieces per wave, K and V each
+  static_assert(kBS % kR == 0 && (kStepTok / kR) % kMqWaves == 0 && (kMqWaves * kR) % kBS == 0,
+                "piece mapping");
+  const int trow = (wave * kR) % kBS + lane / kC;   // row within its block, every piece
+  const unsigned src_off =
+      (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ (trow % kC)));
+  auto issue = [&](int step, char* kst, char* vst) {
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int cur = s0 + sl;
-      if (cur >= nstep) break;
-      if (cur + 1 < nstep) fetch(cur + 1, rk[sl ^ 1], rv[sl ^ 1]);
-      // stage the step; every wave finished the step that last used this
-      // stage before the previous barrier.  Blocks past the segment's end
-      // leave stale rows, which lie past tok_hi: the softmax masks them and
-      // their V rows are selected to zero.
-      char* kstage = kv + sl * 2 * kHalf;
-      char* vstage = kstage + kHalf;
-#pragma unroll
-      for (int bb = 0; bb < 2 * kNS; ++bb)
-        if (2 * kNS * cur + bb < nblk) {
-          *reinterpret_cast<Chunk*>(kstage + bb * kBS * kRow + s_off) = rk[sl][bb];
-          *reinterpret_cast<Chunk*>(vstage + bb * kBS * kRow + s_off) = rv[sl][bb];
-        }
-      __syncthreads();
-      if (!idle) {
-        f32x16 sc[kNS];
-#pragma unroll
-        for (int j = 0; j < kNS; ++j) sc[j] = wide_qk<kFp8>(qb, kstage + 32 * j * kRow, lane);
-        const int t0 = tok_lo + cur * kStepTok;
-        if (t0 + kStepTok > full_end)
-          wide_tail<G, true, kFp8>(st, sc, vstage, p.qk_scale, lane, row0, t0, causal_base, n_seq,
-                                   nq, tok_hi);
-        else
-          wide_tail<G, false, kFp8>(st, sc, vstage, p.qk_scale, lane, row0, t0, causal_base,
-                                    n_seq, nq, tok_hi);
+    for (int l = 0; l < kLoads; ++l) {
+      const int piece = wave + kMqWaves * l;
+      const int b = 2 * kNS * step + piece * kR / kBS;
+      if (b < nblk) {
+        const unsigned raw = (unsigned)bt_s[b];
+        const long long off = (raw < (unsigned long long)p.num_blocks ? (long long)raw : 0) * block_bytes;
+        __builtin_amdgcn_global_load_lds((GlobalVoid*)(kbytes + off + src_off),
+                                         (LdsVoid*)(kst + piece * kWave * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((GlobalVoid*)(vbytes + off + src_off),
+                                         (LdsVoid*)(vst + piece * kWave * 16), 16, 0, 0);
       }
     }
+  };
+  // one step: wait for this wave's loads of it, then for every wave's; send
+  // the next step's loads into the other stage; fold this one
+  auto step = [&](int cur, char* kst, char* vst, char* knext, char* vnext) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (cur + 1 < nstep) issue(cur + 1, knext, vnext);
+    if (!idle) fold_step(cur, kst, vst);
+  };
+  issue(0, stage[0][0], stage[0][1]);
+  for (int cur = 0; cur < nstep; cur += 2) {
+    step(cur, stage[0][0], stage[0][1], stage[1][0], stage[1][1]);
+    if (cur + 1 >= nstep) break;
+    step(cur + 1, stage[1][0], stage[1][1], stage[0][0], stage[0][1]);
   }
   __syncthreads();                                  // the stages are free for the next segment
   if (!idle) wide_store<G, kFp8>(p, st, g, q0, nq, row0, lane, whole, slot);
@@ -1105,13 +1138,16 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* kv, int
 template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_wide_kernel(MqParams p) {
-  __shared__ __attribute__((aligned(16))) char kv[2 * 2 * wide_step<kFp8>() * lds_row<kFp8>()];   // 2 stages
+  // two stages of K and V rows, each its own array
+  constexpr int kHalf = wide_step<kFp8>() * wide_row_bytes<kFp8>();
+  __shared__ __attribute__((aligned(16))) char k0[kHalf], v0[kHalf], k1[kHalf], v1[kHalf];
+  char* const stage[2][2] = {{k0, v0}, {k1, v1}};
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
   const int g = blockIdx.x % p.Hkv;                 // KV head
   for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_wide_segment<G, kFp8>(p, kv, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+    mq_wide_segment<G, kFp8>(p, stage, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
