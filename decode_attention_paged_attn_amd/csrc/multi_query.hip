@@ -75,6 +75,9 @@ constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a row's referen
 #ifndef PDA_MQ_NT_REG
 #define PDA_MQ_NT_REG 1
 #endif
+#ifndef PDA_WIDE_REVERSE
+#define PDA_WIDE_REVERSE 1
+#endif
 #ifndef PDA_MQ_NT_STAGE
 #define PDA_MQ_NT_STAGE 0
 #endif
@@ -252,29 +255,42 @@ __global__ __launch_bounds__(kWave) void mq_plan_kernel(MqParams p) {
   }
 }
 
-// The segments of run w, in order: (tile i, tokens [tok_lo, tok_hi), whole
-// tile?, partial slot).  Uniform over the work-group.
-template <typename F>
+// The tile holding unit u: the last tile whose first unit is <= u.
+__device__ __forceinline__ int tile_of_unit(const MqParams& p, int u, int n_tiles) {
+  int lo = 0, hi = n_tiles - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.t_ub[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The segments of run w: (tile i, tokens [tok_lo, tok_hi), whole tile?,
+// partial slot), in tile order, or last tile first when kReverse.  Uniform over
+// the work-group.  Last tile first, a run that covers about one tile starts at
+// token 0 of its later tile and reaches the end of the earlier one about when
+// the other runs of the sequence reach theirs, so the runs resident together
+// read the same K/V blocks at about the same time.
+template <bool kReverse = false, typename F>
 __device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& fn) {
   const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4];
   const int u_lo = w * k;
   const int u_hi = min(u_lo + k, U);
   if (u_lo >= u_hi || n_tiles <= 0) return;
-  // the tile holding unit u_lo: the last tile whose first unit is <= u_lo
-  int lo = 0, hi = n_tiles - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.t_ub[mid] <= u_lo) lo = mid; else hi = mid - 1;
-  }
-  int u = u_lo;
-  for (int i = lo; i < n_tiles && u < u_hi; ++i) {
+  auto segment = [&](int i) {
     const int before = p.t_ub[i];
     const int nu = (i + 1 < n_tiles ? p.t_ub[i + 1] : U) - before;
-    const int p_lo = u - before;
+    const int p_lo = max(u_lo - before, 0);
     const int p_hi = min(u_hi - before, nu);
-    if (p_hi <= p_lo) continue;
-    fn(i, p_lo * p.P, min(p_hi * p.P, p.t_ntok[i]), p_lo == 0 && p_hi == nu, w + p.t_rank[i]);
-    u = before + p_hi;
+    if (p_hi > p_lo)
+      fn(i, p_lo * p.P, min(p_hi * p.P, p.t_ntok[i]), p_lo == 0 && p_hi == nu, w + p.t_rank[i]);
+  };
+  const int first = tile_of_unit(p, u_lo, n_tiles);
+  if constexpr (kReverse) {
+    const int last = tile_of_unit(p, u_hi - 1, n_tiles);
+    for (int i = last; i >= first; --i) segment(i);
+  } else {
+    for (int i = first; i < n_tiles && p.t_ub[i] < u_hi; ++i) segment(i);
   }
 }
 
@@ -1146,7 +1162,8 @@ void mq_wide_kernel(MqParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
   const int g = blockIdx.x % p.Hkv;                 // KV head
-  for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
+  for_each_segment<PDA_WIDE_REVERSE != 0>(p, w, [&](int i, int tok_lo, int tok_hi, bool whole,
+                                                     int slot) {
     mq_wide_segment<G, kFp8>(p, stage, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
