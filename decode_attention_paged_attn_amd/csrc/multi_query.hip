@@ -758,15 +758,36 @@ constexpr int wide_fold_ns() { return kFp8 ? 2 : 1; }
 template <bool kFp8>
 constexpr int wide_step() { return 2 * kBS * wide_ns<kFp8>(); }   // tokens per step
 // A wide-kernel stage holds whole token rows of one KV head, 256 bytes fp16
-// and 128 FP8, unpadded (the layout the direct global-to-LDS loads write):
-// 16-byte chunk c of row t sits in slot c ^ (t mod chunks per row), so the rows
-// an operand load reads at once fall on distinct banks.
+// and 128 FP8, unpadded (the layout the direct global-to-LDS loads write).
+// Token t sits in row slot wide_prow(t), and its 16-byte chunk c in chunk slot
+// c ^ wide_swz(row slot), chosen so that the operand reads find their bytes in
+// distinct banks of the 64 x 4-byte LDS (zero bank-conflict cycles counted):
+//  - fp16 K (ds_read_b128, 16 lanes a cycle: one chunk of 16 rows): the swizzle
+//    is a bijection of the row's low 4 bits;
+//  - fp16 V (ds_read_b64_tr_b16, 32 lanes a cycle: chunks 4u .. 4u+3 of 4
+//    consecutive rows): the swizzle's bits 2-3 take 4 values over the 4 rows
+//    (swapping the row's 2-bit halves does both; row ^ chunk put the 4 rows on
+//    the same banks: chunked prefill 0.699 -> 0.672 ms);
+//  - FP8 V (ds_read_b32, 64 lanes: whole rows t and t + 4) needs the two rows
+//    in different 128-byte halves of the banks, so rows 4..7 of each 8 trade
+//    places in pairs; FP8 K (16 lanes: one chunk of 16 rows) then needs the
+//    chunk swizzle to be a bijection over the row slots of either parity.
 template <bool kFp8>
 constexpr int wide_row_bytes() { return kD * KvFmt<kFp8>::kElemBytes; }
 template <bool kFp8>
+__device__ __forceinline__ int wide_prow(int t) {       // an involution
+  if constexpr (kFp8) return t ^ ((t >> 2) & 1);
+  return t;
+}
+template <bool kFp8>
+__device__ __forceinline__ int wide_swz(int pr) {
+  if constexpr (kFp8) return (pr >> 1) & 7;
+  return ((pr & 3) << 2) | ((pr >> 2) & 3);
+}
+template <bool kFp8>
 __device__ __forceinline__ int wide_at(int t, int c) {
-  constexpr int kChunks = wide_row_bytes<kFp8>() / 16;
-  return t * wide_row_bytes<kFp8>() + 16 * (c ^ (t & (kChunks - 1)));
+  const int pr = wide_prow<kFp8>(t);
+  return pr * wide_row_bytes<kFp8>() + 16 * (c ^ wide_swz<kFp8>(pr));
 }
 
 __device__ __forceinline__ int wide_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
@@ -1097,9 +1118,10 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
   };
   // Direct global-to-LDS staging (global_load_lds_dwordx4, probed on the
   // device: lane l's 16 bytes land at the wave's LDS base + 16 l).  A step's
-  // K (or V) rows are kLoads pieces of 1024 bytes, kR rows each; wave w moves
-  // pieces w, w + 4, ..., lane l slot l % kC of row l / kC of its piece, so it
-  // fetches chunk (l % kC) ^ row of that token.  The loads of step cur + 1 go
+  // K (or V) rows are kLoads pieces of 1024 bytes, kR row slots each; wave w
+  // moves pieces w, w + 4, ..., lane l chunk slot l % kC of row slot l / kC of
+  // its piece, so it fetches chunk (l % kC) ^ wide_swz(row slot) of the token
+  // wide_prow(row slot).  The loads of step cur + 1 go
   // out right after the barrier of step cur into the other stage (last read
   // in step cur - 1, which every wave has finished); each wave waits for its
   // own before the next barrier.  Blocks past the segment's end are not
@@ -1115,9 +1137,10 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
   constexpr int kLoads = kStepTok / kR / kMqWaves;  // pieces per wave, K and V each
   static_assert(kBS % kR == 0 && (kStepTok / kR) % kMqWaves == 0 && (kMqWaves * kR) % kBS == 0,
                 "piece mapping");
-  const int trow = (wave * kR) % kBS + lane / kC;   // row within its block, every piece
+  const int prow = (wave * kR) % kBS + lane / kC;   // row slot within its block, every piece
+  const int trow = wide_prow<kFp8>(prow);           // the token it holds
   const unsigned src_off =
-      (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ (trow % kC)));
+      (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ wide_swz<kFp8>(prow)));
   auto issue = [&](int step, char* kst, char* vst) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
