@@ -130,6 +130,27 @@ def test_queries_past_context_and_empty():
     compare_lse(l, ref_lse)
 
 
+# One long sequence makes the runs of the wide kernel long (tens of units), so
+# a run sweeps across many short tiles, some with no token to see (context 0,
+# or every query before the first cached token), and a run's segments are
+# visited last tile first: cut tiles with several partials, empty tiles and
+# whole tiles all in one call.
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_runs_across_many_tiles(kv_dtype, causal):
+    rng = np.random.default_rng(7)
+    short = [int(x) for x in rng.integers(1, 90, size=29)]
+    lens = [60000] + short[:10] + [0] + short[10:20] + [3] + short[20:]
+    nq = [40] * len(lens)                                  # 160 rows per sequence at G = 4
+    case = W.build_mq_case(lens, nq, 8, 2, causal=causal, seed=91, device="cuda",
+                           name=f"mq_wide_many_tiles_{kv_dtype}", kv_dtype=kv_dtype)
+    ref, ref_lse = oracle_mq(case)
+    for P in (0, 64):
+        out, lse = run_mq(case, P)
+        compare_out(to_np(out), ref)
+        compare_lse(to_np(lse), ref_lse)
+
+
 @pytest.mark.parametrize("P", [0, 64])
 def test_partial_entry_point(P):
     case = W.build_mq_case(SMALL_LENS, SMALL_NQ, 16, 4, causal=True, seed=43, device="cuda",
