@@ -747,10 +747,12 @@ void mq_shared_kernel(MqParams p) {
 //     8 tokens and builds the operand of tile u from element u of each.
 
 constexpr int kWideRows = 32;         // query rows per wave
-// 32-token sub-steps per staged step (one barrier each): two (one for fp16
-// spilled while fp16 was staged through registers)
+// 32-token sub-steps per staged step (one barrier per step): four over FP8
+// (its 128-token stages fit two work-groups per CU: chunked prefill 0.658 ->
+// 0.653 ms, cascade 183 -> 178 us against two), two over fp16 (four would not
+// fit; two spilled while its K/V went through registers)
 template <bool kFp8>
-constexpr int wide_ns() { return 2; }
+constexpr int wide_ns() { return kFp8 ? 4 : 2; }
 // 32-token sub-steps per online-softmax update: two for FP8 (chunked prefill
 // 0.84 -> 0.75 ms against one), one for fp16 (two spill)
 template <bool kFp8>
