@@ -171,22 +171,28 @@ def measure(case, P, steps, warmup, flush_mib=0):
                               case.context_lens, case.scale, out=out, lse_out=lse,
                               partition_tokens=P, workspace=ws, **kw)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    _warm(step, warmup)
+    # the timed pass: ``steps`` calls back to back, nothing else in the stream
+    # but the optional cache flush
     t0 = time.perf_counter()
     for i in range(steps):
         if scratch is not None:
             scratch.fill_(i & 0xFF)      # evicts K/V from the last-level cache between calls
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-call durations for the roofline: a second pass, each call bracketed
+    # by HIP events on the stream it is launched on
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     ev_mean = sum(ev_ms) / len(ev_ms)
     nbytes = kv_bytes(case.lens, Hkv, elem=case.kv_bytes_per_elem)
@@ -204,23 +210,44 @@ def measure(case, P, steps, warmup, flush_mib=0):
     }
 
 
-def _time_events(step, steps, warmup):
-    """Mean ms per step: wall clock and HIP events on torch's current stream."""
+MIN_WARM_S = 0.2
+
+
+def _warm(step, warmup):
+    """``warmup`` untimed calls, then more until MIN_WARM_S of them have run: a
+    GPU left idle (the CPU baseline runs seconds) needs that long to be back at
+    its working clock, far longer than a few calls of a 100-us workload."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < MIN_WARM_S:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
+def _time_events(step, steps, warmup):
+    """Mean ms per step: the wall clock of ``steps`` back-to-back calls, then the
+    per-call durations of a second pass of ``steps`` calls, each bracketed by HIP
+    events on torch's current stream (the events stay out of the wall-clock pass:
+    recorded around every call they cost a short call up to 9% of its rate)."""
+    import torch
+    _warm(step, warmup)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / steps * 1e3
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) / steps * 1e3
     ev = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     return wall_ms, sum(ev) / len(ev), ev[len(ev) // 2]
 
@@ -319,7 +346,7 @@ def bench_multi_query(case, P, steps, warmup):
         "kv_bytes_unique": nbytes, "flops": flops,
         "tflops": round(flops / (ev_ms / 1e3) / 1e12, 2),
         "kv_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
-        "roofline": roof, "steps": steps, "warmup": warmup, "dtype": case.kv_dtype,
+        "roofline": roof, "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": case.kv_dtype,
         "data": "synthetic", "kernel_source_sha256_16": source_hash("multi_query"),
         "config": {"workload": case.name, "sequences": case.S, "query_tokens": case.T,
                    "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 128,
@@ -373,7 +400,7 @@ def bench_cascade(case, steps, warmup):
                      "frac": round(unique_tok * row / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "cascade call (prefix pass + suffix pass + merge)",
                      "traffic": measured_traffic(f"cascade:{case.name}", "cascade")},
-        "steps": steps, "warmup": warmup, "dtype": case.kv_dtype, "data": "synthetic",
+        "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": case.kv_dtype, "data": "synthetic",
         "config": {"workload": case.name, "requests": B, "kv_dtype": case.kv_dtype,
                    "groups": len(case.prefix_lens_host),
                    "prefix_tokens": [int(x) for x in case.prefix_lens_host],
@@ -423,7 +450,7 @@ def bench_partial_merge(case, steps, warmup):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": "R partial calls + merge_partials", "traffic": None},
-        "steps": steps, "warmup": warmup, "dtype": "fp16", "data": "synthetic",
+        "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": "fp16", "data": "synthetic",
         "config": {"workload": case.name, "batch": B, "q_heads": Hq, "kv_heads": case.Hkv,
                    "head_dim": 128, "ranges": R, "tokens_per_sequence": int(case.lens[0]),
                    "kv_bytes_per_step": nbytes}}), flush=True)
@@ -483,7 +510,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="agentic_80k")
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -541,6 +568,11 @@ def main():
     if args.op == "append":
         bench_append(case, args.steps, args.warmup)
         return
+    # the extra workloads get their memory now, while it is fresh: built after
+    # the headline's pools were freed, a workload measured 4% slower than in a
+    # process of its own
+    also_cases = [W.CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)
+                  for name in [x for x in args.also.split(",") if x and x != args.config]]
     P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
     m = measure(case, P, args.steps, args.warmup, args.flush_mib)
     nbytes = m["kv_bytes"]
@@ -553,6 +585,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "min_warm_s": MIN_WARM_S,
         "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -591,21 +624,16 @@ def main():
         rec["stream_read_ceiling"] = ceiling
         rec["frac_of_stream_read_ceiling"] = round(m["achieved"] / ceiling["GBps"], 4)
     also = {}
-    for name in [x for x in args.also.split(",") if x and x != args.config]:
-        del case
-        torch.cuda.empty_cache()
-        case = W.CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)
-        mm = measure(case, case.partition_tokens, args.steps, args.warmup, args.flush_mib)
-        also[case.name] = {"value": mm["value"], "unit": "GB/s",
+    for acase in also_cases:
+        mm = measure(acase, acase.partition_tokens, args.steps, args.warmup, args.flush_mib)
+        also[acase.name] = {"value": mm["value"], "unit": "GB/s",
                            "pct_hbm_peak": round(100.0 * mm["value"] / HBM_PEAK_GBS, 2),
                            "event_GBps": mm["achieved"], "ms_per_step": mm["ms_per_step"],
                            "decode_attn_tokens_per_s": mm["tokens_per_s"],
                            "kv_bytes_per_step": mm["kv_bytes"]}
     if also:
         rec["also"] = also
-        del case
-        torch.cuda.empty_cache()
-        case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
+    del also_cases
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(rec), flush=True)
