@@ -271,11 +271,10 @@ __device__ __forceinline__ int tile_of_unit(const MqParams& p, int u, int n_tile
 // token 0 of its later tile and reaches the end of the earlier one about when
 // the other runs of the sequence reach theirs, so the runs resident together
 // read the same K/V blocks at about the same time.
-template <bool kReverse = false, typename F>
-__device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& fn) {
-  const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4];
-  const int u_lo = w * k;
-  const int u_hi = min(u_lo + k, U);
+template <bool kReverse, typename F>
+__device__ __forceinline__ void for_each_segment_in(const MqParams& p, int w, int u_lo, int u_hi,
+                                                    F&& fn) {
+  const int U = p.hdr[1], n_tiles = p.hdr[4];
   if (u_lo >= u_hi || n_tiles <= 0) return;
   auto segment = [&](int i) {
     const int before = p.t_ub[i];
@@ -292,6 +291,12 @@ __device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& f
   } else {
     for (int i = first; i < n_tiles && p.t_ub[i] < u_hi; ++i) segment(i);
   }
+}
+template <bool kReverse = false, typename F>
+__device__ __forceinline__ void for_each_segment(const MqParams& p, int w, F&& fn) {
+  const int k = p.hdr[0], U = p.hdr[1];
+  const int u_lo = w * k;
+  for_each_segment_in<kReverse>(p, w, u_lo, min(u_lo + k, U), fn);
 }
 
 // ---------------------------------------------------------------------------
@@ -553,7 +558,7 @@ struct BlockWindow {
 
 template <int G, int NT, bool kFp8>
 __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
-                               bool whole, int slot) {
+                               bool whole, int slot, MqSeg<NT>& st, bool defer) {
   using Fmt = KvFmt<kFp8>;
   using VRow = typename Fmt::VRow;
   constexpr int E = Fmt::kElemBytes;
@@ -577,7 +582,6 @@ __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int 
   BlockWindow win(p.bt + (long long)s * p.bt_stride + tok_lo / kBS, nblk, lane, p.num_blocks,
                   (long long)kBS * row_bytes);
 
-  MqSeg<NT> st;
   mq_seg_init(st);
   auto load = [&](long long off, u32x4 (&kr)[KL], VRow (&vr)[4]) {
 #pragma unroll
@@ -609,20 +613,81 @@ __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int 
                                     causal_base, n, nq, tok_hi);
     }
   }
-  mq_store<G, NT, Qt, kFp8>(p, st, g, q0, nq, 0, lane, whole, slot);
+  if (!defer) mq_store<G, NT, Qt, kFp8>(p, st, g, q0, nq, 0, lane, whole, slot);
 }
 
+// One work-group per (run, group of hg KV heads) with two waves per KV head:
+// wave (half, head) folds half `half` of the run's units, the first half in
+// tile order and the second last tile first, so the tile holding the split
+// (if the split falls inside one) is the last each of the two folds.  The
+// second writes its state (max, sum, accumulators) to LDS, and after the one
+// barrier the first rescales both to the common max, adds them and stores the
+// tile's segment of the whole run: a run twice as long at the same occupancy,
+// half the partials to write and merge.
 template <int G, int NT, bool kFp8>
-__global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(2 * kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_reg_kernel(MqParams p) {
+  constexpr int kState = NT * (2 + 32);                  // floats per lane
+  __shared__ float xs[kMqWaves][kState][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int n_hgroups = p.Hkv / p.hg;
+  const int hg = p.hg;
+  const int half = wave >= hg ? 1 : 0;
+  const int gl = wave - half * hg;
+  const int n_hgroups = p.Hkv / hg;
   const int w = blockIdx.x / n_hgroups;                  // run of the unit stream
-  const int g = (blockIdx.x % n_hgroups) * p.hg + wave;  // KV head
-  for_each_segment(p, w, [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
-    mq_reg_segment<G, NT, kFp8>(p, lane, g, i, tok_lo, tok_hi, whole, slot);
-  });
+  const int g = (blockIdx.x % n_hgroups) * hg + gl;      // KV head
+  const int k = p.hdr[0], U = p.hdr[1], n_tiles = p.hdr[4];
+  const int u_lo = w * k, u_hi = min(u_lo + k, U);
+  const int mid = u_lo + max(u_hi - u_lo + 1, 0) / 2;
+  int shared_tile = -1;                                  // uniform over the work-group
+  if (n_tiles > 0 && u_lo < mid && mid < u_hi) {
+    const int i0 = tile_of_unit(p, mid - 1, n_tiles);
+    if (i0 == tile_of_unit(p, mid, n_tiles)) shared_tile = i0;
+  }
+  MqSeg<NT> st;
+  auto seg = [&](int i, int tok_lo, int tok_hi, bool whole, int slot) {
+    mq_reg_segment<G, NT, kFp8>(p, lane, g, i, tok_lo, tok_hi, whole, slot, st, i == shared_tile);
+  };
+  if (half == 0) for_each_segment_in<false>(p, w, u_lo, mid, seg);
+  else for_each_segment_in<true>(p, w, mid, u_hi, seg);
+  if (shared_tile >= 0 && half == 1) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      xs[gl][b][lane] = st.m[b];
+      xs[gl][NT + b][lane] = st.lp[b];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[gl][2 * NT + 32 * b + 4 * u + r][lane] = st.acc[b][u][r];
+    }
+  }
+  __syncthreads();
+  if (shared_tile >= 0 && half == 0) {
+    const int c = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const float mb = xs[gl][b][lane];
+      const float m = fmaxf(st.m[b], mb);
+      const float aa = st.m[b] == m ? 1.0f : fast_exp2(st.m[b] - m);   // 0 for an empty side
+      const float ab = mb == m ? 1.0f : fast_exp2(mb - m);
+      st.lp[b] = st.lp[b] * aa + xs[gl][NT + b][lane] * ab;
+      st.m[b] = m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(aa, 4 * c + r, kWave), br = __shfl(ab, 4 * c + r, kWave);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          st.acc[b][u][r] = st.acc[b][u][r] * ar + xs[gl][2 * NT + 32 * b + 4 * u + r][lane] * br;
+      }
+    }
+    const int i = shared_tile;
+    const int before = p.t_ub[i];
+    const int nu = (i + 1 < n_tiles ? p.t_ub[i + 1] : U) - before;
+    const bool whole = u_lo <= before && u_hi >= before + nu;
+    constexpr int Qt = 16 * NT / G;
+    mq_store<G, NT, Qt, kFp8>(p, st, g, p.t_q0[i], p.t_nq[i], 0, lane, whole, w + p.t_rank[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1308,7 +1373,7 @@ constexpr int kMqVariants = 4;
 struct MqDeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMqVariants][2][kMqWaves + 1] = {};   // [log2 G][variant][fp8][waves]
+  int wg_per_cu[4][kMqVariants][2][2 * kMqWaves + 1] = {};   // [log2 G][variant][fp8][waves]
 };
 MqDeviceFacts g_mq_dev[kMaxDevices];
 
@@ -1371,7 +1436,8 @@ bool mq_is_shared(int variant) { return variant >= 2; }
 // Runs of the unit stream: as many work-groups as fit on all CUs at once,
 // divided by the work-groups one run has (its head groups, or its KV heads).
 int mq_run_count(int G, int variant, int Hkv, bool fp8) {
-  const int waves = mq_is_shared(variant) ? kMqWaves : mq_head_group(Hkv);
+  // register kernel: two waves per KV head of its head group
+  const int waves = mq_is_shared(variant) ? kMqWaves : 2 * mq_head_group(Hkv);
   const int per_run = mq_is_shared(variant) ? Hkv : Hkv / mq_head_group(Hkv);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024 / per_run;
@@ -1385,7 +1451,7 @@ int mq_run_count(int G, int variant, int Hkv, bool fp8) {
     for (int lg = 0; lg < 4; ++lg)
       for (int v = 0; v < kMqVariants; ++v)
         for (int f8 = 0; f8 < 2; ++f8)
-          for (int w = 1; w <= kMqWaves; ++w) {
+          for (int w = 1; w <= 2 * kMqWaves; ++w) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                     &n, mq_kernel_ptr(1 << lg, v, f8 != 0), w * kWave, 0) != hipSuccess ||
@@ -1482,7 +1548,7 @@ void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((mq_reg_kernel<G, V + 1, kFp8>),
                        dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
-                       dim3((unsigned)(pl.hg * kWave)), 0, stream, mp);
+                       dim3((unsigned)(2 * pl.hg * kWave)), 0, stream, mp);
   }
   mq_launch_aux<Qt>(false, mp, pl, stream);
 }
