@@ -29,9 +29,10 @@
 //
 // Three tile kernels, picked by the average query rows per sequence:
 //   * register kernel (up to 32 rows): one work-group per (run, group of up to
-//     4 KV heads), one wave per KV head, a tile of one or two 16-row blocks per
-//     wave; each wave streams its own K/V through a ring of register buffers,
-//     as the decode kernel does;
+//     4 KV heads), two waves per KV head (each half of the run, combined in LDS
+//     at the end), a tile of one or two 16-row blocks per wave; each wave
+//     streams its own K/V through a ring of register buffers, as the decode
+//     kernel does;
 //   * shared kernel (up to 64 rows): one work-group of 4 waves per (run, KV
 //     head) and a 64-row tile, 16 rows per wave; the 256 threads load each
 //     16-token block of K and V once (16 bytes of each per thread, a few blocks
@@ -554,7 +555,8 @@ struct BlockWindow {
 };
 
 // ---------------------------------------------------------------------------
-// register kernel: one wave per KV head, one 16-row tile per wave
+// register kernel: two waves per KV head (halves of the run), a tile of one
+// or two 16-row blocks per wave
 
 template <int G, int NT, bool kFp8>
 __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
