@@ -61,7 +61,6 @@ __all__ = [
     "merge_partials",
     "partition_ranges",
     "split_k_partials",
-    "balanced_segments",
     "kv_append",
     "fp8_e4m3_value",
     "fp8_e4m3_decode",
@@ -69,7 +68,6 @@ __all__ = [
     "kv_append_fp8",
     "paged_decode_attention_fp8",
     "kv_cache_bytes",
-    "kv_read_bytes",
 ]
 
 
@@ -233,40 +231,6 @@ def partition_ranges(n_tokens, partition_tokens):
     return [(p * P, min((p + 1) * P, n)) for p in range(-(-n // P))]
 
 
-def balanced_segments(context_lens, unit_tokens, n_runs):
-    """The token ranges of each run of the unit stream.
-
-    Each sequence's tokens are cut into units of ``unit_tokens`` tokens (the
-    last one shorter); the units of all sequences in order form one stream of
-    U units, and run w is units [w*k, (w+1)*k) with
-    k = ceil(U / n_runs).  Returns, in stream order, one
-    (w, b, tok_lo, tok_hi) per sequence b that run w touches: a
-    contiguous range of that sequence's tokens.
-
-    This is a reading, not a page's formula: the pages only fix that the KV of
-    a sequence is cut into contiguous token ranges computed independently and
-    merged afterwards (KernelFlume paper §3.1, §3.2); sizing the cut so every
-    work-group gets the same number of units is the plainest way to keep a
-    whole GPU busy for any mix of lengths.
-    """
-    P = int(unit_tokens)
-    nu = [-(-int(n) // P) for n in context_lens]
-    U = sum(nu)
-    if U == 0:
-        return []
-    k = -(-U // int(n_runs))
-    before = [sum(nu[:b]) for b in range(len(nu))]
-    out = []
-    for w in range(int(n_runs)):
-        u_lo, u_hi = w * k, min((w + 1) * k, U)
-        for b, n in enumerate(context_lens):
-            lo = max(u_lo, before[b]) - before[b]
-            hi = min(u_hi, before[b] + nu[b]) - before[b]
-            if hi > lo:
-                out.append((w, b, lo * P, min(hi * P, int(n))))
-    return out
-
-
 def split_k_partials(q, k_pool, v_pool, block_table, context_lens, scale,
                      partition_tokens, block_size=16):
     """Per-partition partials of every (sequence, query head).
@@ -419,19 +383,3 @@ def kv_cache_bytes(seq_lens, n_kv_heads, head_dim, n_layers, bytes_per_elem=2):
     """
     return sum(2 * int(s) * n_kv_heads * head_dim * n_layers * bytes_per_elem
                for s in seq_lens)
-
-
-def kv_read_bytes(context_lens, n_kv_heads, head_dim, bytes_per_elem=2):
-    """Bytes of K and V one decode-attention call must read for one layer.
-
-    Only valid tokens count: sum_b ctx_b * 2 * H_kv * D * bytes.  Scanning C
-    bytes takes about C / BW_HBM (KernelFlume paper §4.2), which is what the
-    KV-read bandwidth metric divides by.
-    """
-    return kv_cache_bytes(context_lens, n_kv_heads, head_dim, 1, bytes_per_elem)
-
-
-def fp16_round(x):
-    """Round float64 values to fp16, nearest-even (the output precision)."""
-    return np.asarray(x, dtype=np.float64).astype(np.float16)
-

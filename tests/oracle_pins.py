@@ -342,34 +342,6 @@ def pin_poison_not_read(O):
     assert np.all(np.isfinite(o1)) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def pin_balanced_segments(O):
-    rng = np.random.default_rng(22)
-    for trial in range(30):
-        lens = [int(x) for x in rng.integers(0, 300, size=int(rng.integers(1, 9)))]
-        P = int(rng.choice([16, 32, 64]))
-        n_wg = int(rng.integers(1, 12))
-        segs = O.balanced_segments(lens, P, n_wg)
-        nu = [-(-n // P) for n in lens]
-        k = -(-sum(nu) // n_wg) if sum(nu) else 0
-        per_wg = {}
-        for w, b, lo, hi in segs:
-            assert 0 <= w < n_wg and 0 <= lo < hi <= lens[b]
-            assert lo % P == 0
-            per_wg[w] = per_wg.get(w, 0) + -(-hi // P) - lo // P
-        assert all(v <= k for v in per_wg.values())
-        # every sequence is tiled exactly, in order, by the ranges of increasing w
-        for b, n in enumerate(lens):
-            mine = [(w, lo, hi) for w, bb, lo, hi in segs if bb == b]
-            assert [x[0] for x in mine] == sorted(x[0] for x in mine)
-            pos = 0
-            for _, lo, hi in mine:
-                assert lo == pos
-                pos = hi
-            assert pos == n
-    # a worked case: lengths 40 and 8 with 16-token units give 3 + 1 units; 2 groups take 2 each
-    assert O.balanced_segments([40, 8], 16, 2) == [(0, 0, 0, 32), (1, 0, 32, 40), (1, 1, 0, 8)]
-
-
 def pin_kv_append(O):
     ex = _golden("paged_layout_example.json")
     row = [blk["physical_frame"] for blk in ex["logical_blocks"]]
@@ -543,7 +515,6 @@ ALL_PINS = [
     pin_merge_equals_full,
     pin_merge_page_equations,
     pin_partitions,
-    pin_balanced_segments,
     pin_poison_not_read,
     pin_kv_append,
     pin_fp8_decode,

@@ -1,9 +1,8 @@
 """Multi-query and cascade attention on the GPU against the float64 oracle.
 
 Every call goes through the C ABI (ctypes binding).  Small cases are checked
-in full; the full-size workloads on sampled queries, which the oracle
-computes one by one from its definition, in the launch configuration the
-benchmark times.
+in full, and so are the full-size workloads (every query row, every request), in
+the launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -334,78 +333,36 @@ def test_cascade_equals_naive_decode():
     compare_out(to_np(naive), ref)
 
 
-# --- full-size workloads, sampled ------------------------------------------------
-
-def sampled_mq_oracle(case, picks):
-    """Oracle rows for (sequence, query index) picks, from the sequence's own blocks."""
-    Hq, Hkv = case.Hq, case.Hkv
-    G = Hq // Hkv
-    qs = case.query_start.cpu().numpy()
-    res = []
-    for s, i in picks:
-        n = int(case.lens[s])
-        nq = int(case.n_queries[s])
-        vis = MQ.visible_tokens(n, nq, i, case.causal)
-        nb = -(-vis // 16)
-        idx = torch.tensor([int(x) for x in case.block_table_host[s, :nb]], dtype=torch.int64,
-                           device=case.k_cache.device)
-        kp, vp = host_kv(case, case.k_cache.index_select(0, idx),
-                         case.v_cache.index_select(0, idx))
-        qrow = case.q[int(qs[s]) + i].cpu().numpy()
-        o = np.zeros((Hq, 128))
-        l = np.zeros(Hq)
-        for g in range(Hkv):
-            K = O._gather_sequence_blocks(kp, np.arange(nb), vis, g, 16)
-            V = O._gather_sequence_blocks(vp, np.arange(nb), vis, g, 16)
-            o[g * G:(g + 1) * G], l[g * G:(g + 1) * G] = O.attend(qrow[g * G:(g + 1) * G], K, V,
-                                                                 case.scale)
-        res.append((int(qs[s]) + i, o, l))
-    return res
-
+# --- full-size workloads, every row --------------------------------------------
 
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
 @pytest.mark.parametrize("config", ["spec_verify", "chunked_prefill"])
-def test_full_size_sampled(config, kv_dtype):
+def test_full_size_every_row(config, kv_dtype):
+    """Every query row of the full-size workload against the oracle."""
     case = W.MQ_CONFIGS[config](device="cuda", kv_dtype=kv_dtype)
     out, lse = run_mq(case)
-    rng = np.random.default_rng(51)
-    picks = []
-    for s in range(case.S):
-        nq = int(case.n_queries[s])
-        cand = sorted({0, nq - 1, *rng.integers(0, nq, size=3).tolist()})
-        picks += [(s, int(i)) for i in cand][:5 if config == "chunked_prefill" else 2]
-    if config == "spec_verify":
-        picks = picks[:24]
     o, l = to_np(out), to_np(lse)
-    for row, ref, ref_l in sampled_mq_oracle(case, picks):
-        compare_out(o[row], ref, what=f"row {row}")
-        compare_lse(l[row], ref_l, what=f"lse row {row}")
     assert np.all(np.isfinite(o))
+    ref, ref_lse = oracle_mq(case)
+    _say(f"[oracle] {case.name}: {case.T} query rows")
+    compare_out(o, ref, what=case.name)
+    compare_lse(l, ref_lse, what=case.name)
     del case
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
-def test_full_size_cascade_sampled(kv_dtype):
+def test_full_size_cascade_every_request(kv_dtype):
+    """All 200 requests of the shared-prefix workload against the oracle's
+    attention over each request's prefix followed by its suffix."""
     c = W.shared_prefix(device="cuda", kv_dtype=kv_dtype)
     out, lse = run_cascade(c)
     o, l = to_np(out), to_np(lse)
     assert np.all(np.isfinite(o))
-    rng = np.random.default_rng(52)
-    gs = c.group_start_host
-    for b in sorted({0, c.B - 1, *rng.integers(0, c.B, size=6).tolist()}):
-        r = int(np.searchsorted(gs, b, side="right") - 1)
-        pl, sl = int(c.prefix_lens_host[r]), int(c.suffix_lens_host[b])
-        frames = (list(c.prefix_table_host[r, :-(-pl // 16)]) +
-                  list(c.suffix_table_host[b, :-(-sl // 16)]))
-        idx = torch.tensor([int(x) for x in frames], dtype=torch.int64, device="cuda")
-        kp, vp = host_kv(c, c.k_cache.index_select(0, idx), c.v_cache.index_select(0, idx))
-        npb = -(-pl // 16)
-        ref, ref_l = MQ.cascade_attention(
-            c.q[b:b + 1].cpu().numpy(), kp, vp, np.arange(npb)[None], [pl], [0, 1],
-            np.arange(npb, len(frames))[None], [sl], c.scale)
-        compare_out(o[b:b + 1], ref, what=f"request {b}")
-        compare_lse(l[b:b + 1], ref_l, what=f"lse request {b}")
+    ref, ref_lse = MQ.cascade_attention(*host_cascade(c), c.scale)
+    _say(f"[oracle] {c.name}: {c.B} requests")
+    compare_out(o, ref, what=c.name)
+    compare_lse(l, ref_lse, what=c.name)
     del c
     torch.cuda.empty_cache()
 
@@ -421,11 +378,9 @@ def test_most_sequences_per_call():
     out, lse = run_mq(case)
     o, l = to_np(out), to_np(lse)
     assert np.all(np.isfinite(o))
-    seqs = [s for s in rng.choice(S, size=40, replace=False) if nq[s] > 0]
-    picks = [(int(s), int(i)) for s in seqs for i in range(int(nq[s]))]
-    for row, ref, ref_l in sampled_mq_oracle(case, picks):
-        compare_out(o[row], ref, what=f"row {row}")
-        compare_lse(l[row], ref_l, what=f"lse row {row}")
+    ref, ref_lse = oracle_mq(case)
+    compare_out(o, ref, what="4000 sequences")
+    compare_lse(l, ref_lse, what="4000 sequences")
 
 
 def test_binding_rejects_bad_buffers_before_a_launch():

@@ -22,7 +22,6 @@ _gather_blocks = O._gather_sequence_blocks
 _merge = O.merge_partials
 _ranges = O.partition_ranges
 _token_location = O.token_location
-_segments = O.balanced_segments
 _append = O.kv_append
 _fp8 = O.fp8_e4m3_value
 _fp8_encode = O.fp8_e4m3_encode
@@ -76,9 +75,6 @@ MUTANTS = {
                            if K.shape[0] > 1 else _attend(q, K, V, scale)),
     "merge_wrong_sign": ("merge_partials", _merge_wrong_sign),
     "merge_unnormalised": ("merge_partials", _merge_unnormalised),
-    "segments_skip_last_unit": ("balanced_segments",
-                                lambda lens, P, n: [(w, b, lo, hi - P if hi - lo > P else hi)
-                                                    for w, b, lo, hi in _segments(lens, P, n)]),
     "append_one_slot_late": ("kv_append",
                              lambda k, v, kn, vn, bt, lens, bs=16: _append(
                                  k, v, kn, vn, bt, [n + 1 if 0 < n and n % bs else n for n in lens],

@@ -1,9 +1,9 @@
 """HIP path against the float64 oracle, element by element, on seeded inputs.
 
 Every call goes through the C ABI (ctypes binding).  Small cases are checked in
-full; the full-size workloads are checked on sampled sequences, which the
-oracle computes one at a time, in the launch configuration the benchmark
-times.
+full; the full-size workloads too, every sequence, which the oracle computes
+one at a time from a host copy of its own blocks, in the launch configuration
+the benchmark times.
 """
 import math
 import os
@@ -16,6 +16,7 @@ import torch
 import decode_attention_paged_attn_amd as pda
 from decode_attention_paged_attn_amd import workloads as W
 import oracle.paged_attention as O
+from tests.schedule import workspace_segments
 from tests.parity import (ROW_REL_TOL, compare_lse, compare_out, compare_ulps, p_rounding_bound,
                           to_np)
 
@@ -171,7 +172,7 @@ def test_split_partials_in_workspace(P):
     o_ws = raw[lay["o_offset"]:lay["o_offset"] + 4 * nsl * Hq * 128].view(torch.float32)
     l_ws = l_ws.reshape(nsl, Hq).numpy()
     o_ws = o_ws.reshape(nsl, Hq, 128).numpy()
-    segs = O.balanced_segments(lens, lay["unit_tokens"], lay["n_runs"])
+    segs = workspace_segments(lens, lay["unit_tokens"], lay["n_runs"])
     nu = [-(-n // lay["unit_tokens"]) for n in lens]
     assert hdr[1] == sum(nu) and hdr[2] == lay["n_runs"] and hdr[3] == lay["unit_tokens"]
     assert list(hdr[4:]) == [sum(nu[:b]) for b in range(case.B)]
@@ -272,52 +273,68 @@ def test_graph_capture_replays_match_eager():
         _ = (case.q.float() * 2).sum().item()    # eager work between replays
 
 
-# --- full-size workloads, sampled sequences ------------------------------------
+# --- full-size workloads, every sequence ---------------------------------------
 
-def _check_sampled(case, out, lse, seq_ids):
-    q, k, v, table, lens = W.host_sequences(case, seq_ids)
-    ref, ref_lse = oracle_of(case, q, k, v, table, lens)
-    o, l = to_np(out), to_np(lse)
-    for i, b in enumerate(seq_ids):
-        compare_out(o[b], ref[i], what=f"{case.name} seq {b} (ctx {lens[i]})")
-        compare_lse(l[b], ref_lse[i], what=f"{case.name} seq {b}")
+def _check_every_sequence(case, results, chunk_tokens=1 << 18):
+    """Each (label, out, lse) over the whole batch against the oracle, on every
+    sequence.  The oracle reads host copies of the blocks of a few sequences at
+    a time (up to ``chunk_tokens`` tokens, or one longer sequence), so host
+    memory stays bounded whatever the batch."""
+    got = [(label, to_np(o), to_np(l)) for label, o, l in results]
+    b0, done = 0, 0
+    while b0 < case.B:
+        b1, tok = b0 + 1, int(case.lens[b0])
+        while b1 < case.B and tok + int(case.lens[b1]) <= chunk_tokens:
+            tok += int(case.lens[b1])
+            b1 += 1
+        ids = list(range(b0, b1))
+        q, k, v, table, lens = W.host_sequences(case, ids)
+        ref, ref_lse = oracle_of(case, q, k, v, table, lens)
+        for label, o, l in got:
+            compare_out(o[b0:b1], ref, what=f"{case.name} {label} seqs {b0}..{b1 - 1}")
+            compare_lse(l[b0:b1], ref_lse, what=f"{case.name} {label} seqs {b0}..{b1 - 1}")
+        del q, k, v
+        b0 = b1
+        if b0 - done >= 32 or b0 == case.B:
+            done = b0
+            _say(f"[oracle] {case.name}: {b0} of {case.B} sequences checked")
 
 
-def _sample(lens, rng, k=2):
-    order = np.argsort(lens, kind="stable")
-    pick = {int(order[0]), int(order[-1])}
-    pick.update(int(x) for x in rng.choice(len(lens), size=k, replace=False))
-    return sorted(pick)
-
-
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
 @pytest.mark.parametrize("name,P", [("llama8b_4k", 0), ("agentic_80k", 512), ("agentic_80k", 0),
                                     ("ragged_mixed", 0)])
-def test_full_size_workload(name, P):
-    case = W.CONFIGS[name](device="cuda")
+def test_full_size_workload(name, P, kv_dtype):
+    case = W.CONFIGS[name](device="cuda", kv_dtype=kv_dtype)
     out, lse = run(case, P)
     assert torch.isfinite(out.float()).all()
-    ids = _sample(case.lens, np.random.default_rng(0))
-    _check_sampled(case, out, lse, ids)
     # a rerun is bitwise identical
     out2, lse2 = run(case, P)
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    del out2, lse2
+    _check_every_sequence(case, [(f"P={P}", out, lse)])
     del case
     torch.cuda.empty_cache()
 
 
-def test_full_size_partial_merge():
-    case = W.disagg_merge(device="cuda")
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+def test_full_size_partial_merge(kv_dtype):
+    """32 sequences of 128K tokens as 4 range partials + merge_partials, and the
+    single pass over the whole sequences: both against the oracle on every
+    sequence, and against each other to fp16 ulps."""
+    case = W.disagg_merge(device="cuda", kv_dtype=kv_dtype)
     views = W.range_views(case, case.ranges)
     o_parts = torch.empty((case.ranges, case.B, case.Hq, 128), dtype=torch.float32, device="cuda")
     l_parts = torch.empty((case.ranges, case.B, case.Hq), dtype=torch.float32, device="cuda")
     for r, (bt, ln) in enumerate(views):
         _say(f"[run] {case.name} range {r}")
         pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln, case.scale,
-                                      o=o_parts[r], lse=l_parts[r])
+                                      o=o_parts[r], lse=l_parts[r], **case.attn_kwargs())
     merged, mlse = pda.merge_partials(o_parts, l_parts)
     single, slse = run(case)
     compare_ulps(to_np(merged), to_np(single), ulps=2, rowwise=True)
-    _check_sampled(case, merged, mlse, [0, 17, 31])
+    del o_parts, l_parts
+    _check_every_sequence(case, [("4 partials + merge", merged, mlse),
+                                 ("single pass", single, slse)])
     del case
     torch.cuda.empty_cache()
 
@@ -363,7 +380,7 @@ def test_kv_append_full_size():
     rows = [i for i in range(0, case.num_blocks, 97) if i not in touched]
     assert torch.equal(case.k_cache[rows], before[[r // 97 for r in rows]])
     out, lse = run(case)
-    _check_sampled(case, out, lse, [0, 31, 63])
+    _check_every_sequence(case, [("after append", out, lse)])
     del case
     torch.cuda.empty_cache()
 
@@ -414,16 +431,6 @@ def test_fp8_every_code_decodes_exactly():
     for b in range(4):
         for h in range(32):
             assert np.array_equal(out[b, h].cpu().numpy(), want[b, h // 4]), (b, h)
-
-
-@pytest.mark.parametrize("name,P", [("llama8b_4k", 0), ("agentic_80k", 512), ("ragged_mixed", 0)])
-def test_fp8_full_size_workload(name, P):
-    case = W.CONFIGS[name](device="cuda", kv_dtype="fp8")
-    out, lse = run(case, P)
-    assert torch.isfinite(out.float()).all()
-    _check_sampled(case, out, lse, _sample(case.lens, np.random.default_rng(1)))
-    del case
-    torch.cuda.empty_cache()
 
 
 def test_fp8_partial_api_and_merge():
@@ -480,8 +487,7 @@ def test_many_sequences():
     o, l = to_np(out), to_np(lse)
     empty = np.flatnonzero(case.lens == 0)
     assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
-    ids = sorted(set(_sample(case.lens, np.random.default_rng(3), k=8)) | {int(empty[1])})
-    _check_sampled(case, out, lse, ids)
+    _check_every_sequence(case, [("b8192", out, lse)])
     del case
     torch.cuda.empty_cache()
 
