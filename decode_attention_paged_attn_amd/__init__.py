@@ -8,6 +8,7 @@ built the calls raise; there is no fallback.
 from ._binding import (  # noqa: F401
     PdaError,
     cascade_decode_attn,
+    decode_workspace_size,
     library_path,
     load_library,
     merge_partials,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "PdaError",
     "cascade_decode_attn",
+    "decode_workspace_size",
     "library_path",
     "load_library",
     "merge_partials",

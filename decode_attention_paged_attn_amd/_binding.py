@@ -39,6 +39,8 @@ class PdaLayout(ctypes.Structure):
 _SIGNATURES = {
     "pda_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.POINTER(_c_size)]),
+    "paged_decode_attn_workspace_size": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                  ctypes.POINTER(_c_size)]),
     "pda_workspace_layout": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_int, ctypes.POINTER(PdaLayout)]),
     "paged_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
@@ -151,6 +153,17 @@ def workspace_size(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DI
                                                  partition_tokens, ctypes.byref(c)))
         n = _ws_cache[key] = int(c.value)
     return n
+
+
+def decode_workspace_size(B, Hq, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,
+                          block_size=BLOCK_SIZE):
+    """Bytes of decode workspace for any supported KV-head count of Hq query heads
+    (paged_decode_attn_workspace_size), on the current device."""
+    c = _c_size(0)
+    _check(load_library().paged_decode_attn_workspace_size(B, Hq, D, block_size,
+                                                           max_blocks_per_seq, partition_tokens,
+                                                           ctypes.byref(c)))
+    return int(c.value)
 
 
 def workspace_layout(B, Hq, Hkv, max_blocks_per_seq, partition_tokens=0, D=HEAD_DIM,

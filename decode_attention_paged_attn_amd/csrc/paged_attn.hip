@@ -1090,6 +1090,30 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size, int max_bl
   return ok();
 }
 
+int paged_decode_attn_workspace_size(int B, int Hq, int D, int block_size,
+                                     int max_blocks_per_seq, int partition_tokens,
+                                     size_t* bytes) {
+  if (!bytes) return fail(PDA_EINVAL, "bytes is null");
+  if (Hq <= 0) return fail(PDA_EINVAL, "Hq must be > 0 (got %d)", Hq);
+  // the largest need over every KV-head count the call may come with; if no
+  // count is accepted, the last one's error stands
+  size_t need = 0;
+  int rc = PDA_EINVAL;
+  bool any = false;
+  for (int Hkv = 1; Hkv <= Hq; ++Hkv) {
+    if (Hq % Hkv != 0) continue;
+    size_t n = 0;
+    rc = pda_workspace_size(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens, &n);
+    if (rc == PDA_OK) {
+      need = std::max(need, n);
+      any = true;
+    }
+  }
+  if (!any) return rc;
+  *bytes = need;
+  return ok();
+}
+
 int pda_workspace_layout(int B, int Hq, int Hkv, int D, int block_size, int max_blocks_per_seq,
                          int partition_tokens, int kv_fp8, pda_layout* layout) {
   if (!layout) return fail(PDA_EINVAL, "layout is null");

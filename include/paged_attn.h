@@ -92,6 +92,20 @@ int pda_workspace_size(int B, int Hq, int Hkv, int D, int block_size,
                        int max_blocks_per_seq, int partition_tokens,
                        size_t* bytes);
 
+/*
+ * The same bytes for a caller that does not yet know Hkv: the largest
+ * pda_workspace_size over every KV-head count Hkv that divides Hq and is
+ * supported, so one workspace of this size serves paged_decode_attn,
+ * paged_decode_attn_partial and their FP8 and fused-append forms whatever
+ * grouping of the Hq query heads the call uses.  This is the sizing call of
+ * the decode boundary (a split-K workspace for the attention node's partial,
+ * KernelFlume paper §3.2).  Returns the last error of pda_workspace_size if no
+ * KV-head count is accepted.
+ */
+int paged_decode_attn_workspace_size(int B, int Hq, int D, int block_size,
+                                     int max_blocks_per_seq, int partition_tokens,
+                                     size_t* bytes);
+
 /* Workspace layout of one call shape; see pda_workspace_layout. */
 typedef struct {
   size_t header_offset; /* int32 [4 + B]: k, U, n_runs, unit_tokens,

@@ -71,6 +71,28 @@ def test_workspace_size_rejects(lib, kw, code):
     assert lib.pda_last_error()
 
 
+def test_decode_workspace_size_covers_every_kv_head_count(lib):
+    """paged_decode_attn_workspace_size (no Hkv argument) is the largest
+    pda_workspace_size over the supported KV-head counts of Hq."""
+    for B, Hq, mb, P in ((3, 32, 100, 256), (16, 32, 12800, 512), (1, 8, 1, 0)):
+        n = ctypes.c_size_t(0)
+        assert lib.paged_decode_attn_workspace_size(B, Hq, 128, 16, mb, P, ctypes.byref(n)) == 0
+        per = []
+        for Hkv in range(1, Hq + 1):
+            if Hq % Hkv == 0:
+                rc, m = _ws(B=B, Hq=Hq, Hkv=Hkv, mb=mb, P=P)
+                if rc == 0:
+                    per.append(m)
+        assert per and n.value == max(per)
+        assert pda.decode_workspace_size(B, Hq, mb, P) == n.value
+    n = ctypes.c_size_t(0)
+    assert lib.paged_decode_attn_workspace_size(2, 8, 64, 16, 4, 0, ctypes.byref(n)) == 2   # D
+    assert lib.paged_decode_attn_workspace_size(-1, 8, 128, 16, 4, 0, ctypes.byref(n)) == 1
+    assert lib.paged_decode_attn_workspace_size(2, 8, 128, 16, 4, 24, ctypes.byref(n)) == 1
+    assert lib.paged_decode_attn_workspace_size(2, 0, 128, 16, 4, 0, ctypes.byref(n)) == 1
+    assert lib.paged_decode_attn_workspace_size(2, 8, 128, 16, 4, 0, None) == 1
+
+
 def test_workspace_size_formula(lib):
     # header int32[4 + B], lse fp32[n_slots, Hq], o fp32[n_slots, Hq, D], each 256-aligned
     B, Hq, Hkv, mb, P = 3, 32, 8, 100, 256
