@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     multi_query_workspace_size,
     paged_decode_attn,
     paged_decode_attn_append,
+    paged_decode_attn_noalloc,
     paged_decode_attn_partial,
     paged_kv_append,
     paged_multi_query_attn,
@@ -34,6 +35,7 @@ __all__ = [
     "multi_query_workspace_size",
     "paged_decode_attn",
     "paged_decode_attn_append",
+    "paged_decode_attn_noalloc",
     "paged_decode_attn_partial",
     "paged_kv_append",
     "paged_multi_query_attn",

@@ -46,6 +46,9 @@ _SIGNATURES = {
     "paged_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int, _c_int,
                                    _c_int, _c_int, _c_i64, _c_int, _c_float, _c_int, _vp, _vp,
                                    _c_size, _vp]),
+    "paged_decode_attn_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int, _c_int,
+                                           _c_int, _c_int, _c_int, _c_i64, _c_int, _c_float,
+                                           _c_int, _vp, _vp]),
     "paged_decode_attn_partial": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _c_int,
                                            _c_int, _c_int, _c_int, _c_int, _c_i64, _c_int,
                                            _c_float, _c_int, _vp, _c_size, _vp]),
@@ -293,6 +296,33 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, context_lens, scale, out
                     lse_out, return_lse, partition_tokens, workspace, max_blocks_per_seq,
                     k_scale, v_scale)
     return (out, lse) if (return_lse or lse_out is not None) else out
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, block_table, context_lens, scale, out,
+                              lse_out=None, partition_tokens=0, max_blocks_per_seq=None):
+    """paged_decode_attn with the library's fixed device scratch as its workspace
+    (paged_decode_attn_noalloc in include/paged_attn.h): fp16 caches; ``out``
+    (fp16 [B, Hq, D]) and the optional ``lse_out`` (fp32 [B, Hq]) are the
+    caller's, so nothing is allocated here or in the library.  Calls that may
+    overlap on one GPU share its scratch and must be ordered by the caller."""
+    dev = _check_inputs(q, k_cache, v_cache, block_table, context_lens)
+    if is_fp8_cache(k_cache):
+        raise TypeError("paged_decode_attn_noalloc takes fp16 caches")
+    B, Hq, D = q.shape
+    num_blocks, bs, Hkv, _ = k_cache.shape
+    width = block_table.shape[1]
+    mb = width if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    if mb > width:
+        raise ValueError("max_blocks_per_seq exceeds the block table width")
+    bt_stride = block_table.stride(0) if B > 0 else max(mb, 1)
+    _check_buffer(out, torch.float16, (B, Hq, D), dev, "the output")
+    if lse_out is not None:
+        _check_buffer(lse_out, torch.float32, (B, Hq), dev, "lse")
+    _check(load_library().paged_decode_attn_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), bt_stride,
+        _ptr(context_lens), B, Hq, Hkv, D, bs, num_blocks, mb, float(scale),
+        int(partition_tokens), _ptr(lse_out), _stream(dev)))
+    return (out, lse_out) if lse_out is not None else out
 
 
 def paged_decode_attn_partial(q, k_cache, v_cache, block_table, context_lens, scale, o=None,

@@ -77,6 +77,9 @@ int ok() {
 
 }  // namespace pda
 
+// Fixed device scratch of paged_decode_attn_noalloc (see below).
+static __device__ __align__(256) unsigned char scratch[PDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace pda;
@@ -1074,6 +1077,40 @@ int run_append(bool fp8, void* k_cache, void* v_cache, const void* k_new, const 
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch for paged_decode_attn_noalloc: the split-K workspace of
+// a call that may not allocate.  Every device the library runs on holds its
+// own copy for the life of the process.  Host code never uses the array's
+// name as an address: its device address is looked up once per device.
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch (null with *err set if the
+// lookup failed); looked up on the first call on each device, that device
+// being current.
+void* scratch_ptr(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    s.ptr = s.err == hipSuccess ? p : nullptr;
+  });
+  *err = s.err;
+  return s.ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1141,6 +1178,29 @@ int paged_decode_attn(void* out, const void* q, const void* k_cache, const void*
                        context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
                        scale, false, 1.0f, 1.0f, partition_tokens, workspace, workspace_bytes,
                        stream);
+}
+
+int paged_decode_attn_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int64_t block_table_stride,
+                              const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                              int block_size, int64_t num_blocks, int max_blocks_per_seq,
+                              float scale, int partition_tokens, float* lse_out, void* stream) {
+  int rc = check_shape(B, Hq, Hkv, D, block_size, max_blocks_per_seq, partition_tokens);
+  if (rc != PDA_OK) return rc;
+  if (B == 0) return ok();
+  const Plan pl = make_plan(B, Hq, Hkv, max_blocks_per_seq, partition_tokens, kernel_kind(false, false));
+  if (pl.total > (size_t)PDA_NOALLOC_SCRATCH_BYTES)
+    return fail(PDA_EUNSUPPORTED,
+                "this call needs %zu bytes of split-K workspace, above the %zu bytes of fixed "
+                "scratch; use paged_decode_attn with a caller workspace",
+                pl.total, (size_t)PDA_NOALLOC_SCRATCH_BYTES);
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws) return fail(PDA_EHIP, "device scratch lookup failed: %s", hipGetErrorString(e));
+  return run_attention(true, out, lse_out, q, k_cache, v_cache, block_table, block_table_stride,
+                       context_lens, B, Hq, Hkv, D, block_size, num_blocks, max_blocks_per_seq,
+                       scale, false, 1.0f, 1.0f, partition_tokens, ws,
+                       (size_t)PDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int paged_decode_attn_append(void* out, const void* q, const void* k_new, const void* v_new,

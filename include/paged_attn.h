@@ -178,6 +178,31 @@ int paged_decode_attn(void* out, const void* q, const void* k_cache,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split-K workspace is instead a fixed
+ * device array of PDA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends; its device address is looked up (never
+ * allocated) on the first call on each device.  No allocation of any kind is
+ * made on the call.  Arguments, results and errors are those of
+ * paged_decode_attn (the same kernels, bit for bit the same output); a call
+ * whose split-K workspace (at most pda_workspace_size for its shape) exceeds
+ * the scratch returns PDA_EUNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents: calls that
+ * may overlap on one GPU (several streams, several host threads) race and
+ * must be ordered by the caller.  Nothing in the scratch needs clearing
+ * between calls: each call writes what it reads.
+ */
+#define PDA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int paged_decode_attn_noalloc(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              int64_t block_table_stride, const int32_t* context_lens,
+                              int B, int Hq, int Hkv, int D, int block_size,
+                              int64_t num_blocks, int max_blocks_per_seq, float scale,
+                              int partition_tokens, float* lse_out, void* stream);
+
+/*
  * The partial of a token range: same inputs as paged_decode_attn, where the
  * block table and context_lens describe the range a caller owns (a column
  * slice of the full table via block_table_stride, and the range's length).
