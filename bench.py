@@ -10,7 +10,14 @@ Prints ONE JSON line:
                  tokens (sum_b ctx_b * 2 * Hkv * D * 2 B) / wall time per step
   roofline       the same bytes / the average call time measured with HIP
                  events on the launch stream, against the 8 TB/s HBM peak
-  cpu_baseline   the float64 CPU oracle on a bounded sample of the workload
+  flushed        the headline call timed by events with 1 GiB of scratch read
+                 before each call (the last-level cache then holds no K/V)
+  also           the other decode workloads: the Llama-3.1-8B 4K batch, the ragged
+                 256-sequence batch, the 32 x 128K batch as 4 range partials +
+                 merge_partials (and its single pass), the agentic batch over an
+                 FP8 cache, and at the Q48:KV8 and MHA Q40:KV40 head shapes
+  cpu_baseline   the float64 CPU oracle: all cores (a process pool over every
+                 sequence) and one core (a bounded sample)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -85,43 +92,119 @@ def measured_traffic(key, op="attention"):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(case, budget_s):
-    """Time the float64 oracle (gather + compute) on whole sequences until the budget."""
-    import numpy as np
-    import oracle.paged_attention as O
-    from decode_attention_paged_attn_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:                                    # threadpoolctl missing
-        threads = 1
-    rng = np.random.default_rng(1)
-    order = rng.permutation(case.B)
-    done, tokens, spent = [], 0, 0.0
-    for b in order:
-        q, k, v, table, lens = W.host_sequences(case, [int(b)])
-        t0 = time.perf_counter()
-        if case.kv_dtype == "fp8":
-            O.paged_decode_attention_fp8(q, k, v, table, lens, case.scale, case.k_scale,
-                                         case.v_scale)
-        else:
-            O.paged_decode_attention(q, k, v, table, lens, case.scale)
-        spent += time.perf_counter() - t0
-        done.append(int(b))
-        tokens += int(lens[0])
-        if spent >= budget_s:
-            break
-    gbs = kv_bytes([tokens], case.Hkv, elem=case.kv_bytes_per_elem) / spent / 1e9
-    cpu = ""
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
-        pass
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "cpu_model": cpu,
-            "sample": f"{len(done)} of {case.B} sequences ({tokens} tokens, all {case.Hq} query "
-                      f"heads), float64 numpy gather + two-pass softmax, {spent:.1f} s"}
+        return ""
+
+
+def _oracle_one(case, q, k, v, table, lens):
+    import oracle.paged_attention as O
+    if case["kv_dtype"] == "fp8":
+        O.paged_decode_attention_fp8(q, k, v, table, lens, case["scale"], case["k_scale"],
+                                     case["v_scale"])
+    else:
+        O.paged_decode_attention(q, k, v, table, lens, case["scale"])
+
+
+def _pool_init():
+    """A pool worker computes with one thread: BLAS limited before numpy loads."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+def _pool_task(args):
+    """One sequence in a worker: attach to the shared host copy, gather + attend."""
+    from multiprocessing import shared_memory
+    import numpy as np
+    meta, shm_names = args
+    shms = [shared_memory.SharedMemory(name=n) for n in shm_names]
+    try:
+        arrs = [np.ndarray(shape, dtype=np.dtype(dt), buffer=sh.buf)
+                for (shape, dt), sh in zip(meta["arrays"], shms)]
+        t0 = time.perf_counter()
+        _oracle_one(meta["case"], *arrs, meta["lens"])
+        return time.perf_counter() - t0
+    finally:
+        for sh in shms:
+            sh.close()
+
+
+def cpu_baseline(case, budget_s):
+    """The float64 oracle as it stands, on host copies of whole sequences of the
+    workload: (i) one core (one process, BLAS limited to one thread), sequences in
+    a fixed random order until ``budget_s`` seconds of work; (ii) all cores: a
+    process pool, one worker per core of this process's CPU share (at most 16),
+    over every sequence of the workload, gathering from one host copy in shared
+    memory.  Times cover gather + compute only."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    import numpy as np
+    from decode_attention_paged_attn_amd import workloads as W
+    meta_case = {"kv_dtype": case.kv_dtype, "scale": case.scale, "k_scale": case.k_scale,
+                 "v_scale": case.v_scale}
+    elem = case.kv_bytes_per_elem
+    # (i) one core
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        one_thread = threadpool_limits(limits=1)
+    except Exception:                                    # threadpoolctl missing
+        one_thread = contextlib.nullcontext()
+    order = np.random.default_rng(1).permutation(case.B)
+    done, tokens, spent = [], 0, 0.0
+    with one_thread:
+        for b in order:
+            q, k, v, table, lens = W.host_sequences(case, [int(b)])
+            t0 = time.perf_counter()
+            _oracle_one(meta_case, q, k, v, table, lens)
+            spent += time.perf_counter() - t0
+            done.append(int(b))
+            tokens += int(lens[0])
+            if spent >= budget_s:
+                break
+    one = kv_bytes([tokens], case.Hkv, elem=elem) / spent / 1e9
+    # (ii) all cores of this process's share, one worker per core
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    workers = max(1, min(share, 16, case.B))
+    tasks, shms = [], []
+    try:
+        for b in range(case.B):
+            q, k, v, table, lens = W.host_sequences(case, [b])
+            arrays, names = [], []
+            for a in (q, k, v, table):
+                a = np.ascontiguousarray(a)
+                sh = shared_memory.SharedMemory(create=True, size=max(a.nbytes, 1))
+                np.ndarray(a.shape, dtype=a.dtype, buffer=sh.buf)[...] = a
+                shms.append(sh)
+                arrays.append((a.shape, a.dtype.str))
+                names.append(sh.name)
+            tasks.append(({"case": meta_case, "arrays": arrays, "lens": lens}, names))
+            del q, k, v
+        with mp.get_context("spawn").Pool(workers, initializer=_pool_init) as pool:
+            pool.map(_pool_task, tasks[:workers])          # workers up and numpy loaded
+            t0 = time.perf_counter()
+            pool.map(_pool_task, tasks, chunksize=1)
+            wall = time.perf_counter() - t0
+    finally:
+        for sh in shms:
+            sh.close()
+            sh.unlink()
+    all_tok = int(case.lens.sum())
+    pool_gbs = kv_bytes([all_tok], case.Hkv, elem=elem) / wall / 1e9
+    return {"value": round(pool_gbs, 4), "unit": "GB/s", "cores": int(workers), "kind": "oracle",
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "cpu_share": share,
+            "sample": f"all {case.B} sequences ({all_tok} tokens, all {case.Hq} query heads), "
+                      f"float64 numpy gather + two-pass softmax in a pool of {workers} "
+                      f"single-threaded processes over one shared host copy, {wall:.1f} s wall",
+            "one_core": {"value": round(one, 4), "unit": "GB/s", "cores": 1,
+                         "sample": f"{len(done)} of {case.B} sequences ({tokens} tokens), "
+                                   f"one process, BLAS limited to 1 thread, {spent:.1f} s"}}
 
 
 def copy_calibration(mib, steps):
@@ -162,7 +245,14 @@ def measure(case, P, steps, warmup, flush_mib=0):
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     unit = pda.workspace_layout(B, Hq, Hkv, width, P,
                                 kv_fp8=case.kv_dtype == "fp8")["unit_tokens"]
-    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda") if flush_mib else None
+    scratch = torch.ones(flush_mib << 20, dtype=torch.uint8, device="cuda") if flush_mib else None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def flush():
+        # read (ordinary loads, which allocate in L2 and the last-level cache)
+        # a buffer four times the last-level cache: no K/V stays cached, and no
+        # dirty lines are left to write back during the timed call
+        pda.stream_read(scratch, sink, False)
 
     kw = case.attn_kwargs()
 
@@ -177,7 +267,7 @@ def measure(case, P, steps, warmup, flush_mib=0):
     t0 = time.perf_counter()
     for i in range(steps):
         if scratch is not None:
-            scratch.fill_(i & 0xFF)      # evicts K/V from the last-level cache between calls
+            flush()
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -188,7 +278,7 @@ def measure(case, P, steps, warmup, flush_mib=0):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         if scratch is not None:
-            scratch.fill_(i & 0xFF)
+            flush()
         starts[i].record(stream)
         step()
         ends[i].record(stream)
@@ -197,6 +287,10 @@ def measure(case, P, steps, warmup, flush_mib=0):
     ev_mean = sum(ev_ms) / len(ev_ms)
     nbytes = kv_bytes(case.lens, Hkv, elem=case.kv_bytes_per_elem)
     ms_per_step = wall / steps * 1e3
+    if scratch is not None:
+        # the wall clock also ran the scratch reads: the rate of a flushed
+        # call is the event-bracketed one
+        ms_per_step = ev_mean
     return {
         "kv_bytes": nbytes,
         "unit_tokens": unit,
@@ -408,9 +502,9 @@ def bench_cascade(case, steps, warmup):
                    "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}), flush=True)
 
 
-def bench_partial_merge(case, steps, warmup):
-    """R range partials (paged_decode_attn_partial over block-table column slices)
-    plus merge_partials, against single-pass attention over the same batch."""
+def measure_partial_merge(case, steps, warmup):
+    """R range partials (paged_decode_attn_partial on block-table column slices)
+    + merge_partials per step, and the single pass over the same batch."""
     import torch
     import decode_attention_paged_attn_amd as pda
     from decode_attention_paged_attn_amd import workloads as W
@@ -423,37 +517,58 @@ def bench_partial_merge(case, steps, warmup):
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(pda.workspace_size(B, Hq, case.Hkv, case.block_table.shape[1], 0), 1),
                      dtype=torch.uint8, device="cuda")
+    kw = case.attn_kwargs()
 
     def split_path():
         for r, (bt, ln) in enumerate(views):
             pda.paged_decode_attn_partial(case.q, case.k_cache, case.v_cache, bt, ln, case.scale,
-                                          o=o_parts[r], lse=l_parts[r], workspace=ws)
+                                          o=o_parts[r], lse=l_parts[r], workspace=ws, **kw)
         pda.merge_partials(o_parts, l_parts, out=out, lse_out=lse)
 
     def single():
         pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
-                              case.context_lens, case.scale, out=out, lse_out=lse, workspace=ws)
+                              case.context_lens, case.scale, out=out, lse_out=lse, workspace=ws,
+                              **kw)
 
     wall_ms, ev_ms, _ = _time_events(split_path, steps, warmup)
     s_wall, s_ev, _ = _time_events(single, steps, warmup)
-    nbytes = kv_bytes(case.lens, case.Hkv)
+    nbytes = kv_bytes(case.lens, case.Hkv, elem=case.kv_bytes_per_elem)
+    return {"value": round(nbytes / (wall_ms / 1e3) / 1e9, 2), "unit": "GB/s",
+            "pct_hbm_peak": round(100.0 * nbytes / (wall_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+            "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+            "ms_per_step": round(wall_ms, 5), "event_ms": round(ev_ms, 5),
+            "decode_attn_tokens_per_s": round(B / (wall_ms / 1e3), 1),
+            "kv_bytes_per_step": nbytes, "ranges": R,
+            "step": f"{R} x paged_decode_attn_partial + merge_partials",
+            "single_pass_event_ms": round(s_ev, 5),
+            "single_pass_event_GBps": round(nbytes / (s_ev / 1e3) / 1e9, 2),
+            "split_over_single_time": round(ev_ms / s_ev, 4)}
+
+
+def bench_partial_merge(case, steps, warmup):
+    """R range partials (paged_decode_attn_partial over block-table column slices)
+    plus merge_partials, against single-pass attention over the same batch."""
+    m = measure_partial_merge(case, steps, warmup)
+    nbytes = m["kv_bytes_per_step"]
+    ev_ms = m["event_ms"]
     print(json.dumps({
         "metric": "disaggregated partial merge: KV-read GB/s (R range partials + merge_partials)",
         "op": "paged_decode_attn_partial x R + merge_partials", "unit": "GB/s",
-        "value": round(nbytes / (wall_ms / 1e3) / 1e9, 2),
-        "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
-        "ms_per_step": round(wall_ms, 5), "event_ms": round(ev_ms, 5),
-        "single_pass_event_ms": round(s_ev, 5),
-        "single_pass_event_GBps": round(nbytes / (s_ev / 1e3) / 1e9, 2),
-        "split_over_single_time": round(ev_ms / s_ev, 4),
-        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
+        "value": m["value"], "event_GBps": m["event_GBps"], "ms_per_step": m["ms_per_step"],
+        "event_ms": ev_ms, "single_pass_event_ms": m["single_pass_event_ms"],
+        "single_pass_event_GBps": m["single_pass_event_GBps"],
+        "split_over_single_time": m["split_over_single_time"],
+        "roofline": {"bound": "hbm", "achieved": m["event_GBps"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "kernel": "R partial calls + merge_partials", "traffic": None},
-        "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": case.name, "batch": B, "q_heads": Hq, "kv_heads": case.Hkv,
-                   "head_dim": 128, "ranges": R, "tokens_per_sequence": int(case.lens[0]),
-                   "kv_bytes_per_step": nbytes}}), flush=True)
+                     "frac": round(m["event_GBps"] / HBM_PEAK_GBS, 4),
+                     "kernel": "R partial calls + merge_partials",
+                     "traffic": measured_traffic(f"disagg_merge_partial/{case.kv_dtype}")},
+        "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": case.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": case.B, "q_heads": case.Hq,
+                   "kv_heads": case.Hkv, "head_dim": 128, "ranges": case.ranges,
+                   "tokens_per_sequence": int(case.lens[0]), "kv_bytes_per_step": nbytes}}),
+        flush=True)
 
 
 def bench_append(case, steps, warmup):
@@ -517,8 +632,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-read", action="store_true",
                     help="skip the streaming-read ceiling measured beside the headline")
-    ap.add_argument("--also", default="llama8b_4k",
-                    help="comma-separated extra workloads reported under 'also'")
+    ap.add_argument("--also", default="llama8b_4k,ragged_mixed,disagg_merge:partial,agentic_80k:fp8,"
+                                      "agentic_80k_q48kv8,agentic_80k_q40kv40",
+                    help="comma-separated extra workloads reported under 'also': a workload "
+                         "name, ':fp8' for its FP8 cache, ':partial' for its R range partials "
+                         "+ merge_partials (disagg_merge)")
+    ap.add_argument("--flush-record-mib", type=int, default=1024,
+                    help="also time the headline with this many MiB of scratch read before "
+                         "each call (event-timed; 0: skip)")
     ap.add_argument("--op", default="attention",
                     choices=["attention", "append", "multi_query", "cascade", "partial_merge"],
                     help="attention (default): paged_decode_attn; append: paged_kv_append of "
@@ -529,8 +650,8 @@ def main():
     ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
                     help="element type of the K/V cache (fp8: E4M3 codes with per-tensor scales)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="write this many MiB of scratch between timed calls (outside the "
-                         "event pair; the wall clock includes it)")
+                    help="read this many MiB of scratch before each timed call (outside the "
+                         "event pair; the headline is then event-timed)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: time a plain device copy of MIB MiB (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -562,7 +683,8 @@ def main():
         bench_cascade(case, args.steps, args.warmup)
         return
     if args.op == "partial_merge":
-        bench_partial_merge(W.disagg_merge(device="cuda"), args.steps, args.warmup)
+        bench_partial_merge(W.disagg_merge(device="cuda", kv_dtype=args.kv_dtype), args.steps,
+                            args.warmup)
         return
     case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if args.op == "append":
@@ -571,8 +693,14 @@ def main():
     # the extra workloads get their memory now, while it is fresh: built after
     # the headline's pools were freed, a workload measured 4% slower than in a
     # process of its own
-    also_cases = [W.CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)
-                  for name in [x for x in args.also.split(",") if x and x != args.config]]
+    also_cases = []
+    for spec in [x for x in args.also.split(",") if x]:
+        parts = spec.split(":")
+        kv = "fp8" if "fp8" in parts[1:] else args.kv_dtype
+        partial = "partial" in parts[1:]
+        if parts[0] == args.config and kv == args.kv_dtype and not partial:
+            continue
+        also_cases.append((spec, partial, W.CONFIGS[parts[0]](device="cuda", kv_dtype=kv)))
     P = case.partition_tokens if args.partition_tokens is None else args.partition_tokens
     m = measure(case, P, args.steps, args.warmup, args.flush_mib)
     nbytes = m["kv_bytes"]
@@ -619,18 +747,34 @@ def main():
     }
     if args.flush_mib:
         rec["flush_mib_between_steps"] = args.flush_mib
+        rec["value_timing"] = "events (each call bracketed; the scratch reads outside)"
+    if args.flush_record_mib:
+        fm = measure(case, P, args.steps, 0, args.flush_record_mib)
+        rec["flushed"] = {"flush_mib_before_each_call": args.flush_record_mib,
+                          "event_GBps": fm["achieved"],
+                          "pct_hbm_peak": round(100.0 * fm["achieved"] / HBM_PEAK_GBS, 2),
+                          "event_ms": fm["event_ms"]}
     if not args.no_stream_read:
         ceiling = stream_read_ceiling()
         rec["stream_read_ceiling"] = ceiling
         rec["frac_of_stream_read_ceiling"] = round(m["achieved"] / ceiling["GBps"], 4)
     also = {}
-    for acase in also_cases:
-        mm = measure(acase, acase.partition_tokens, args.steps, args.warmup, args.flush_mib)
-        also[acase.name] = {"value": mm["value"], "unit": "GB/s",
-                           "pct_hbm_peak": round(100.0 * mm["value"] / HBM_PEAK_GBS, 2),
-                           "event_GBps": mm["achieved"], "ms_per_step": mm["ms_per_step"],
-                           "decode_attn_tokens_per_s": mm["tokens_per_s"],
-                           "kv_bytes_per_step": mm["kv_bytes"]}
+    for spec, partial, acase in also_cases:
+        key = acase.name + ("_4partials_merge" if partial else "")
+        if partial:
+            also[key] = measure_partial_merge(acase, args.steps, args.warmup)
+        else:
+            mm = measure(acase, acase.partition_tokens, args.steps, args.warmup, args.flush_mib)
+            also[key] = {"value": mm["value"], "unit": "GB/s",
+                         "pct_hbm_peak": round(100.0 * mm["value"] / HBM_PEAK_GBS, 2),
+                         "event_GBps": mm["achieved"],
+                         "event_pct_hbm_peak": round(100.0 * mm["achieved"] / HBM_PEAK_GBS, 2),
+                         "ms_per_step": mm["ms_per_step"], "event_ms": mm["event_ms"],
+                         "decode_attn_tokens_per_s": mm["tokens_per_s"],
+                         "kv_bytes_per_step": mm["kv_bytes"], "partition_tokens": mm["unit_tokens"],
+                         "traffic": measured_traffic(f"{spec.split(':')[0]}/{acase.kv_dtype}")}
+        also[key]["kv_dtype"] = acase.kv_dtype
+        also[key]["workload"] = spec
     if also:
         rec["also"] = also
     del also_cases

@@ -59,7 +59,7 @@ namespace {
 using namespace pda;
 
 constexpr int kMqWaves = 4;           // waves per work-group (KV heads, or row groups)
-constexpr int kMqMaxKvHeads = 8;
+constexpr int kMqMaxKvHeads = 64;
 constexpr int kMqMaxSeqs = 4000;      // sequences per call: their facts live in the plan's LDS
 constexpr int kMqHdrInts = 8;         // k, U, n_runs, P, n_tiles, n_fix
 constexpr int kMqTileArrays = 8;      // seq, q0, nq, base, ntok, ub, rank, fix
@@ -630,8 +630,10 @@ template <int G, int NT, bool kFp8>
 __global__ __launch_bounds__(2 * kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_reg_kernel(MqParams p) {
   constexpr int kState = NT * (2 + 32);                  // floats per lane
-  __shared__ float xs[kMqWaves][kState][kWave];
   const int lane = threadIdx.x & (kWave - 1);
+  // [hg][kState][kWave]: one state per KV head of the group, sized at launch
+  extern __shared__ float xs_dyn[];
+  auto xs = [&](int head, int i) -> float& { return xs_dyn[(head * kState + i) * kWave + lane]; };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hg = p.hg;
   const int half = wave >= hg ? 1 : 0;
@@ -656,12 +658,12 @@ void mq_reg_kernel(MqParams p) {
   if (shared_tile >= 0 && half == 1) {
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
-      xs[gl][b][lane] = st.m[b];
-      xs[gl][NT + b][lane] = st.lp[b];
+      xs(gl, b) = st.m[b];
+      xs(gl, NT + b) = st.lp[b];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xs[gl][2 * NT + 32 * b + 4 * u + r][lane] = st.acc[b][u][r];
+        for (int r = 0; r < 4; ++r) xs(gl, 2 * NT + 32 * b + 4 * u + r) = st.acc[b][u][r];
     }
   }
   __syncthreads();
@@ -669,18 +671,18 @@ void mq_reg_kernel(MqParams p) {
     const int c = lane >> 4;
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
-      const float mb = xs[gl][b][lane];
+      const float mb = xs(gl, b);
       const float m = fmaxf(st.m[b], mb);
       const float aa = st.m[b] == m ? 1.0f : fast_exp2(st.m[b] - m);   // 0 for an empty side
       const float ab = mb == m ? 1.0f : fast_exp2(mb - m);
-      st.lp[b] = st.lp[b] * aa + xs[gl][NT + b][lane] * ab;
+      st.lp[b] = st.lp[b] * aa + xs(gl, NT + b) * ab;
       st.m[b] = m;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ar = __shfl(aa, 4 * c + r, kWave), br = __shfl(ab, 4 * c + r, kWave);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          st.acc[b][u][r] = st.acc[b][u][r] * ar + xs[gl][2 * NT + 32 * b + 4 * u + r][lane] * br;
+          st.acc[b][u][r] = st.acc[b][u][r] * ar + xs(gl, 2 * NT + 32 * b + 4 * u + r) * br;
       }
     }
     const int i = shared_tile;
@@ -896,12 +898,45 @@ __device__ __forceinline__ void wide_load_q(const MqParams& p, int g, int q0, in
   }
 }
 
+// Per-lane byte offsets, within a stage and for token chunk c = 0, of the V
+// reads of wide_v_operands (chunk c adds 16 rows, a constant: the row swizzle
+// depends on a row's low 4 bits only).  fp16: entry 2u + r is the 8-byte
+// transposed-read piece of tile u, token row 8r + 4hf + b; FP8: entry 4jj + i
+// is the 4 bytes (dims 4n .. 4n+3) of token row 8jj + 4hf + i.  Computed once
+// per segment and kept opaque, so that every read is one of these registers
+// plus an immediate offset (the stage, the sub-step and c), with no address
+// arithmetic in the token loop.
+template <bool kFp8>
+__device__ __forceinline__ void wide_v_offsets(int lane, unsigned (&voff)[8]) {
+  const int n = lane & 31, hf = lane >> 5;
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        voff[4 * jj + i] = (unsigned)(wide_at<true>(8 * jj + 4 * hf + i, n >> 2) + 4 * (n & 3));
+  } else {
+    const int a = n & 3, b = (n >> 2) & 3, g16 = n >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        voff[2 * u + r] = (unsigned)(wide_at<false>(8 * r + 4 * hf + b, 4 * u + 2 * g16 + (a >> 1)) +
+                                     8 * (a & 1));
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) asm volatile("" : "+v"(voff[x]));
+}
+
 // B operands of the 4 p.V tiles for token chunk c from the step's V rows in
-// LDS (row stride kRow).  Tokens at or past `valid` (relative to the step) are
-// exact zeros, selected so that stale or poisoned rows cannot leak NaN.
+// LDS (row stride kRow; voff from wide_v_offsets).  Tokens at or past `valid`
+// (relative to the step) are exact zeros, selected so that stale or poisoned
+// rows cannot leak NaN.
 template <bool kMasked, bool kFp8>
-__device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int hf, int n,
-                                                int valid, half8_t (&vb)[4]) {
+__device__ __forceinline__ void wide_v_operands(const char* vstage, const unsigned (&voff)[8],
+                                                int c, int hf, int valid, half8_t (&vb)[4]) {
+  constexpr int kRow = wide_row_bytes<kFp8>();
+  const char* vc = vstage + 16 * c * kRow;
   if constexpr (kFp8) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -909,7 +944,7 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * c + 8 * jj + 4 * hf + i;
-        w[i] = *reinterpret_cast<const unsigned*>(vstage + wide_at<true>(tok, n >> 2) + 4 * (n & 3));
+        w[i] = *reinterpret_cast<const unsigned*>(vc + voff[4 * jj + i]);
         if (kMasked && tok >= valid) w[i] = 0u;                      // code 0 = +0
       }
       // 4x4 byte transpose: col[u] = byte u (dim 4n + u) of the 4 tokens
@@ -938,15 +973,13 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, int c, int h
     // 32u + 16 (n / 16) + 4a .. +3 of token 16c + 8r + 4hf + b, so lane n gets
     // dim 32u + n of the four tokens k = 8hf + 4r + b: tile u covers dims
     // 32u .. 32u + 31, column n dim 32u + n.
-    const int a = n & 3, b = (n >> 2) & 3, g16 = n >> 4;
     typedef __fp16 fp16x4 __attribute__((vector_size(8)));    // the builtin's element type
     typedef __attribute__((address_space(3))) fp16x4 LdsHalf4;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int tok = 16 * c + 8 * r + 4 * hf + b;
-        const char* src = vstage + wide_at<false>(tok, 4 * u + 2 * g16 + (a >> 1)) + 8 * (a & 1);
+        const char* src = vc + voff[2 * u + r];
         half4_t x = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LdsHalf4*)src));
         if (kMasked) {
 #pragma unroll
@@ -1002,7 +1035,8 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
 // see everything and are never stored.
 template <int G, bool kMasked, bool kFp8, int kNS>
 __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
-                                          const char* vstage, float qk_scale, int lane, int row0,
+                                          const char* vstage, const unsigned (&voff)[8],
+                                          float qk_scale, int lane, int row0,
                                           int t0, int causal_base, int n_seq, int nq,
                                           int tok_hi) {
   constexpr int kRow = wide_row_bytes<kFp8>();
@@ -1064,7 +1098,7 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
 #pragma unroll
       for (int t = 0; t < 8; ++t) pa[t] = static_cast<_Float16>(pr[8 * c + t]);
       half8_t vb[4];
-      wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, c, hf, n, valid, vb);
+      wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, voff, c, hf, valid, vb);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[u], st.acc[u], 0, 0, 0);
@@ -1175,6 +1209,8 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.acc[u][r] = 0.0f;
 
+  unsigned voff[8];
+  wide_v_offsets<kFp8>(lane, voff);
   // the step's sub-steps, kFS at a time; a group wholly past tok_hi would
   // add exact zeros and is skipped
   constexpr int kFS = wide_fold_ns<kFp8>();
@@ -1191,10 +1227,10 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
       __builtin_amdgcn_s_setprio(0);
       const char* vs = vstage + 32 * j0 * kRow;
       if (t0 + 32 * kFS > full_end)
-        wide_tail<G, true, kFp8, kFS>(st, sc, vs, p.qk_scale, lane, row0, t0, causal_base, n_seq,
+        wide_tail<G, true, kFp8, kFS>(st, sc, vs, voff, p.qk_scale, lane, row0, t0, causal_base, n_seq,
                                       nq, tok_hi);
       else
-        wide_tail<G, false, kFp8, kFS>(st, sc, vs, p.qk_scale, lane, row0, t0, causal_base,
+        wide_tail<G, false, kFp8, kFS>(st, sc, vs, voff, p.qk_scale, lane, row0, t0, causal_base,
                                        n_seq, nq, tok_hi);
     }
   };
@@ -1294,7 +1330,9 @@ __device__ __forceinline__ void merge_rows_small(const float* o, const float* ls
   for (int r = 0; r < kMergeRows; ++r)
 #pragma unroll
     for (int sg = 0; sg < kSmallSeg; ++sg) {
-      const long long at = (slot0 + sg) * rows + row0 + r;
+      // rows past the tile's last row (rows need not be a multiple of
+      // kMergeRows) re-read the last one; they are never stored
+      const long long at = (slot0 + sg) * rows + min(row0 + r, rows - 1);
       lv[r][sg] = sg < nseg ? lse[at] : -INFINITY;
       ov[r][sg] = sg < nseg ? *reinterpret_cast<const f32x2*>(o + at * kD + 2 * lane)
                             : f32x2{0.0f, 0.0f};
@@ -1326,9 +1364,9 @@ template <int Qt>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  // rows of a tile: Qt * Hq = (16 << variant) * Hkv, a multiple of kMergeRows
+  // rows of a tile: Qt * Hq, in groups of kMergeRows (the last one may be short)
   const long long rows = (long long)Qt * p.Hq;
-  const long long groups = rows / kMergeRows;
+  const long long groups = (rows + kMergeRows - 1) / kMergeRows;
   const int n_fix = p.hdr[5];
   for (long long idx = (long long)blockIdx.x * 4 + wave;; idx += (long long)gridDim.x * 4) {
     const int f = (int)min(idx / groups, (long long)p.tiles_max - 1);
@@ -1346,13 +1384,14 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqParams p) {
     } else {
 #pragma unroll
       for (int r = 0; r < kMergeRows; ++r)
-        merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, rows, row0 + r, lane, res[r], lse_res[r]);
+        merge_row(p.ws_o, p.ws_lse, slot0, 1, nseg, rows, min(row0 + r, rows - 1), lane, res[r],
+                  lse_res[r]);
     }
 #pragma unroll
     for (int r = 0; r < kMergeRows; ++r) {
       const long long row = row0 + r;
       const int qi = (int)(row / p.Hq), h = (int)(row % p.Hq);
-      if (qi >= nq) continue;
+      if (row >= rows || qi >= nq) continue;
       const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + 2 * lane;
       if (p.out_f16) {
         half2_t hv = {static_cast<_Float16>(res[r].x), static_cast<_Float16>(res[r].y)};
@@ -1372,14 +1411,17 @@ constexpr int kMaxDevices = 64;
 // tile kernel variants: 0, 1 = register kernel with NT = 1, 2 (16- and 32-row
 // tiles); 2 = shared kernel (64-row tiles); 3 = wide kernel (128-row tiles)
 constexpr int kMqVariants = 4;
+// query heads per KV head the kernels are built for, and their table index
+constexpr int kMqGroups = 5;
+constexpr int kMqGroupSizes[kMqGroups] = {1, 2, 4, 6, 8};
 struct MqDeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kMqVariants][2][2 * kMqWaves + 1] = {};   // [log2 G][variant][fp8][waves]
+  int wg_per_cu[kMqGroups][kMqVariants][2][2 * kMqWaves + 1] = {};   // [G index][variant][fp8][waves]
 };
 MqDeviceFacts g_mq_dev[kMaxDevices];
 
-int mq_log2(int x) { return x == 1 ? 0 : x == 2 ? 1 : x == 4 ? 2 : 3; }
+int mq_gidx(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 6 ? 3 : 4; }
 
 template <int G, bool kFp8>
 const void* mq_kernel_ptr_g(int variant) {
@@ -1397,6 +1439,7 @@ const void* mq_kernel_ptr_f(int G, int variant) {
     case 1: return mq_kernel_ptr_g<1, kFp8>(variant);
     case 2: return mq_kernel_ptr_g<2, kFp8>(variant);
     case 4: return mq_kernel_ptr_g<4, kFp8>(variant);
+    case 6: return mq_kernel_ptr_g<6, kFp8>(variant);
     default: return mq_kernel_ptr_g<8, kFp8>(variant);
   }
 }
@@ -1435,6 +1478,14 @@ int mq_tile_queries(int variant, int G) { return (16 << variant) / G; }
 
 bool mq_is_shared(int variant) { return variant >= 2; }
 
+// Dynamic LDS of a register-kernel launch with `waves` waves (two per KV head
+// of its group): the state one wave of each pair hands to the other.
+size_t mq_dyn_lds(int variant, int waves) {
+  if (mq_is_shared(variant)) return 0;
+  const int NT = variant + 1;
+  return (size_t)(waves / 2) * NT * (2 + 32) * kWave * sizeof(float);
+}
+
 // Runs of the unit stream: as many work-groups as fit on all CUs at once,
 // divided by the work-groups one run has (its head groups, or its KV heads).
 int mq_run_count(int G, int variant, int Hkv, bool fp8) {
@@ -1450,19 +1501,20 @@ int mq_run_count(int G, int variant, int Hkv, bool fp8) {
         cus <= 0)
       cus = 256;
     f.cus = cus;
-    for (int lg = 0; lg < 4; ++lg)
+    for (int lg = 0; lg < kMqGroups; ++lg)
       for (int v = 0; v < kMqVariants; ++v)
         for (int f8 = 0; f8 < 2; ++f8)
           for (int w = 1; w <= 2 * kMqWaves; ++w) {
             int n = 0;
             if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &n, mq_kernel_ptr(1 << lg, v, f8 != 0), w * kWave, 0) != hipSuccess ||
+                    &n, mq_kernel_ptr(kMqGroupSizes[lg], v, f8 != 0), w * kWave,
+                    mq_dyn_lds(v, w)) != hipSuccess ||
                 n <= 0)
               n = 1;
             f.wg_per_cu[lg][v][f8][w] = n;
           }
   });
-  return std::max(1, f.cus * f.wg_per_cu[mq_log2(G)][variant][fp8 ? 1 : 0][waves] / per_run);
+  return std::max(1, f.cus * f.wg_per_cu[mq_gidx(G)][variant][fp8 ? 1 : 0][waves] / per_run);
 }
 
 struct MqPlan {
@@ -1479,8 +1531,8 @@ int mq_check(int S, int T, int Hq, int Hkv, int D, int block_size, int max_block
   if (Hq <= 0 || Hkv <= 0) return fail(PDA_EINVAL, "Hq and Hkv must be > 0 (got %d, %d)", Hq, Hkv);
   if (Hq % Hkv != 0) return fail(PDA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built (1, 2, 4, 8 are)", G);
+  if (G != 1 && G != 2 && G != 4 && G != 6 && G != 8)
+    return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built (1, 2, 4, 6, 8 are)", G);
   if (Hkv > kMqMaxKvHeads)
     return fail(PDA_EUNSUPPORTED, "Hkv = %d above the maximum %d", Hkv, kMqMaxKvHeads);
   if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
@@ -1531,7 +1583,7 @@ void mq_launch_aux(bool plan, const MqParams& mp, const MqPlan& pl, hipStream_t 
   // one wave per kMergeRows rows of the at most n_runs - 1 cut tiles (the rows
   // of empty tiles, rare, are covered by the grid-stride loop)
   const long long merge_groups =
-      (long long)std::max(pl.n_runs - 1, 1) * Qt * mp.Hq / kMergeRows;
+      ((long long)std::max(pl.n_runs - 1, 1) * Qt * mp.Hq + kMergeRows - 1) / kMergeRows;
   hipLaunchKernelGGL((mq_merge_kernel<Qt>),
                      dim3((unsigned)std::min<long long>((merge_groups + 3) / 4, 1 << 20)),
                      dim3(256), 0, stream, mp);
@@ -1550,7 +1602,8 @@ void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((mq_reg_kernel<G, V + 1, kFp8>),
                        dim3((unsigned)(pl.n_runs * (mp.Hkv / pl.hg))),
-                       dim3((unsigned)(2 * pl.hg * kWave)), 0, stream, mp);
+                       dim3((unsigned)(2 * pl.hg * kWave)), (unsigned)mq_dyn_lds(V, 2 * pl.hg),
+                       stream, mp);
   }
   mq_launch_aux<Qt>(false, mp, pl, stream);
 }
@@ -1571,6 +1624,7 @@ void mq_launch_f(int G, const MqParams& mp, const MqPlan& pl, hipStream_t stream
     case 1: mq_launch<1, kFp8>(mp, pl, stream); break;
     case 2: mq_launch<2, kFp8>(mp, pl, stream); break;
     case 4: mq_launch<4, kFp8>(mp, pl, stream); break;
+    case 6: mq_launch<6, kFp8>(mp, pl, stream); break;
     default: mq_launch<8, kFp8>(mp, pl, stream); break;
   }
 }

@@ -84,7 +84,7 @@ namespace {
 
 using namespace pda;
 
-constexpr int kMaxKvHeads = 8;        // one wave per KV head
+constexpr int kMaxKvHeads = 64;       // one wave per KV head; head groups of up to 4 per work-group
 #ifndef PDA_MAX_WAVES_PER_WG
 #define PDA_MAX_WAVES_PER_WG 4
 #endif
@@ -721,15 +721,20 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams p) {
 // Kernel kinds: 0 = fp16, 1 = FP8, 2 = fp16 and 3 = FP8 with the fused append.
 constexpr int kMaxDevices = 64;
 constexpr int kKinds = 4;
+constexpr int kGroups = 5;
 struct DeviceFacts {
   std::once_flag once;
   int cus = 0;
-  int wg_per_cu[4][kKinds][kMaxWavesPerWG + 1] = {};   // [log2 G][kind][waves per work-group]
-  int lds_pad[4][kKinds][kMaxWavesPerWG + 1] = {};     // dynamic LDS bytes per launch
+  int wg_per_cu[kGroups][kKinds][kMaxWavesPerWG + 1] = {};   // [group index][kind][waves per WG]
+  int lds_pad[kGroups][kKinds][kMaxWavesPerWG + 1] = {};     // dynamic LDS bytes per launch
 };
 DeviceFacts g_dev[kMaxDevices];
 
-int log2_group(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
+// The query heads per KV head the split kernel is built for, and their index
+// in the per-device tables.
+constexpr int kGroupSizes[kGroups] = {1, 2, 4, 6, 8};
+int group_index(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 6 ? 3 : 4; }
+bool group_built(int G) { return G == 1 || G == 2 || G == 4 || G == 6 || G == 8; }
 
 int kernel_kind(bool fp8, bool append) { return (fp8 ? 1 : 0) + (append ? 2 : 0); }
 
@@ -739,6 +744,7 @@ const void* split_kernel_ptr(int G, int kind) {
       case 1: return reinterpret_cast<const void*>(&split_kernel<1, true, true>);
       case 2: return reinterpret_cast<const void*>(&split_kernel<2, true, true>);
       case 4: return reinterpret_cast<const void*>(&split_kernel<4, true, true>);
+      case 6: return reinterpret_cast<const void*>(&split_kernel<6, true, true>);
       default: return reinterpret_cast<const void*>(&split_kernel<8, true, true>);
     }
   }
@@ -747,6 +753,7 @@ const void* split_kernel_ptr(int G, int kind) {
       case 1: return reinterpret_cast<const void*>(&split_kernel<1, false, true>);
       case 2: return reinterpret_cast<const void*>(&split_kernel<2, false, true>);
       case 4: return reinterpret_cast<const void*>(&split_kernel<4, false, true>);
+      case 6: return reinterpret_cast<const void*>(&split_kernel<6, false, true>);
       default: return reinterpret_cast<const void*>(&split_kernel<8, false, true>);
     }
   }
@@ -755,6 +762,7 @@ const void* split_kernel_ptr(int G, int kind) {
       case 1: return reinterpret_cast<const void*>(&split_kernel<1, true>);
       case 2: return reinterpret_cast<const void*>(&split_kernel<2, true>);
       case 4: return reinterpret_cast<const void*>(&split_kernel<4, true>);
+      case 6: return reinterpret_cast<const void*>(&split_kernel<6, true>);
       default: return reinterpret_cast<const void*>(&split_kernel<8, true>);
     }
   }
@@ -762,6 +770,7 @@ const void* split_kernel_ptr(int G, int kind) {
     case 1: return reinterpret_cast<const void*>(&split_kernel<1, false>);
     case 2: return reinterpret_cast<const void*>(&split_kernel<2, false>);
     case 4: return reinterpret_cast<const void*>(&split_kernel<4, false>);
+    case 6: return reinterpret_cast<const void*>(&split_kernel<6, false>);
     default: return reinterpret_cast<const void*>(&split_kernel<8, false>);
   }
 }
@@ -800,15 +809,15 @@ void device_facts(DeviceFacts& f, int dev) {
       hipSuccess)
     lds_wg = 0;
   f.cus = cus;
-  for (int lg = 0; lg < 4; ++lg)
+  for (int lg = 0; lg < kGroups; ++lg)
     for (int kd = 0; kd < kKinds; ++kd)
       for (int w = 1; w <= kMaxWavesPerWG; ++w) {
-        const void* fn = split_kernel_ptr(1 << lg, kd);
+        const void* fn = split_kernel_ptr(kGroupSizes[lg], kd);
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, w * kWave, 0) != hipSuccess ||
             n <= 0)
           n = 1;
-        const int pad = occupancy_pad(1 << lg, kd, w, lds_cu, lds_wg, n);
+        const int pad = occupancy_pad(kGroupSizes[lg], kd, w, lds_cu, lds_wg, n);
         if (pad > 0) {
           int m = 0;
           if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, fn, w * kWave, pad) == hipSuccess &&
@@ -834,12 +843,12 @@ int run_count(int G, int Hkv, int kind) {
   const int n_hgroups = Hkv / hg;
   const DeviceFacts* f = facts();
   if (!f) return 1024 / n_hgroups;  // no device: a fixed size keeps sizing queries usable
-  return std::max(1, f->cus * f->wg_per_cu[log2_group(G)][kind][hg] / n_hgroups);
+  return std::max(1, f->cus * f->wg_per_cu[group_index(G)][kind][hg] / n_hgroups);
 }
 
 int lds_pad(int G, int Hkv, int kind) {
   const DeviceFacts* f = facts();
-  return f ? f->lds_pad[log2_group(G)][kind][head_group(Hkv)] : 0;
+  return f ? f->lds_pad[group_index(G)][kind][head_group(Hkv)] : 0;
 }
 
 struct Plan {
@@ -856,8 +865,8 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
   if (Hq <= 0 || Hkv <= 0) return fail(PDA_EINVAL, "Hq and Hkv must be > 0 (got %d, %d)", Hq, Hkv);
   if (Hq % Hkv != 0) return fail(PDA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built (1, 2, 4, 8 are)", G);
+  if (!group_built(G))
+    return fail(PDA_EUNSUPPORTED, "Hq/Hkv = %d not built (1, 2, 4, 6, 8 are)", G);
   if (Hkv > kMaxKvHeads)
     return fail(PDA_EUNSUPPORTED, "Hkv = %d above the maximum %d", Hkv, kMaxKvHeads);
   if (D != kD) return fail(PDA_EUNSUPPORTED, "head dim %d not built (128 is)", D);
@@ -985,6 +994,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
       case 1: hipLaunchKernelGGL((split_kernel<1, true, true>), grid, block, pad, stream, sp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, true, true>), grid, block, pad, stream, sp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, true, true>), grid, block, pad, stream, sp); break;
+      case 6: hipLaunchKernelGGL((split_kernel<6, true, true>), grid, block, pad, stream, sp); break;
       default: hipLaunchKernelGGL((split_kernel<8, true, true>), grid, block, pad, stream, sp); break;
     }
   } else if (fp8) {
@@ -992,6 +1002,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
       case 1: hipLaunchKernelGGL((split_kernel<1, true>), grid, block, pad, stream, sp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, true>), grid, block, pad, stream, sp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, true>), grid, block, pad, stream, sp); break;
+      case 6: hipLaunchKernelGGL((split_kernel<6, true>), grid, block, pad, stream, sp); break;
       default: hipLaunchKernelGGL((split_kernel<8, true>), grid, block, pad, stream, sp); break;
     }
   } else if (append) {
@@ -999,6 +1010,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
       case 1: hipLaunchKernelGGL((split_kernel<1, false, true>), grid, block, pad, stream, sp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, false, true>), grid, block, pad, stream, sp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, false, true>), grid, block, pad, stream, sp); break;
+      case 6: hipLaunchKernelGGL((split_kernel<6, false, true>), grid, block, pad, stream, sp); break;
       default: hipLaunchKernelGGL((split_kernel<8, false, true>), grid, block, pad, stream, sp); break;
     }
   } else {
@@ -1006,6 +1018,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
       case 1: hipLaunchKernelGGL((split_kernel<1, false>), grid, block, pad, stream, sp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, false>), grid, block, pad, stream, sp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, false>), grid, block, pad, stream, sp); break;
+      case 6: hipLaunchKernelGGL((split_kernel<6, false>), grid, block, pad, stream, sp); break;
       default: hipLaunchKernelGGL((split_kernel<8, false>), grid, block, pad, stream, sp); break;
     }
   }

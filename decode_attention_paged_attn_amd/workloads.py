@@ -262,12 +262,20 @@ def agentic_lengths(rng, B=16, median=80 * K1, sigma=0.42, lo=8 * K1, hi=200 * K
     return np.clip(np.rint(np.exp(math.log(median) + sigma * z)), lo, hi).astype(np.int64)
 
 
-def agentic_80k(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
-    """Long-context agentic decode: batch 16, 32/8 heads, P = 512 partitions."""
+def agentic_80k(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16", heads=(32, 8)):
+    """Long-context agentic decode: batch 16, 32/8 heads, P = 512 partitions.
+
+    ``heads`` = (Hq, Hkv) gives the other head shapes the KernelFlume paper
+    evaluates (§6.3): GQA Q48:KV8, Q64:KV8 and MHA Q32:KV32, Q40:KV40,
+    Q48:KV48, on the same lengths.
+    """
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = agentic_lengths(rng)
-    return build_case(lens, 32, 8, seed=seed, device=device, rng=rng, kv_dtype=kv_dtype,
-                      rng_backend=rng_backend, name="agentic_b16_median80k" + _suffix(kv_dtype),
+    Hq, Hkv = heads
+    shape = "" if (Hq, Hkv) == (32, 8) else f"_q{Hq}kv{Hkv}"
+    return build_case(lens, Hq, Hkv, seed=seed, device=device, rng=rng, kv_dtype=kv_dtype,
+                      rng_backend=rng_backend,
+                      name="agentic_b16_median80k" + shape + _suffix(kv_dtype),
                       partition_tokens=512)
 
 
@@ -543,10 +551,22 @@ def shared_prefix(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
                               name="cascade_g4x50_prefix16k_suffix1k" + _suffix(kv_dtype))
 
 
+def _agentic_heads(Hq, Hkv):
+    def make(seed=0, device="cpu", rng_backend="torch", kv_dtype="fp16"):
+        return agentic_80k(seed, device, rng_backend, kv_dtype, heads=(Hq, Hkv))
+    make.__doc__ = f"The agentic batch at Q{Hq}:KV{Hkv} heads."
+    return make
+
+
 CONFIGS = {
     "tiny": tiny,
     "llama8b_4k": llama8b_4k,
     "agentic_80k": agentic_80k,
+    "agentic_80k_q48kv8": _agentic_heads(48, 8),
+    "agentic_80k_q64kv8": _agentic_heads(64, 8),
+    "agentic_80k_q32kv32": _agentic_heads(32, 32),
+    "agentic_80k_q40kv40": _agentic_heads(40, 40),
+    "agentic_80k_q48kv48": _agentic_heads(48, 48),
     "ragged_mixed": ragged_mixed,
     "disagg_merge": disagg_merge,
 }

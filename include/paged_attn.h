@@ -36,8 +36,10 @@
  * Asynchronous Overlap"; logical block i holds tokens 16i .. 16i+15 (figure
  * "Virtual Sequence Address Space" on that page).
  *
- * Supported shapes: D = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 8},
- * Hkv <= 8.  Other shapes return PDA_EUNSUPPORTED.
+ * Supported shapes: D = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 6, 8},
+ * 1 <= Hkv <= 64.  This covers the head configurations the KernelFlume paper
+ * evaluates (§6.3): GQA Q32:KV8, Q48:KV8, Q64:KV8 and MHA Q32:KV32, Q40:KV40,
+ * Q48:KV48.  Other shapes return PDA_EUNSUPPORTED.
  *
  * Conventions
  * -----------
@@ -387,7 +389,7 @@ int paged_decode_attn_append_fp8(void* out, const void* q, const void* k_new,
  * workspace    device memory of at least pda_multi_query_workspace_size()
  *              bytes, 256-byte aligned; it holds the schedule and partials.
  * Shapes as for paged_decode_attn (D = 128, block_size = 16, Hq / Hkv in
- * {1, 2, 4, 8}, Hkv <= 8), and S <= 4000.  pda_multi_query_workspace_size
+ * {1, 2, 4, 6, 8}, Hkv <= 64), and S <= 4000.  pda_multi_query_workspace_size
  * covers both cache formats.
  *
  * Cascade attention for B decode requests in R groups that share a prefix

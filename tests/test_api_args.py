@@ -60,7 +60,8 @@ def _ws(B=2, Hq=8, Hkv=2, D=128, bs=16, mb=32, P=0):
     (dict(P=24), 1),               # not a multiple of the block size
     (dict(P=-16), 1),
     (dict(P=1 << 21), 2),          # above the largest unit
-    (dict(Hq=32, Hkv=16), 2),      # more KV heads than waves in a work-group
+    (dict(Hq=12, Hkv=4), 2),       # G = 3 not built (1, 2, 4, 6, 8 are)
+    (dict(Hq=128, Hkv=128), 2),    # more than 64 KV heads
     (dict(B=-1), 1),
     (dict(mb=-1), 1),
     (dict(Hkv=0), 1),
@@ -91,6 +92,18 @@ def test_decode_workspace_size_covers_every_kv_head_count(lib):
     assert lib.paged_decode_attn_workspace_size(2, 8, 128, 16, 4, 24, ctypes.byref(n)) == 1
     assert lib.paged_decode_attn_workspace_size(2, 0, 128, 16, 4, 0, ctypes.byref(n)) == 1
     assert lib.paged_decode_attn_workspace_size(2, 8, 128, 16, 4, 0, None) == 1
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (48, 8), (64, 8), (32, 32), (40, 40), (48, 48),
+                                   (12, 3), (10, 5), (6, 6), (56, 7), (30, 5)])
+def test_workspace_size_accepts_the_head_shapes(lib, Hq, Hkv):
+    """The pages' GQA (Q32:KV8, Q48:KV8, Q64:KV8) and MHA (Q32:KV32, Q40:KV40,
+    Q48:KV48) shapes, and odd KV-head counts, are built."""
+    rc, n = _ws(B=4, Hq=Hq, Hkv=Hkv, mb=64)
+    assert rc == 0 and n > 0
+    c = ctypes.c_size_t(0)
+    assert lib.pda_multi_query_workspace_size(4, 20, Hq, Hkv, 128, 16, 64, 0,
+                                              ctypes.byref(c)) == 0 and c.value > 0
 
 
 def test_workspace_size_formula(lib):
@@ -201,7 +214,7 @@ def _mq_ws(S=3, T=9, Hq=8, Hkv=2, D=128, bs=16, mb=32, P=0):
     (dict(T=-1), 1),
     (dict(Hq=12, Hkv=4), 2),       # G = 3 not built
     (dict(Hq=7, Hkv=2), 1),        # Hq % Hkv != 0
-    (dict(Hq=16, Hkv=16), 2),      # more than 8 KV heads
+    (dict(Hq=128, Hkv=128), 2),    # more than 64 KV heads
     (dict(Hq=0), 1),
     (dict(D=64), 2),
     (dict(bs=32), 2),

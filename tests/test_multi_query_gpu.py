@@ -66,7 +66,13 @@ SMALL_LENS = [0, 1, 5, 16, 17, 40, 100, 257, 600, 33]
 SMALL_NQ = [2, 1, 8, 3, 0, 17, 5, 33, 64, 1]
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+# the pages' GQA and MHA head shapes (Q32:KV8, Q48:KV8, Q64:KV8; Q32:KV32,
+# Q40:KV40, Q48:KV48) and small or odd KV-head counts
+SHAPES = [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8), (6, 8), (8, 8), (6, 1), (1, 32), (1, 40),
+          (1, 48), (4, 3), (2, 5), (1, 6), (8, 7), (6, 5)]
+
+
+@pytest.mark.parametrize("G,Hkv", SHAPES)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("P", [0, 32, 256])
 def test_small_all_group_sizes(G, Hkv, causal, P):
@@ -87,7 +93,7 @@ VARIANT_ROWS = {"register16": 12, "register32": 28, "shared64": 48, "wide128": 2
                 "wide128_part": 100}   # 100 rows: the last wave of a tile is partly used
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (6, 8), (6, 1), (1, 40)])
 @pytest.mark.parametrize("variant", sorted(VARIANT_ROWS))
 @pytest.mark.parametrize("causal", [True, False])
 def test_tile_kernel_variants(G, Hkv, variant, causal):
@@ -148,6 +154,31 @@ def test_wide_runs_across_many_tiles(kv_dtype, causal):
         out, lse = run_mq(case, P)
         compare_out(to_np(out), ref)
         compare_lse(to_np(lse), ref_lse)
+
+
+# The register kernel folds each run in two halves (two waves per KV head) and
+# combines them through LDS when the split falls inside one tile.  That needs
+# runs of two or more units: one long sequence makes them long, and a few short
+# ones (at most 32 rows each, so the register kernel is picked) sit around it.
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("G,Hkv", [(4, 1), (2, 2), (4, 3), (4, 8), (6, 5)])
+def test_register_kernel_halves_combined(kv_dtype, causal, G, Hkv):
+    rows = 32 if G != 6 else 30
+    nq_long = rows // G
+    lens = [7, 20000, 40, 3, 900]
+    nq = [1, nq_long, 2, 3, max(1, nq_long - 1)]
+    case = W.build_mq_case(lens, nq, G * Hkv, Hkv, causal=causal, seed=95 + G + Hkv,
+                           device="cuda", name=f"mq_reg_halves_G{G}_{Hkv}", kv_dtype=kv_dtype)
+    ws = torch.zeros(pda.multi_query_workspace_size(case.S, case.T, case.Hq, case.Hkv,
+                                                    case.block_table.shape[1], 16),
+                     dtype=torch.uint8, device="cuda")
+    out, lse = run_mq(case, 16, workspace=ws)
+    hdr = ws[:32].cpu().view(torch.int32).numpy()
+    assert hdr[0] >= 2, f"runs of {hdr[0]} units: the two halves never share a tile"
+    ref, ref_lse = oracle_mq(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
 
 
 @pytest.mark.parametrize("P", [0, 64])
@@ -215,7 +246,7 @@ def test_graph_capture_replays_match_eager():
 
 # --- FP8 (E4M3) cache -------------------------------------------------------------
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("G,Hkv", SHAPES)
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_small_all_group_sizes(G, Hkv, causal):
     case = W.build_mq_case(SMALL_LENS, SMALL_NQ, G * Hkv, Hkv, causal=causal, seed=140 + G,
@@ -227,7 +258,7 @@ def test_fp8_small_all_group_sizes(G, Hkv, causal):
         compare_lse(to_np(lse), ref_lse)
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (6, 8), (6, 1)])
 @pytest.mark.parametrize("variant", sorted(VARIANT_ROWS))
 def test_fp8_tile_kernel_variants(G, Hkv, variant):
     per_seq = max(1, VARIANT_ROWS[variant] // G)
@@ -299,7 +330,7 @@ def test_cascade_page_example_shape():
     compare_lse(to_np(lse), ref_lse)
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (6, 8), (1, 40)])
 def test_cascade_groups_and_edges(G, Hkv):
     # group 2 has an empty prefix; some requests have no suffix
     c = W.build_cascade_case([64, 37, 0, 16], [3, 5, 2, 1], [5, 0, 17, 16, 1, 40, 0, 3, 9, 0, 2],
@@ -310,7 +341,7 @@ def test_cascade_groups_and_edges(G, Hkv):
     compare_lse(to_np(lse), ref_lse)
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (6, 8)])
 def test_cascade_fp8(G, Hkv):
     c = W.build_cascade_case([64, 37, 0, 16], [3, 5, 2, 1], [5, 0, 17, 16, 1, 40, 0, 3, 9, 0, 2],
                              G * Hkv, Hkv, seed=148 + G, device="cuda",

@@ -74,7 +74,14 @@ def test_tiny_workload(P):
 RAGGED = [1, 2, 15, 16, 17, 31, 33, 100, 255, 256, 257, 511, 512, 513, 1000, 1537]
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+# Group sizes and KV-head counts: the pages' GQA shapes Q32:KV8, Q48:KV8 and
+# Q64:KV8 (G = 4, 6, 8 at 8 KV heads) and MHA Q32:KV32, Q40:KV40, Q48:KV48,
+# plus small and odd KV-head counts (work-groups of 1 to 4 KV heads).
+SHAPES = [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8), (6, 8), (8, 8), (6, 1), (1, 32), (1, 40),
+          (1, 48), (4, 3), (2, 5), (1, 6), (8, 7), (6, 5)]
+
+
+@pytest.mark.parametrize("G,Hkv", SHAPES)
 @pytest.mark.parametrize("P", [0, 32, 256])
 def test_ragged_lengths_all_group_sizes(G, Hkv, P):
     case = W.build_case(RAGGED, G * Hkv, Hkv, pool_blocks=sum(-(-n // 16) for n in RAGGED) + 7,
@@ -200,10 +207,11 @@ def test_split_partials_in_workspace(P):
     compare_lse(to_np(lse), ref_lse)
 
 
-def test_partial_api_and_merge():
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (48, 8), (64, 8), (40, 40)])
+def test_partial_api_and_merge(Hq, Hkv):
     R, per = 4, 256
     lens = [R * per] * 3
-    case = W.build_case(lens, 32, 8, seed=9, device="cuda")
+    case = W.build_case(lens, Hq, Hkv, seed=9, device="cuda")
     cols = per // 16
     o_parts, l_parts = [], []
     for r in range(R):
@@ -302,7 +310,8 @@ def _check_every_sequence(case, results, chunk_tokens=1 << 18):
 
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
 @pytest.mark.parametrize("name,P", [("llama8b_4k", 0), ("agentic_80k", 512), ("agentic_80k", 0),
-                                    ("ragged_mixed", 0)])
+                                    ("ragged_mixed", 0), ("agentic_80k_q48kv8", 512),
+                                    ("agentic_80k_q40kv40", 512)])
 def test_full_size_workload(name, P, kv_dtype):
     case = W.CONFIGS[name](device="cuda", kv_dtype=kv_dtype)
     out, lse = run(case, P)
@@ -406,7 +415,7 @@ def test_fp8_tiny_workload(P):
     compare_lse(to_np(lse), ref_lse)
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("G,Hkv", SHAPES)
 def test_fp8_ragged_lengths(G, Hkv):
     case = W.build_case(RAGGED, G * Hkv, Hkv, pool_blocks=sum(-(-n // 16) for n in RAGGED) + 7,
                         seed=200 + G, device="cuda", name=f"ragged_fp8_G{G}", kv_dtype="fp8")
@@ -550,7 +559,8 @@ def _fused_vs_separate(case, kn, vn, P=0, **kw):
     return out_f, lse_f
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1), (4, 8), (6, 8), (1, 40),
+                                   (2, 5)])
 @pytest.mark.parametrize("P", [0, 32, 512])
 def test_fused_append_equals_append_then_attend(G, Hkv, P):
     lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257, 1000]
@@ -614,7 +624,7 @@ def test_fp8_kv_append_then_attend(Hq, Hkv):
     compare_lse(to_np(lse)[keep], ref_lse[keep])
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (4, 8)])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1), (4, 8), (6, 8), (1, 48), (4, 3)])
 @pytest.mark.parametrize("P", [0, 64])
 def test_fp8_fused_append_equals_append_then_attend(G, Hkv, P):
     lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 100, 256, 257, 1000]
@@ -655,8 +665,8 @@ def test_stream_read_reads_without_writing(nbytes):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("G", [1, 2, 4, 8])
-@pytest.mark.parametrize("Hkv", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 6, 8])
+@pytest.mark.parametrize("Hkv", [1, 2, 4, 8, 32, 40, 48])
 def test_split_kernel_runs_at_the_tuned_occupancy(fp8, G, Hkv):
     """The schedule fills every CU with exactly the tuned waves per SIMD (the
     launch pads LDS when a kernel's registers would let more in): 1 for fp16
