@@ -502,9 +502,10 @@ def bench_cascade(case, steps, warmup):
                    "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}), flush=True)
 
 
-def measure_partial_merge(case, steps, warmup):
+def measure_partial_merge(case, steps, warmup, single_pass=True):
     """R range partials (paged_decode_attn_partial on block-table column slices)
-    + merge_partials per step, and the single pass over the same batch."""
+    + merge_partials per step, and (single_pass) the single pass over the same
+    batch."""
     import torch
     import decode_attention_paged_attn_amd as pda
     from decode_attention_paged_attn_amd import workloads as W
@@ -531,9 +532,10 @@ def measure_partial_merge(case, steps, warmup):
                               **kw)
 
     wall_ms, ev_ms, _ = _time_events(split_path, steps, warmup)
-    s_wall, s_ev, _ = _time_events(single, steps, warmup)
+    s_ev = _time_events(single, steps, warmup)[1] if single_pass else float("nan")
     nbytes = kv_bytes(case.lens, case.Hkv, elem=case.kv_bytes_per_elem)
     return {"value": round(nbytes / (wall_ms / 1e3) / 1e9, 2), "unit": "GB/s",
+            "traffic": measured_traffic(f"disagg_merge_partial/{case.kv_dtype}"),
             "pct_hbm_peak": round(100.0 * nbytes / (wall_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
             "event_GBps": round(nbytes / (ev_ms / 1e3) / 1e9, 2),
             "ms_per_step": round(wall_ms, 5), "event_ms": round(ev_ms, 5),
@@ -545,10 +547,10 @@ def measure_partial_merge(case, steps, warmup):
             "split_over_single_time": round(ev_ms / s_ev, 4)}
 
 
-def bench_partial_merge(case, steps, warmup):
+def bench_partial_merge(case, steps, warmup, single_pass=True):
     """R range partials (paged_decode_attn_partial over block-table column slices)
     plus merge_partials, against single-pass attention over the same batch."""
-    m = measure_partial_merge(case, steps, warmup)
+    m = measure_partial_merge(case, steps, warmup, single_pass)
     nbytes = m["kv_bytes_per_step"]
     ev_ms = m["event_ms"]
     print(json.dumps({
@@ -562,7 +564,7 @@ def bench_partial_merge(case, steps, warmup):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(m["event_GBps"] / HBM_PEAK_GBS, 4),
                      "kernel": "R partial calls + merge_partials",
-                     "traffic": measured_traffic(f"disagg_merge_partial/{case.kv_dtype}")},
+                     "traffic": m["traffic"]},
         "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S, "dtype": case.kv_dtype,
         "data": "synthetic",
         "config": {"workload": case.name, "batch": case.B, "q_heads": case.Hq,
@@ -647,6 +649,8 @@ def main():
                          "--config spec_verify or chunked_prefill; cascade: "
                          "cascade_decode_attn on --config shared_prefix; partial_merge: 4 range "
                          "partials + merge_partials on disagg_merge, against single pass")
+    ap.add_argument("--partial-only", action="store_true",
+                    help="--op partial_merge: time only the partials + merge (no single pass)")
     ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
                     help="element type of the K/V cache (fp8: E4M3 codes with per-tensor scales)")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -684,7 +688,7 @@ def main():
         return
     if args.op == "partial_merge":
         bench_partial_merge(W.disagg_merge(device="cuda", kv_dtype=args.kv_dtype), args.steps,
-                            args.warmup)
+                            args.warmup, single_pass=not args.partial_only)
         return
     case = W.CONFIGS[args.config](device="cuda", kv_dtype=args.kv_dtype)
     if args.op == "append":

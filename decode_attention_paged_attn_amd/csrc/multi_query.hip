@@ -1000,10 +1000,16 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
   f32x16 sc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sc[r] = 0.0f;
+  // every K read of the sub-step goes out before the first MFMA, so the LDS
+  // latency is paid once (fp16 chunked prefill -1%)
   if constexpr (kFp8) {
+    u32x4 kw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      kw[j] = *reinterpret_cast<const u32x4*>(kstage + wide_at<true>(n, 4 * hf + j));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kstage + wide_at<true>(n, 4 * hf + j));
+      const u32x4 w = kw[j];
       half8_t kop[2];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1018,12 +1024,15 @@ __device__ __forceinline__ f32x16 wide_qk(const half8_t (&qb)[8], const char* ks
       sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[1], qb[2 * j + 1], sc, 0, 0, 0);
     }
   } else {
+    half8_t kop[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const half8_t kop =
-          *reinterpret_cast<const half8_t*>(kstage + wide_at<false>(n, 8 * hf + kk));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qb[kk], sc, 0, 0, 0);
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      kop[kk] = *reinterpret_cast<const half8_t*>(kstage + wide_at<false>(n, 8 * hf + kk));
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[kk], qb[kk], sc, 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 LDS reads, then
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // the 8 MFMAs
   }
   return sc;
 }
@@ -1082,6 +1091,16 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
   float ps = 0.0f;
 #pragma unroll
   for (int j = 0; j < kNS; ++j) {
+    const int valid = tok_hi - t0 - 32 * j;
+    // fp16: both chunks' V operands first, their LDS reads overlapping the
+    // exponentials (chunked prefill 616 -> 586 us); FP8 decodes its operands
+    // with VALU work of its own and reads them per chunk (574 vs 556 us)
+    half8_t vb[2][4];
+    if constexpr (!kFp8) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, voff, c, hf, valid, vb[c]);
+    }
     float pr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1090,18 +1109,16 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
     }
 #pragma unroll
     for (int r = 0; r < 16; r += 4) ps += (pr[r] + pr[r + 1]) + (pr[r + 2] + pr[r + 3]);
-    const int valid = tok_hi - t0 - 32 * j;
     if constexpr (wide_prio_pv<kFp8>()) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       half8_t pa;
 #pragma unroll
       for (int t = 0; t < 8; ++t) pa[t] = static_cast<_Float16>(pr[8 * c + t]);
-      half8_t vb[4];
-      wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, voff, c, hf, valid, vb);
+      if constexpr (kFp8) wide_v_operands<kMasked, kFp8>(vstage + 32 * j * kRow, voff, c, hf, valid, vb[c]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[u], st.acc[u], 0, 0, 0);
+        st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa, vb[c][u], st.acc[u], 0, 0, 0);
     }
     if constexpr (wide_prio_pv<kFp8>()) __builtin_amdgcn_s_setprio(0);
   }
