@@ -386,8 +386,25 @@ __device__ __forceinline__ void mq_v_operands(const typename KvFmt<kFp8>::VRow (
 // before min(base + qi, n_seq, tok_hi) when causal, before tok_hi otherwise;
 // rows past the tile's queries see everything and are never stored.  Tokens at
 // or past t0 + nvalid are exact zeros.
-template <int G, int NT, bool kMasked, bool kFp8>
-__device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4],
+// Where a fold finds the Q operands of row block b, chunk i: registers, or an
+// LDS copy [b][i][lane] shared by the waves of a work-group (read at every
+// block, so that only one row block's operands are live at a time).
+template <int NT>
+struct MqQRegs {
+  const half8_t (&qa)[NT][4];
+  __device__ __forceinline__ half8_t get(int b, int i) const { return qa[b][i]; }
+};
+typedef __attribute__((address_space(3))) u32x4 LdsU32x4;
+struct MqQLds {
+  const LdsU32x4* base;
+  int lane;
+  __device__ __forceinline__ half8_t get(int b, int i) const {
+    return __builtin_bit_cast(half8_t, base[(b * 4 + i) * kWave + lane]);
+  }
+};
+
+template <int G, int NT, bool kMasked, bool kFp8, typename QSrc>
+__device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const QSrc& qa,
                                         const u32x4 (&kr)[KvFmt<kFp8>::kKLoads],
                                         const typename KvFmt<kFp8>::VRow (&vr)[4],
                                         float qk_scale, int lane, int row0, int t0, int nvalid,
@@ -403,7 +420,7 @@ __device__ __forceinline__ void mq_fold(MqSeg<NT>& st, const half8_t (&qa)[NT][4
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[i], qa[b][i], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[i], qa.get(b, i), sc, 0, 0, 0);
     float sv[4];
     if (kMasked) {
       const int qi = (row0 + 16 * b + n) / G;
@@ -558,19 +575,23 @@ struct BlockWindow {
 // register kernel: two waves per KV head (halves of the run), a tile of one
 // or two 16-row blocks per wave
 
-template <int G, int NT, bool kFp8>
-__device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
-                               bool whole, int slot, MqSeg<NT>& st, bool defer) {
+// Folds tokens [tok_lo, tok_hi) of sequence s into st for the tile of nq
+// queries from row q0 (causal: query qi sees base + qi tokens), KV head g.
+// With qlds (the tile's Q operands in LDS, [b][i][lane]) the operands are read
+// there at every block instead of held in registers.
+template <int G, int NT, bool kFp8, bool kQLds = false>
+__device__ __forceinline__ void mq_reg_fold(const MqParams& p, int lane, int g, int s, int q0,
+                                            int nq, int base, int tok_lo, int tok_hi,
+                                            MqSeg<NT>& st, const LdsU32x4* qlds = nullptr) {
   using Fmt = KvFmt<kFp8>;
   using VRow = typename Fmt::VRow;
   constexpr int E = Fmt::kElemBytes;
   constexpr int KL = Fmt::kKLoads;
-  constexpr int Qt = 16 * NT / G;
   const int c = lane >> 4, t = lane & 15;
-  const int s = p.t_seq[i], q0 = p.t_q0[i], nq = p.t_nq[i], base = p.t_base[i];
   const int n = mq_seq_len(p, s);
   half8_t qa[NT][4];
-  mq_load_q<G, NT, kFp8>(p, g, q0, nq, 0, lane, qa);
+  if constexpr (!kQLds) mq_load_q<G, NT, kFp8>(p, g, q0, nq, 0, lane, qa);
+  unsigned qoff = 0;
   // blocks wholly before the tile's first query's end skip the mask
   const int causal_base = p.causal ? base : kNoMask;
   const int full_end = p.causal ? min(min(max(base, 0), n), tok_hi) : tok_hi;
@@ -607,14 +628,32 @@ __device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int 
       const int nxt = cur + NB - 1;
       if (nxt < nblk) load(win.offset(nxt), kbuf[(sl + NB - 1) % NB], vbuf[(sl + NB - 1) % NB]);
       const int t0 = tok_lo + cur * kBS;
-      if (t0 + kBS > full_end)
-        mq_fold<G, NT, true, kFp8>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0,
-                                   tok_hi - t0, causal_base, n, nq, tok_hi);
-      else
-        mq_fold<G, NT, false, kFp8>(st, qa, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0, kBS,
-                                    causal_base, n, nq, tok_hi);
+      auto fold = [&](const auto& qsrc) {
+        if (t0 + kBS > full_end)
+          mq_fold<G, NT, true, kFp8>(st, qsrc, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0,
+                                     tok_hi - t0, causal_base, n, nq, tok_hi);
+        else
+          mq_fold<G, NT, false, kFp8>(st, qsrc, kbuf[sl], vbuf[sl], p.qk_scale, lane, 0, t0,
+                                      kBS, causal_base, n, nq, tok_hi);
+      };
+      // opaque: LDS reads of Q stay in the loop, not hoisted into registers
+      if constexpr (kQLds) asm volatile("" : "+v"(qoff));
+      if constexpr (kQLds) {
+        fold(MqQLds{(const LdsU32x4*)((const __attribute__((address_space(3))) char*)qlds + qoff),
+                    lane});
+      } else {
+        fold(MqQRegs<NT>{qa});
+      }
     }
   }
+}
+
+template <int G, int NT, bool kFp8>
+__device__ __forceinline__ void mq_reg_segment(const MqParams& p, int lane, int g, int i, int tok_lo, int tok_hi,
+                               bool whole, int slot, MqSeg<NT>& st, bool defer) {
+  constexpr int Qt = 16 * NT / G;
+  const int q0 = p.t_q0[i], nq = p.t_nq[i];
+  mq_reg_fold<G, NT, kFp8>(p, lane, g, p.t_seq[i], q0, nq, p.t_base[i], tok_lo, tok_hi, st);
   if (!defer) mq_store<G, NT, Qt, kFp8>(p, st, g, q0, nq, 0, lane, whole, slot);
 }
 
@@ -695,6 +734,204 @@ void mq_reg_kernel(MqParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// whole-tile register kernel (fp16 cache): one work-group of kTileParts waves
+// per (tile, KV head).  Wave j folds part j of the tile's blocks (as the
+// register kernel folds a run), the parts' softmax states meet in LDS, and the
+// work-group finishes the rows and writes them: no plan, no partials, no
+// merge.  The work-group finds its tile itself from query_start.
+
+constexpr int kTileParts = 8;
+constexpr int kTileMaxTokens = 8192;  // longest context the host sends this way
+constexpr int kTileMaxGroups = 1 << 20;
+
+// dynamic LDS of a whole-tile launch: each part's accumulators (NT x 4
+// registers x 64 lanes x 8 floats), then its row max and sum (NT x 2 x 16),
+// then the tile's Q operands (NT x 4 chunks x 64 lanes x 16 bytes)
+constexpr size_t mq_tile_state_floats(int NT) {
+  return (size_t)kTileParts * NT * (4 * kWave * 8 + 2 * 16);
+}
+constexpr size_t mq_tile_lds(int NT) {
+  return mq_tile_state_floats(NT) * sizeof(float) + (size_t)NT * 4 * kWave * 16;
+}
+
+// Tile i of the call (sequence s owns tiles toff[s] .. toff[s] + nt_s - 1,
+// nt_s = ceil(queries of s / Qt)): its sequence and its rank in it, found by
+// one pass of the work-group over query_start.  False when the call has no
+// tile i.  sh: 10 ints of LDS.  Every thread calls it.
+template <int Qt>
+__device__ bool mq_find_tile(const MqParams& p, int i, int* sh, int& s_out, int& j_out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  constexpr int kThreads = kWave * kTileParts;
+  if (tid == 0) sh[kTileParts] = -1;
+  int carry = 0;                                   // tiles of the earlier chunks
+  for (int s0 = 0; s0 < p.S; s0 += kThreads) {
+    const int s = s0 + tid;
+    const int nt = s < p.S ? (mq_q_end(p, s) - mq_q_begin(p, s) + Qt - 1) / Qt : 0;
+    const int incl = wave_inclusive_scan_i32(nt, lane);
+    if (lane == kWave - 1) sh[wave] = incl;        // wave totals
+    __syncthreads();
+    int before = carry, total = 0;
+#pragma unroll
+    for (int w = 0; w < kTileParts; ++w) {
+      const int x = sh[w];
+      before += w < wave ? x : 0;
+      total += x;
+    }
+    const int excl = before + incl - nt;
+    if (nt > 0 && excl <= i && i < excl + nt) {
+      sh[kTileParts] = s;
+      sh[kTileParts + 1] = i - excl;
+    }
+    carry += total;
+    __syncthreads();                               // before the totals are rewritten
+  }
+  __syncthreads();                                 // (S = 0: the initial -1)
+  // the same in every lane: said so, the caller's branch and its token loop
+  // stay uniform (scalar) control flow
+  s_out = __builtin_amdgcn_readfirstlane(sh[kTileParts]);
+  j_out = __builtin_amdgcn_readfirstlane(sh[kTileParts + 1]);
+  return s_out >= 0;
+}
+
+typedef __attribute__((address_space(3))) float LdsF32;
+typedef const __attribute__((address_space(4))) MqParams ConstMqParams;
+
+// Rows 4c + r of row block b (lane (c, n): head dims 8n .. 8n+7) from the
+// parts' states in LDS: rescaled to their common max, summed, normalised and
+// stored.  Kept out of line, reading the parameters from the kernel-argument
+// segment: inlined, or with the fields passed as arguments, the caller kept
+// them live through its token loop and went past the register budget of two
+// waves per SIMD (spills inside the loop); a reference to the kernel's
+// parameter copy put the copy on the stack, and the K/V loads through its
+// pointers became flat loads.
+template <int G, int NT, bool kFp8>
+__device__ __attribute__((noinline)) void mq_tile_finish(ConstMqParams* pp, const LdsF32* lds,
+                                                         int b, int r, int lane, int g, int q0,
+                                                         int nq) {
+  ConstMqParams& p = *pp;
+  const int c = lane >> 4, t = lane & 15;
+  const int Hq = p.Hq;
+  const LdsF32* lacc = lds;
+  const LdsF32* lml = lds + kTileParts * NT * 4 * kWave * 8;
+  const int row = 4 * c + r;
+  float mp[kTileParts];
+  float M = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kTileParts; ++q) {
+    mp[q] = lml[((q * NT + b) * 2 + 0) * 16 + row];
+    M = fmaxf(M, mp[q]);
+  }
+  float L = 0.0f;
+  float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < kTileParts; ++q) {
+    const float w = mp[q] == -INFINITY ? 0.0f : fast_exp2(mp[q] - M);   // an empty part adds 0
+    L += w * lml[((q * NT + b) * 2 + 1) * 16 + row];
+    const LdsF32* a = lacc + (((q * NT + b) * 4 + r) * kWave + lane) * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] += w * a[u];
+  }
+  const int m = 16 * b + row;
+  const int qi = m / G, jh = m % G;
+  if (qi >= nq) return;
+  float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  if constexpr (kFp8) inv *= p.v_scale;
+  const float lse = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : -INFINITY;
+  const int h = g * G + jh;
+  const long long dst = ((long long)(q0 + qi) * Hq + h) * kD + 8 * t;
+  if (p.out_f16) {
+    half8_t hv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(o[e] * inv);
+    *reinterpret_cast<half8_t*>(static_cast<_Float16*>(p.out) + dst) = hv;
+  } else {
+    float* d = static_cast<float*>(p.out) + dst;
+    *reinterpret_cast<f32x4*>(d) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<f32x4*>(d + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+  }
+  if (p.lse_out && t == 0) p.lse_out[(long long)(q0 + qi) * Hq + h] = lse;
+}
+
+template <int G, int NT, bool kFp8>
+__global__ __launch_bounds__(kWave * kTileParts) __attribute__((amdgpu_waves_per_eu(2)))
+void mq_tile_kernel(MqParams p) {
+  constexpr int Qt = 16 * NT / G;
+  extern __shared__ float tile_lds[];
+  __shared__ int scan[kTileParts + 2];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int i = blockIdx.x / p.Hkv;                // tile
+  const int g = blockIdx.x % p.Hkv;                // KV head
+  int s, j;
+  if (!mq_find_tile<Qt>(p, i, scan, s, j)) return; // uniform over the work-group
+  const int qb = mq_q_begin(p, s), nq_seq = mq_q_end(p, s) - qb;
+  const int q0 = qb + j * Qt, nq = min(Qt, nq_seq - j * Qt);
+  const int n = mq_seq_len(p, s);
+  int base, ntok;
+  if (p.causal) {
+    base = n - nq_seq + j * Qt + 1;
+    ntok = min(max(base + nq - 1, 0), n);
+  } else {
+    base = n;
+    ntok = n;
+  }
+  // part `wave`: blocks [wave * nblk / 8, (wave + 1) * nblk / 8)
+  const int nblk = (ntok + kBS - 1) / kBS;
+  const int tok_lo = __builtin_amdgcn_readfirstlane(min(wave * nblk / kTileParts * kBS, ntok));
+  const int tok_hi = __builtin_amdgcn_readfirstlane(min((wave + 1) * nblk / kTileParts * kBS, ntok));
+  // the tile's Q operands into LDS once for the 8 waves (wave 4b + i stores
+  // chunk i of row block b, what mq_load_q gives lane (c, t) of a wave), read
+  // back at every block: held in registers they put the token loop past the
+  // register budget of two waves per SIMD
+  LdsU32x4* qlds = (LdsU32x4*)(tile_lds + mq_tile_state_floats(NT));
+  if (wave < 4 * NT) {
+    const int b = wave >> 2, ii = wave & 3;
+    const int c = lane >> 4, t = lane & 15;
+    const int m = 16 * b + t;
+    const int qi = m / G, jh = m % G;
+    const int row = q0 + min(qi, nq - 1);
+    const _Float16* qrow = p.q + ((long long)row * p.Hq + (long long)g * G + jh) * kD;
+    u32x4 x = *reinterpret_cast<const u32x4*>(qrow + KvFmt<kFp8>::q_dim(ii, c)) ^ p.q_sign;
+    if (qi >= nq) x = u32x4{0u, 0u, 0u, 0u};
+    qlds[(b * 4 + ii) * kWave + lane] = x;
+  }
+  __syncthreads();
+  MqSeg<NT> st;
+  mq_reg_fold<G, NT, kFp8, true>(p, lane, g, s, q0, nq, base, tok_lo, tok_hi, st, qlds);
+
+  // the part's state: accumulators [part][b][r][lane][u], then per row of
+  // each block the reference max and the sum over the part's tokens
+  const int c = lane >> 4, t = lane & 15;
+  float* lacc = tile_lds;
+  float* lml = tile_lds + kTileParts * NT * 4 * kWave * 8;
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* d = lacc + (((wave * NT + b) * 4 + r) * kWave + lane) * 8;
+      *reinterpret_cast<f32x4*>(d) =
+          f32x4{st.acc[b][0][r], st.acc[b][1][r], st.acc[b][2][r], st.acc[b][3][r]};
+      *reinterpret_cast<f32x4*>(d + 4) =
+          f32x4{st.acc[b][4][r], st.acc[b][5][r], st.acc[b][6][r], st.acc[b][7][r]};
+    }
+    float l = st.lp[b];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (c == 0) {
+      lml[((wave * NT + b) * 2 + 0) * 16 + t] = st.m[b];
+      lml[((wave * NT + b) * 2 + 1) * 16 + t] = l;
+    }
+  }
+  __syncthreads();
+  // wave 4b + r finishes rows 4c + r of block b
+  if (wave < 4 * NT)
+    // the kernel's one explicit argument sits at the start of its argument segment
+    mq_tile_finish<G, NT, kFp8>((ConstMqParams*)__builtin_amdgcn_kernarg_segment_ptr(),
+                                (const LdsF32*)tile_lds, wave >> 2, wave & 3, lane, g, q0, nq);
+}
+
+// ---------------------------------------------------------------------------
 // shared kernel: 4 waves per KV head share each K/V block through LDS
 
 template <int G, int NT, bool kFp8>
@@ -771,10 +1008,10 @@ __device__ __forceinline__ void mq_shared_segment(const MqParams& p, char* kv, i
                                                   8 * E * t);
         const int t0 = tok_lo + cur * kBS;
         if (t0 + kBS > full_end)
-          mq_fold<G, NT, true, kFp8>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, tok_hi - t0,
+          mq_fold<G, NT, true, kFp8>(st, MqQRegs<NT>{qa}, kr, vr, p.qk_scale, lane, row0, t0, tok_hi - t0,
                                      causal_base, n, nq, tok_hi);
         else
-          mq_fold<G, NT, false, kFp8>(st, qa, kr, vr, p.qk_scale, lane, row0, t0, kBS,
+          mq_fold<G, NT, false, kFp8>(st, MqQRegs<NT>{qa}, kr, vr, p.qk_scale, lane, row0, t0, kBS,
                                       causal_base, n, nq, tok_hi);
       }
     }
@@ -1534,8 +1771,31 @@ int mq_run_count(int G, int variant, int Hkv, bool fp8) {
   return std::max(1, f.cus * f.wg_per_cu[mq_gidx(G)][variant][fp8 ? 1 : 0][waves] / per_run);
 }
 
+// The whole-tile kernel serves a register variant over an fp16 cache when the
+// call has at least one (sequence, KV head) pair per CU and no context longer
+// than kTileMaxTokens: every work-group then holds one tile of at most
+// kTileMaxTokens / 8 tokens per wave, the hardware hands work-groups to CUs as
+// they free up, and the plan, the partials and the merge are not needed.
+// Longer contexts (one tile could outlast the rest of the call) and smaller
+// calls keep the balanced run schedule.  Measured on MI355X (speculative
+// verification, 32 x 4096, 6 queries): fp16 call 98.6 -> 89.4 us.  FP8 keeps
+// the run schedule: its fold is short enough per block that the LDS reads of
+// Q cost the whole-tile kernel 40%, and with Q in registers its token loop
+// spilled.
+bool mq_whole_tiles(int S, int Hkv, int variant, int max_tokens, int tiles_max) {
+  if (mq_is_shared(variant) || max_tokens > kTileMaxTokens) return false;
+  if ((long long)tiles_max * Hkv > kTileMaxGroups) return false;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    MqDeviceFacts& f = g_mq_dev[dev];
+    if (f.cus > 0) cus = f.cus;
+  }
+  return (long long)S * Hkv >= cus;
+}
+
 struct MqPlan {
   int variant = 0, Qt = 0, P = 0, n_runs = 0, hg = 0, max_tokens = 0, tiles_max = 0, n_slots = 0;
+  bool whole_tiles = false;   // register variants: the whole-tile kernel alone
   size_t hdr_offset = 0, tiles_offset = 0, rec_offset = 0, lse_offset = 0, o_offset = 0,
          total = 0;
 };
@@ -1580,6 +1840,7 @@ MqPlan mq_make_plan(int S, int T, int Hq, int Hkv, int max_blocks, int partition
   pl.hg = mq_head_group(Hkv);
   pl.max_tokens = max_blocks * kBS;
   pl.tiles_max = (T + pl.Qt - 1) / pl.Qt + S;
+  pl.whole_tiles = !fp8 && mq_whole_tiles(S, Hkv, pl.variant, pl.max_tokens, pl.tiles_max);
   pl.n_slots = 2 * pl.n_runs;
   pl.hdr_offset = 0;
   pl.tiles_offset = align256(sizeof(int32_t) * kMqHdrInts);
@@ -1609,6 +1870,14 @@ void mq_launch_aux(bool plan, const MqParams& mp, const MqPlan& pl, hipStream_t 
 template <int G, int V, bool kFp8>
 void mq_launch_v(const MqParams& mp, const MqPlan& pl, hipStream_t stream) {
   constexpr int Qt = (16 << V) / G;
+  if constexpr (V <= 1 && !kFp8) {
+    if (pl.whole_tiles) {
+      hipLaunchKernelGGL((mq_tile_kernel<G, V + 1, kFp8>),
+                         dim3((unsigned)((long long)pl.tiles_max * mp.Hkv)),
+                         dim3(kWave * kTileParts), (unsigned)mq_tile_lds(V + 1), stream, mp);
+      return;
+    }
+  }
   mq_launch_aux<Qt>(true, mp, pl, stream);
   if constexpr (V == 3) {
     hipLaunchKernelGGL((mq_wide_kernel<G, kFp8>), dim3((unsigned)(pl.n_runs * mp.Hkv)),

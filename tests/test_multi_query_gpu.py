@@ -181,6 +181,72 @@ def test_register_kernel_halves_combined(kv_dtype, causal, G, Hkv):
     compare_lse(to_np(lse), ref_lse)
 
 
+# Register-sized tiles (up to 32 rows) over an fp16 cache in a call with at
+# least one (sequence, KV head) pair per CU and contexts of at most 8192 tokens
+# go to the whole-tile kernel: one work-group per (tile, KV head), 8 waves over
+# parts of the tile, combined in LDS; no plan, no merge, the workspace
+# untouched.  FP8 calls of the same shape keep the planned path.  Ragged
+# contexts (empty, shorter than the 8 parts, one block, several), query
+# counts 0, 1 and more than one tile per sequence.
+def _whole_tile_case(G, Hkv, rows, causal, kv_dtype, seed, S=None):
+    rng = np.random.default_rng(seed)
+    S = S or max(256 // Hkv + 5, 8)
+    per_seq = max(1, rows // G)
+    lens = rng.integers(0, 2500, size=S)
+    lens[:6] = [0, 1, 15, 16, 17, 127]
+    nq = rng.integers(1, per_seq + 1, size=S)
+    nq[:4] = [0, per_seq, 1, 3 * per_seq + 1]       # none, one full tile, one query, 4 tiles
+    lens[3] = max(lens[3], nq[3])
+    return W.build_mq_case(lens.tolist(), nq.tolist(), G * Hkv, Hkv, causal=causal, seed=seed,
+                           device="cuda", name=f"mq_whole_G{G}_{Hkv}_r{rows}", kv_dtype=kv_dtype)
+
+
+def _untouched(ws):
+    return bool((ws[:4096] == 0xAB).all())
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 8), (8, 8), (2, 8), (1, 8), (6, 8), (4, 5), (1, 32)])
+@pytest.mark.parametrize("rows", [12, 28])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+def test_whole_tile_kernel(G, Hkv, rows, causal, kv_dtype):
+    case = _whole_tile_case(G, Hkv, rows, causal, kv_dtype, seed=300 + 7 * G + Hkv + rows)
+    ws = torch.full((pda.multi_query_workspace_size(case.S, case.T, case.Hq, case.Hkv,
+                                                    case.block_table.shape[1], 0),),
+                    0xAB, dtype=torch.uint8, device="cuda")
+    out, lse = run_mq(case, 0, workspace=ws)
+    whole = kv_dtype == "fp16"
+    assert _untouched(ws) == whole, f"expected the {'whole-tile' if whole else 'planned'} path"
+    ref, ref_lse = oracle_mq(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_whole_tile_partial_entry_point():
+    case = _whole_tile_case(4, 8, 24, True, "fp16", seed=331)
+    o, lse = pda.paged_multi_query_attn_partial(case.q, case.k_cache, case.v_cache,
+                                                case.block_table, case.context_lens,
+                                                case.query_start, case.scale, causal=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_mq(case)
+    v = case.v_cache.cpu().numpy()
+    compare_out(to_np(o), ref, abs_tol=p_rounding_bound(v))
+    compare_lse(to_np(lse), ref_lse)
+
+
+def test_planned_path_below_one_pair_per_cu():
+    """Fewer (sequence, KV head) pairs than CUs keep the balanced run schedule."""
+    case = _whole_tile_case(4, 8, 24, True, "fp16", seed=332, S=20)
+    ws = torch.full((pda.multi_query_workspace_size(case.S, case.T, case.Hq, case.Hkv,
+                                                    case.block_table.shape[1], 0),),
+                    0xAB, dtype=torch.uint8, device="cuda")
+    out, lse = run_mq(case, 0, workspace=ws)
+    assert not _untouched(ws), "the plan kernel did not run"
+    ref, ref_lse = oracle_mq(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
 @pytest.mark.parametrize("P", [0, 64])
 def test_partial_entry_point(P):
     case = W.build_mq_case(SMALL_LENS, SMALL_NQ, 16, 4, causal=True, seed=43, device="cuda",
