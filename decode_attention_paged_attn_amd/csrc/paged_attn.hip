@@ -84,13 +84,24 @@ namespace {
 
 using namespace pda;
 
-constexpr int kMaxKvHeads = 64;       // one wave per KV head; head groups of up to 4 per work-group
-#ifndef PDA_MAX_WAVES_PER_WG
-#define PDA_MAX_WAVES_PER_WG 4
+constexpr int kMaxKvHeads = 64;       // one wave per KV head, head groups per work-group
+// KV heads (waves) of one work-group at most: 4 over fp16, whose kernel runs
+// one wave per SIMD (1, 2, 4 and 8 measured; 4 best); over FP8 8 where a
+// context may exceed kLongTokens, else 4 (split kernel, 8 against 4: agentic
+// batch 396.2 -> 385.1 us, ragged 1684 -> 1665 us, but Llama 4K 83.4 -> 84.9 us)
+#ifndef PDA_MAX_WAVES_PER_WG_FP16
+#define PDA_MAX_WAVES_PER_WG_FP16 4
 #endif
-constexpr int kMaxWavesPerWG = PDA_MAX_WAVES_PER_WG;   // KV heads of one work-group
+#ifndef PDA_MAX_WAVES_PER_WG_FP8
+#define PDA_MAX_WAVES_PER_WG_FP8 8
+#endif
+constexpr int max_waves_per_wg(bool fp8) {
+  return fp8 ? PDA_MAX_WAVES_PER_WG_FP8 : PDA_MAX_WAVES_PER_WG_FP16;
+}
+constexpr int kMaxWavesPerWG = max_waves_per_wg(false) > max_waves_per_wg(true)
+                                   ? max_waves_per_wg(false) : max_waves_per_wg(true);
+constexpr int kLongTokens = 8192;
 constexpr float kLazyMax = 8.0f;      // log2 headroom of p over a head's running max
-// (1, 2 and 4 heads per work-group measured; 8 is no faster than 4)
 // Occupancy target of the split kernel, held by LDS padding when its registers
 // would allow more, and the depth of its ring of K/V register buffers (blocks
 // in flight + 1).  Measured on MI355X, ring 3 for both: fp16 (G <= 4) runs
@@ -519,10 +530,10 @@ __device__ __forceinline__ void run_segment(const SplitParams& p, float* lds_p, 
 }
 
 template <int G, bool kFp8, bool kAppend = false>
-__global__ __launch_bounds__(kWave * kMaxWavesPerWG)
+__global__ __launch_bounds__(kWave * max_waves_per_wg(kFp8))
 __attribute__((amdgpu_waves_per_eu(waves_per_eu(G, kFp8))))
 void split_kernel(SplitParams p) {
-  __shared__ float lds[kMaxWavesPerWG][kBS * 16 / 2];   // one 16x16 fp16 P tile per wave
+  __shared__ float lds[max_waves_per_wg(kFp8)][kBS * 16 / 2];   // one 16x16 fp16 P tile per wave
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_hgroups = p.Hkv / p.hg;
@@ -775,9 +786,12 @@ const void* split_kernel_ptr(int G, int kind) {
   }
 }
 
-// KV heads (waves) per work-group: the largest divisor of Hkv up to 4.
-int head_group(int Hkv) {
-  for (int hg = kMaxWavesPerWG; hg > 1; --hg)
+// KV heads (waves) per work-group: 8 over FP8 when contexts may exceed
+// kLongTokens and 8 divides Hkv, else the largest divisor of Hkv up to 4
+// (a work-group of 5 to 7 waves would leave wave slots of its CU empty).
+int head_group(int Hkv, bool fp8, int max_tokens) {
+  if (fp8 && max_tokens > kLongTokens && Hkv % 8 == 0 && max_waves_per_wg(true) >= 8) return 8;
+  for (int hg = std::min(4, max_waves_per_wg(fp8)); hg > 1; --hg)
     if (Hkv % hg == 0) return hg;
   return 1;
 }
@@ -791,7 +805,7 @@ int head_group(int Hkv) {
 int occupancy_pad(int G, int kind, int hg, int lds_cu, int lds_wg_max, int regs_wgs) {
   const int target = waves_per_eu(G, kind & 1) * 4 / hg;    // 4 SIMDs per CU
   if (target <= 0 || regs_wgs <= target || lds_cu <= 0) return 0;
-  const int static_lds = (int)sizeof(float) * kMaxWavesPerWG * kBS * 8;
+  const int static_lds = (int)sizeof(float) * max_waves_per_wg(kind & 1) * kBS * 8;
   const int per_wg = (lds_cu / (target + 1) + 1 + 511) / 512 * 512;
   if (per_wg * target > lds_cu || per_wg > lds_wg_max) return 0;
   return std::max(0, per_wg - static_lds);
@@ -811,7 +825,7 @@ void device_facts(DeviceFacts& f, int dev) {
   f.cus = cus;
   for (int lg = 0; lg < kGroups; ++lg)
     for (int kd = 0; kd < kKinds; ++kd)
-      for (int w = 1; w <= kMaxWavesPerWG; ++w) {
+      for (int w = 1; w <= max_waves_per_wg(kd & 1); ++w) {
         const void* fn = split_kernel_ptr(kGroupSizes[lg], kd);
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, w * kWave, 0) != hipSuccess ||
@@ -838,17 +852,17 @@ DeviceFacts* facts() {
   return &f;
 }
 
-int run_count(int G, int Hkv, int kind) {
-  const int hg = head_group(Hkv);
+int run_count(int G, int Hkv, int kind, int hg) {
   const int n_hgroups = Hkv / hg;
   const DeviceFacts* f = facts();
-  if (!f) return 1024 / n_hgroups;  // no device: a fixed size keeps sizing queries usable
+  // no device: the tuned occupancy on 256 CUs keeps sizing queries usable
+  if (!f) return std::max(1, 256 * 4 * waves_per_eu(G, kind & 1) / Hkv);
   return std::max(1, f->cus * f->wg_per_cu[group_index(G)][kind][hg] / n_hgroups);
 }
 
-int lds_pad(int G, int Hkv, int kind) {
+int lds_pad(int G, int kind, int hg) {
   const DeviceFacts* f = facts();
-  return f ? f->lds_pad[group_index(G)][kind][head_group(Hkv)] : 0;
+  return f ? f->lds_pad[group_index(G)][kind][hg] : 0;
 }
 
 struct Plan {
@@ -887,8 +901,8 @@ int check_shape(int B, int Hq, int Hkv, int D, int block_size, int max_blocks, i
 Plan make_plan(int B, int Hq, int Hkv, int max_blocks, int partition_tokens, int kind) {
   Plan pl;
   pl.P = partition_tokens > 0 ? partition_tokens : kBS;
-  pl.n_runs = run_count(Hq / Hkv, Hkv, kind);
-  pl.hg = head_group(Hkv);
+  pl.hg = head_group(Hkv, kind & 1, max_blocks * kBS);
+  pl.n_runs = run_count(Hq / Hkv, Hkv, kind, pl.hg);
   pl.max_tokens = max_blocks * kBS;
   pl.n_slots = pl.n_runs + B;
   pl.hdr_offset = 0;
@@ -988,7 +1002,7 @@ int run_attention(bool out_f16, void* out, float* lse_out, const void* q, const 
   sp.k_inv = 1.0f / k_scale;
   sp.v_inv = 1.0f / v_scale;
   const dim3 grid((unsigned)(pl.n_runs * (Hkv / pl.hg))), block((unsigned)(pl.hg * kWave));
-  const unsigned pad = (unsigned)lds_pad(Hq / Hkv, Hkv, kernel_kind(fp8, append));
+  const unsigned pad = (unsigned)lds_pad(Hq / Hkv, kernel_kind(fp8, append), pl.hg);
   if (fp8 && append) {
     switch (Hq / Hkv) {
       case 1: hipLaunchKernelGGL((split_kernel<1, true, true>), grid, block, pad, stream, sp); break;

@@ -642,6 +642,33 @@ def test_fp8_fused_append_equals_append_then_attend(G, Hkv, P):
     compare_lse(to_np(lse), ref_lse)
 
 
+# FP8 calls whose block table allows contexts past 8192 tokens take up to 8 KV
+# heads per work-group (4 otherwise): small ragged batches at a table 1024
+# blocks wide, at the tuned occupancy, plain and with the fused append.
+@pytest.mark.parametrize("G,Hkv", [(4, 8), (8, 8), (1, 32), (1, 40), (2, 16), (4, 2), (6, 5)])
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_fp8_wide_table_head_groups(G, Hkv, P):
+    lens = [0, 1, 2, 17, 100, 257, 1000, 3000, 40]
+    case = W.build_case(lens, G * Hkv, Hkv, seed=340 + G + Hkv, device="cuda", kv_dtype="fp8",
+                        pool_blocks=sum(-(-n // 16) for n in lens) + 5, width=1024)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lay = pda.workspace_layout(case.B, case.Hq, Hkv, 1024, P, kv_fp8=True)
+    assert lay["n_runs"] == cus * 4 * 2 // Hkv
+    out, lse = run(case, P)
+    ref, ref_lse = oracle_full(case)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+    kn, vn = _new_rows(case, 341 + G)
+    q, k, v, table, ln = W.host_full(case)
+    out, lse = _fused_vs_separate(case, kn, vn, P)
+    k_ref, v_ref = O.kv_append_fp8(k, v, kn.cpu().numpy(), vn.cpu().numpy(), table, ln,
+                                   case.k_scale, case.v_scale)
+    ref, ref_lse = O.paged_decode_attention_fp8(q, k_ref, v_ref, table, ln, case.scale,
+                                                case.k_scale, case.v_scale)
+    compare_out(to_np(out), ref)
+    compare_lse(to_np(lse), ref_lse)
+
+
 def test_fp8_fused_append_full_size():
     case = W.llama8b_4k(device="cuda", kv_dtype="fp8")
     kn, vn = _new_rows(case, 332)
