@@ -1057,8 +1057,25 @@ constexpr int kWideRows = 32;         // query rows per wave
 // (its 128-token stages fit two work-groups per CU: chunked prefill 0.658 ->
 // 0.653 ms, cascade 183 -> 178 us against two), two over fp16 (four would not
 // fit; two spilled while its K/V went through registers)
+#ifndef PDA_WIDE_NS_FP16
+#define PDA_WIDE_NS_FP16 2
+#endif
+#ifndef PDA_WIDE_NS_FP8
+#define PDA_WIDE_NS_FP8 4
+#endif
+#ifndef PDA_WIDE_STAGES
+#define PDA_WIDE_STAGES 2             // LDS stages of K/V: steps in flight + 1
+#endif
 template <bool kFp8>
-constexpr int wide_ns() { return kFp8 ? 4 : 2; }
+constexpr int wide_ns() { return kFp8 ? PDA_WIDE_NS_FP8 : PDA_WIDE_NS_FP16; }
+constexpr int kWideStages = PDA_WIDE_STAGES;
+static_assert(kWideStages >= 2 && kWideStages <= 4, "wide kernel stages");
+// waits until at most n of this wave's vector memory operations are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 // 32-token sub-steps per online-softmax update: two for FP8 (chunked prefill
 // 0.84 -> 0.75 ms against one), one for fp16 (two spill)
 template <bool kFp8>
@@ -1427,7 +1444,8 @@ __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g
 }
 
 template <int G, bool kFp8>
-__device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (&stage)[2][2],
+__device__ __forceinline__ void mq_wide_segment(const MqParams& p,
+                                                char* const (&stage)[kWideStages][2],
                                                 int lane, int wave, int g, int i, int tok_lo,
                                                 int tok_hi, bool whole, int slot) {
   constexpr int E = KvFmt<kFp8>::kElemBytes;
@@ -1493,15 +1511,17 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
   // K (or V) rows are kLoads pieces of 1024 bytes, kR row slots each; wave w
   // moves pieces w, w + 4, ..., lane l chunk slot l % kC of row slot l / kC of
   // its piece, so it fetches chunk (l % kC) ^ wide_swz(row slot) of the token
-  // wide_prow(row slot).  The loads of step cur + 1 go
-  // out right after the barrier of step cur into the other stage (last read
-  // in step cur - 1, which every wave has finished); each wave waits for its
-  // own before the next barrier.  Blocks past the segment's end are not
-  // loaded: their stale rows lie past tok_hi, where the softmax masks them and
-  // their V rows are selected to zero.  The two stages are separate LDS
-  // arrays and the step loop is unrolled by two, so that the compiler can
-  // tell a step's operand reads from the loads in flight into the other stage
-  // and puts no wait for those before them.
+  // wide_prow(row slot).  With S stages, steps cur + 1 .. cur + S - 2 are in
+  // flight while step cur is folded: the loads of step cur + S - 1 go out
+  // right after the barrier of step cur into the stage step cur - 1 used
+  // (which every wave has finished), and before each barrier a wave waits for
+  // its own loads of that step only (every step issues the same loads, so
+  // the count of later ones outstanding is known).  Rows past the segment's
+  // end get its last block again: they lie past tok_hi, where the softmax
+  // masks them and their V rows are selected to zero.  The stages are
+  // separate LDS arrays and the step loop is unrolled by S, so that the
+  // compiler can tell a step's operand reads from the loads in flight into
+  // the other stages and puts no wait for those before them.
   typedef __attribute__((address_space(3))) void LdsVoid;
   typedef const __attribute__((address_space(1))) void GlobalVoid;
   constexpr int kC = kRow / 16;                     // 16-byte chunks per row
@@ -1513,34 +1533,44 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
   const int trow = wide_prow<kFp8>(prow);           // the token it holds
   const unsigned src_off =
       (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ wide_swz<kFp8>(prow)));
+  constexpr int kStepLoads = 2 * kLoads;            // a wave's loads of one step
+  constexpr int S = kWideStages;
   auto issue = [&](int step, char* kst, char* vst) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
       const int piece = wave + kMqWaves * l;
-      const int b = 2 * kNS * step + piece * kR / kBS;
-      if (b < nblk) {
-        const unsigned raw = (unsigned)bt_s[b];
-        const long long off = (raw < (unsigned long long)p.num_blocks ? (long long)raw : 0) * block_bytes;
-        __builtin_amdgcn_global_load_lds((GlobalVoid*)(kbytes + off + src_off),
-                                         (LdsVoid*)(kst + piece * kWave * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((GlobalVoid*)(vbytes + off + src_off),
-                                         (LdsVoid*)(vst + piece * kWave * 16), 16, 0, 0);
-      }
+      const int b = min(2 * kNS * step + piece * kR / kBS, nblk - 1);
+      const unsigned raw = (unsigned)bt_s[b];
+      const long long off = (raw < (unsigned long long)p.num_blocks ? (long long)raw : 0) * block_bytes;
+      __builtin_amdgcn_global_load_lds((GlobalVoid*)(kbytes + off + src_off),
+                                       (LdsVoid*)(kst + piece * kWave * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((GlobalVoid*)(vbytes + off + src_off),
+                                       (LdsVoid*)(vst + piece * kWave * 16), 16, 0, 0);
     }
   };
-  // one step: wait for this wave's loads of it, then for every wave's; send
-  // the next step's loads into the other stage; fold this one
-  auto step = [&](int cur, char* kst, char* vst, char* knext, char* vnext) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (cur + 1 < nstep) issue(cur + 1, knext, vnext);
-    if (!idle) fold_step(cur, kst, vst);
-  };
-  issue(0, stage[0][0], stage[0][1]);
-  for (int cur = 0; cur < nstep; cur += 2) {
-    step(cur, stage[0][0], stage[0][1], stage[1][0], stage[1][1]);
-    if (cur + 1 >= nstep) break;
-    step(cur + 1, stage[1][0], stage[1][1], stage[0][0], stage[0][1]);
+  wait_vmcnt<0>();                                  // the previous segment's stores
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nstep) issue(k, stage[k][0], stage[k][1]);
+  for (int cur = 0; cur < nstep; cur += S) {
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl) {
+      const int c = cur + sl;
+      if (c >= nstep) break;
+      // this wave's loads of step c: the loads of steps c + 1 .. c + S - 2
+      // (those issued) went out after them
+      const int later = min(S - 2, nstep - 1 - c);
+      if (later >= 2) wait_vmcnt<2 * kStepLoads>();
+      else if (later == 1) wait_vmcnt<kStepLoads>();
+      else wait_vmcnt<0>();
+      // a bare barrier: a fence with it would wait for every load in flight.
+      // Each wave has waited for its loads of step c above, and its LDS reads
+      // of the stage the next loads overwrite were consumed by its MFMAs of
+      // step c - 1 before it got here.
+      __builtin_amdgcn_s_barrier();
+      if (c + S - 1 < nstep) issue(c + S - 1, stage[(sl + S - 1) % S][0], stage[(sl + S - 1) % S][1]);
+      if (!idle) fold_step(c, stage[sl][0], stage[sl][1]);
+    }
   }
   __syncthreads();                                  // the stages are free for the next segment
   if (!idle) wide_store<G, kFp8>(p, st, g, q0, nq, row0, lane, whole, slot);
@@ -1549,10 +1579,23 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p, char* const (
 template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void mq_wide_kernel(MqParams p) {
-  // two stages of K and V rows, each its own array
+  // the stages of K and V rows, each its own array
   constexpr int kHalf = wide_step<kFp8>() * wide_row_bytes<kFp8>();
   __shared__ __attribute__((aligned(16))) char k0[kHalf], v0[kHalf], k1[kHalf], v1[kHalf];
-  char* const stage[2][2] = {{k0, v0}, {k1, v1}};
+#if PDA_WIDE_STAGES >= 3
+  __shared__ __attribute__((aligned(16))) char k2[kHalf], v2[kHalf];
+#endif
+#if PDA_WIDE_STAGES >= 4
+  __shared__ __attribute__((aligned(16))) char k3[kHalf], v3[kHalf];
+#endif
+  char* const stage[kWideStages][2] = {{k0, v0}, {k1, v1}
+#if PDA_WIDE_STAGES >= 3
+                                       , {k2, v2}
+#endif
+#if PDA_WIDE_STAGES >= 4
+                                       , {k3, v3}
+#endif
+  };
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int w = blockIdx.x / p.Hkv;                 // run of the unit stream
