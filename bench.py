@@ -16,6 +16,11 @@ Prints ONE JSON line:
                  256-sequence batch, the 32 x 128K batch as 4 range partials +
                  merge_partials (and its single pass), the agentic batch over an
                  FP8 cache, and at the Q48:KV8 and MHA Q40:KV40 head shapes
+  multi_query_and_cascade
+                 the other paths, fp16 and FP8 caches: speculative verification
+                 (32 x 4096, 6 causal queries), chunked prefill (4 x 1024-query
+                 chunks) and shared-prefix cascade decode (200 requests), each as
+                 `--op multi_query` / `--op cascade` reports it (skip: --no-mq)
   cpu_baseline   the float64 CPU oracle: all cores (a process pool over every
                  sequence) and one core (a bounded sample)
 
@@ -403,6 +408,10 @@ def mq_work(case):
 
 
 def bench_multi_query(case, P, steps, warmup):
+    print(json.dumps(measure_multi_query(case, P, steps, warmup)), flush=True)
+
+
+def measure_multi_query(case, P, steps, warmup):
     import torch
     import decode_attention_paged_attn_amd as pda
     ws = torch.empty(max(pda.multi_query_workspace_size(case.S, case.T, case.Hq, case.Hkv,
@@ -431,7 +440,7 @@ def bench_multi_query(case, P, steps, warmup):
     roof["kernel"] = "paged_multi_query_attn call (plan + tile + merge kernels)"
     roof["traffic"] = measured_traffic(f"multi_query:{case.name}", "multi_query")
     value = roof["achieved"] * ev_ms / wall_ms
-    print(json.dumps({
+    return {
         "metric": "multi-query paged attention: " + ("KV-read GB/s" if hbm_bound else "TFLOP/s"),
         "op": "paged_multi_query_attn", "value": round(value, 2), "unit": roof["unit"],
         "ms_per_step": round(wall_ms, 5), "event_ms": {"mean": round(ev_ms, 5),
@@ -445,10 +454,14 @@ def bench_multi_query(case, P, steps, warmup):
         "config": {"workload": case.name, "sequences": case.S, "query_tokens": case.T,
                    "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 128,
                    "causal": case.causal, "partition_tokens": P, "kv_dtype": case.kv_dtype,
-                   "context_tokens": int(case.lens.sum())}}), flush=True)
+                   "context_tokens": int(case.lens.sum())}}
 
 
 def bench_cascade(case, steps, warmup):
+    print(json.dumps(measure_cascade(case, steps, warmup)), flush=True)
+
+
+def measure_cascade(case, steps, warmup):
     """Cascade (prefix pass + suffix pass + merge) against naive decode of the same batch."""
     import torch
     import decode_attention_paged_attn_amd as pda
@@ -481,7 +494,7 @@ def bench_cascade(case, steps, warmup):
         suffix = int(case.suffix_lens_host[lo:hi].sum())
         naive_tok += (hi - lo) * int(case.prefix_lens_host[r]) + suffix
         unique_tok += int(case.prefix_lens_host[r]) + suffix
-    print(json.dumps({
+    return {
         "metric": "cascade decode: requests/s (unique KV-read GB/s in roofline)",
         "op": "cascade_decode_attn", "value": round(B / (wall_ms / 1e3), 1), "unit": "requests/s",
         "ms_per_step": round(wall_ms, 5), "event_ms": {"mean": round(ev_ms, 5),
@@ -499,7 +512,7 @@ def bench_cascade(case, steps, warmup):
                    "groups": len(case.prefix_lens_host),
                    "prefix_tokens": [int(x) for x in case.prefix_lens_host],
                    "suffix_tokens_total": int(case.suffix_lens_host.sum()),
-                   "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}), flush=True)
+                   "q_heads": Hq, "kv_heads": case.Hkv, "head_dim": 128}}
 
 
 def measure_partial_merge(case, steps, warmup, single_pass=True):
@@ -649,6 +662,9 @@ def main():
                          "--config spec_verify or chunked_prefill; cascade: "
                          "cascade_decode_attn on --config shared_prefix; partial_merge: 4 range "
                          "partials + merge_partials on disagg_merge, against single pass")
+    ap.add_argument("--no-mq", action="store_true",
+                    help="skip the multi-query (speculative verification, chunked prefill) "
+                         "and cascade records of the default run")
     ap.add_argument("--partial-only", action="store_true",
                     help="--op partial_merge: time only the partials + merge (no single pass)")
     ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
@@ -782,6 +798,25 @@ def main():
     if also:
         rec["also"] = also
     del also_cases
+    if not args.no_mq:
+        # the other paths of the call set, fp16 and FP8: one record each, as
+        # `--op multi_query` / `--op cascade` print them
+        keep = ("value", "unit", "ms_per_step", "event_ms", "roofline", "kv_GBps", "tflops",
+                "query_tokens_per_s", "naive_decode_ms", "speedup_vs_naive_decode")
+        mq = {}
+        for name in ("spec_verify", "chunked_prefill", "shared_prefix"):
+            for kv in ("fp16", "fp8"):
+                if name == "shared_prefix":
+                    c = W.CASCADE_CONFIGS[name](device="cuda", kv_dtype=kv)
+                    r = measure_cascade(c, args.steps, args.warmup)
+                else:
+                    c = W.MQ_CONFIGS[name](device="cuda", kv_dtype=kv)
+                    r = measure_multi_query(c, 0, args.steps, args.warmup)
+                mq[r["config"]["workload"]] = dict({k: r[k] for k in keep if k in r},
+                                                   metric=r["metric"], kv_dtype=kv)
+                del c
+                torch.cuda.empty_cache()
+        rec["multi_query_and_cascade"] = mq
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(rec), flush=True)
