@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -1535,13 +1536,23 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p,
       (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ wide_swz<kFp8>(prow)));
   constexpr int kStepLoads = 2 * kLoads;            // a wave's loads of one step
   constexpr int S = kWideStages;
-  auto issue = [&](int step, char* kst, char* vst) {
+  // The block ids of the next step to issue are read one step ahead of their
+  // use (scalar loads, waited for only where the addresses need them): read
+  // just before the loads, each id's latency sat between the barrier and the
+  // loads it releases.  An id past the segment's last step is clamped to its
+  // last block, so every read stays inside the segment's part of the table.
+  const unsigned nb32 = (unsigned)min(p.num_blocks, 0xFFFFFFFFll);
+  unsigned ids[kLoads];
+  auto load_ids = [&](int step) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l)
+      ids[l] = (unsigned)bt_s[min(2 * kNS * step + (wave + kMqWaves * l) * kR / kBS, nblk - 1)];
+  };
+  auto issue = [&](char* kst, char* vst) {
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
       const int piece = wave + kMqWaves * l;
-      const int b = min(2 * kNS * step + piece * kR / kBS, nblk - 1);
-      const unsigned raw = (unsigned)bt_s[b];
-      const long long off = (raw < (unsigned long long)p.num_blocks ? (long long)raw : 0) * block_bytes;
+      const long long off = (long long)(ids[l] < nb32 ? ids[l] : 0u) * block_bytes;
       __builtin_amdgcn_global_load_lds((GlobalVoid*)(kbytes + off + src_off),
                                        (LdsVoid*)(kst + piece * kWave * 16), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((GlobalVoid*)(vbytes + off + src_off),
@@ -1551,7 +1562,11 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p,
   wait_vmcnt<0>();                                  // the previous segment's stores
 #pragma unroll
   for (int k = 0; k < S - 1; ++k)
-    if (k < nstep) issue(k, stage[k][0], stage[k][1]);
+    if (k < nstep) {
+      load_ids(k);
+      issue(stage[k][0], stage[k][1]);
+    }
+  if (S - 1 < nstep) load_ids(S - 1);
   for (int cur = 0; cur < nstep; cur += S) {
 #pragma unroll
     for (int sl = 0; sl < S; ++sl) {
@@ -1568,13 +1583,245 @@ __device__ __forceinline__ void mq_wide_segment(const MqParams& p,
       // of the stage the next loads overwrite were consumed by its MFMAs of
       // step c - 1 before it got here.
       __builtin_amdgcn_s_barrier();
-      if (c + S - 1 < nstep) issue(c + S - 1, stage[(sl + S - 1) % S][0], stage[(sl + S - 1) % S][1]);
+      if (c + S - 1 < nstep) {
+        issue(stage[(sl + S - 1) % S][0], stage[(sl + S - 1) % S][1]);
+        load_ids(c + S);
+      }
       if (!idle) fold_step(c, stage[sl][0], stage[sl][1]);
     }
   }
   __syncthreads();                                  // the stages are free for the next segment
   if (!idle) wide_store<G, kFp8>(p, st, g, q0, nq, row0, lane, whole, slot);
 }
+
+// ---------------------------------------------------------------------------
+// fp16 wide fold, software-pipelined over 32-token sub-steps: the QK^T MFMAs
+// of sub-step t + 1 are issued between the exponentials of sub-step t, and
+// its p.V MFMAs follow, so that one wave's matrix and vector work overlap
+// (in wide_tail a sub-step's softmax waits for its own QK^T chain, and its
+// p.V for the softmax).  Same arithmetic per sub-step as wide_tail with one
+// sub-step at a time.
+
+// The lazy reference max check of a sub-step's scores (masked ones are -inf),
+// with the rescale when a score passes the reference.
+__device__ __forceinline__ void wide_pipe_check(WideSeg& st, const f32x16& sc, float qk_scale,
+                                                int lane) {
+  const int hf = lane >> 5;
+  float xl = sc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) xl = fmaxf(xl, sc[r]);
+  if (__ballot(xl * qk_scale > st.m + kLazyMax) != 0) {   // uniform branch
+    const float x = fmaxf(xl, __shfl_xor(xl, 32, kWave));
+    const float mn = fmaxf(st.m, x * qk_scale);           // qk_scale > 0: -inf stays -inf
+    const float a = mn == st.m ? 1.0f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.lp *= a;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float ar = __shfl(a, wide_row(r, hf), kWave);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st.acc[u][r] *= ar;
+    }
+  }
+}
+
+// p of the checked scores sc (masked ones -inf) with the QK^T MFMAs of the
+// next sub-step (K rows at knext) issued in between, then the p.V MFMAs; sc
+// becomes the next sub-step's scores.  The exponent's reference is kept
+// finite, so that with qk_scale > 0 a masked score gives exp2(-inf) = 0 even
+// in a row that has seen no token yet.
+__device__ __forceinline__ void wide_pipe_fold(WideSeg& st, f32x16& sc, const half8_t (&qb)[8],
+                                               const char* knext, const half8_t (&vb)[2][4],
+                                               float qk_scale, int lane) {
+  const int n = lane & 31, hf = lane >> 5;
+  f32x16 sn;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sn[r] = 0.0f;
+  const float m = fmaxf(st.m, -3.0e38f);
+  float ps[2];
+  half8_t pa[2];
+  // the next sub-step's K operands in two halves of 4 registers, each half's
+  // 4 MFMAs between the exponentials of 8 of this sub-step's rows
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    half8_t kop[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      kop[k] = *reinterpret_cast<const half8_t*>(knext + wide_at<false>(n, 8 * hf + 4 * h + k));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[k], qb[4 * h + k], sn, 0, 0, 0);
+      const int r = 8 * h + 2 * k;
+      const float p0 = fast_exp2(fmaf(sc[r], qk_scale, -m));
+      const float p1 = fast_exp2(fmaf(sc[r + 1], qk_scale, -m));
+      pa[h][2 * k] = static_cast<_Float16>(p0);
+      pa[h][2 * k + 1] = static_cast<_Float16>(p1);
+      ps[h] = k == 0 ? p0 + p1 : ps[h] + (p0 + p1);
+    }
+  }
+  st.lp += ps[0] + ps[1];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st.acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[c], vb[c][u], st.acc[u], 0, 0, 0);
+  sc = sn;
+}
+
+template <int G>
+__device__ __forceinline__ void mq_wide_segment_pipe(const MqParams& p,
+                                                     char* const (&stage)[kWideStages][2],
+                                                     int lane, int wave, int g, int i, int tok_lo,
+                                                     int tok_hi, bool whole, int slot) {
+  static_assert(kWideStages == 2 && wide_ns<false>() == 2, "pipelined fold: 2 stages of 2 sub-steps");
+  constexpr int E = 2;
+  constexpr int kRow = wide_row_bytes<false>();
+  constexpr int kNS = 2;
+  const int s = __builtin_amdgcn_readfirstlane(p.t_seq[i]);
+  // uniform per tile: scalar, so that the branches on them are scalar too
+  const int q0 = __builtin_amdgcn_readfirstlane(p.t_q0[i]);
+  const int nq = __builtin_amdgcn_readfirstlane(p.t_nq[i]);
+  const int base = __builtin_amdgcn_readfirstlane(p.t_base[i]);
+  tok_lo = __builtin_amdgcn_readfirstlane(tok_lo);
+  tok_hi = __builtin_amdgcn_readfirstlane(tok_hi);
+  const int n_seq = mq_seq_len(p, s);
+  const int row0 = wave * kWideRows;
+  const int hf = lane >> 5;
+  const bool idle = row0 / G >= nq;                 // none of the tile's queries (uniform)
+  half8_t qb[8];
+  wide_load_q<G>(p, g, q0, nq, row0, lane, qb);
+  const int causal_base = p.causal ? base : kNoMask;
+  const int full_end = p.causal ? min(min(max(base + row0 / G, 0), n_seq), tok_hi) : tok_hi;
+
+  const unsigned row_bytes = (unsigned)(p.Hkv * kD * E);
+  const char* kbytes = reinterpret_cast<const char*>(p.k);
+  const char* vbytes = reinterpret_cast<const char*>(p.v);
+  const int nblk = (tok_hi - tok_lo + kBS - 1) / kBS;
+  const int nstep = (nblk + 2 * kNS - 1) / (2 * kNS);
+  const int nsub = (tok_hi - tok_lo + 31) / 32;     // sub-steps holding tokens
+  ConstI32* bt_s = (ConstI32*)(p.bt + (long long)s * p.bt_stride + tok_lo / kBS);
+  const long long block_bytes = (long long)kBS * row_bytes;
+
+  WideSeg st;
+  st.m = -INFINITY;
+  st.lp = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.acc[u][r] = 0.0f;
+  unsigned voff[8];
+  wide_v_offsets<false>(lane, voff);
+
+  // staging as in mq_wide_segment (2 stages; the loads of step k go out
+  // after the barrier that opens step k - 1)
+  typedef __attribute__((address_space(3))) void LdsVoid;
+  typedef const __attribute__((address_space(1))) void GlobalVoid;
+  constexpr int kC = kRow / 16;
+  constexpr int kR = kWave / kC;
+  constexpr int kLoads = wide_step<false>() / kR / kMqWaves;
+  static_assert(kBS % kR == 0 && (wide_step<false>() / kR) % kMqWaves == 0 && (kMqWaves * kR) % kBS == 0,
+                "piece mapping");
+  const int prow = (wave * kR) % kBS + lane / kC;
+  const int trow = wide_prow<false>(prow);
+  const unsigned src_off =
+      (unsigned)((trow * p.Hkv + g) * kD * E + 16 * ((lane % kC) ^ wide_swz<false>(prow)));
+  const unsigned nb32 = (unsigned)min(p.num_blocks, 0xFFFFFFFFll);
+  unsigned ids[kLoads];
+  auto load_ids = [&](int step) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l)
+      ids[l] = (unsigned)bt_s[min(2 * kNS * step + (wave + kMqWaves * l) * kR / kBS, nblk - 1)];
+  };
+  auto issue = [&](char* kst, char* vst) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int piece = wave + kMqWaves * l;
+      const long long off = (long long)(ids[l] < nb32 ? ids[l] : 0u) * block_bytes;
+      __builtin_amdgcn_global_load_lds((GlobalVoid*)(kbytes + off + src_off),
+                                       (LdsVoid*)(kst + piece * kWave * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((GlobalVoid*)(vbytes + off + src_off),
+                                       (LdsVoid*)(vst + piece * kWave * 16), 16, 0, 0);
+    }
+  };
+
+  wait_vmcnt<0>();                                  // the previous segment's stores
+  if (nstep > 0) {
+    load_ids(0);
+    issue(stage[0][0], stage[0][1]);
+  }
+  if (nstep > 1) load_ids(1);
+  __syncthreads();                                  // step 0's rows are in
+  if (nstep > 1) {
+    issue(stage[1][0], stage[1][1]);
+    load_ids(2);
+  }
+  f32x16 sc;
+  if (!idle && nsub > 0) sc = wide_qk<false>(qb, stage[0][0], lane);
+  half8_t vb[2][4];
+  for (int cur = 0; cur < nstep; cur += 2) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int c = cur + sl;
+      if (c >= nstep) break;
+      char* const kcur = stage[sl][0];
+      char* const vcur = stage[sl][1];
+      const char* knxt = stage[sl ^ 1][0];
+      // sub-step t: its mask and max check, then its V operands (registers)
+      auto prepare = [&](int t, const char* vsub) {
+        const int t0 = tok_lo + 32 * t;
+        if (t0 + 32 > full_end) {                   // causal diagonal or segment end
+          const int qi = (row0 + (lane & 31)) / G;
+          int e = tok_hi;
+          if (qi < nq && causal_base != kNoMask) e = min(min(max(causal_base + qi, 0), n_seq), tok_hi);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[r] = t0 + wide_row(r, hf) < e ? sc[r] : -INFINITY;
+        }
+        wide_pipe_check(st, sc, p.qk_scale, lane);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) wide_v_operands<false, false>(vsub, voff, cc, hf, 0, vb[cc]);
+        if (t0 + 32 > tok_hi) {                     // rows past the segment: exact zeros
+          const int valid = tok_hi - t0;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)     // element 4r + e: token 16cc + 8r + 4hf + e
+                  if (16 * cc + 8 * r + 4 * hf + e >= valid) vb[cc][u][4 * r + e] = static_cast<_Float16>(0.0f);
+        }
+      };
+      const bool work0 = !idle;                     // sub-step 2c holds tokens (c < nstep)
+      const bool work1 = !idle && kNS * c + 1 < nsub;
+      if (work0) {
+        prepare(kNS * c, vcur);
+        wide_pipe_fold(st, sc, qb, kcur + 32 * kRow, vb, p.qk_scale, lane);
+      }
+      if (work1) prepare(kNS * c + 1, vcur + 32 * kRow);
+      // the next step's rows are in once every wave's loads of it are (the
+      // fenced barrier waits for this wave's loads and LDS reads); this
+      // stage's reads have then returned, so the loads of step c + 2 may
+      // refill it.  A fence the compiler models, on every step: with a bare
+      // barrier and a wait of our own it still waited for the loads in
+      // flight before later reads of the other stage.
+      __syncthreads();
+      if (c + 2 < nstep) {
+        issue(kcur, vcur);
+        load_ids(c + 3);
+      }
+      // the next sub-step's K rows come from the next stage; past the
+      // segment's last sub-step they are stale rows, read and then unused
+      if (work1) wide_pipe_fold(st, sc, qb, knxt, vb, p.qk_scale, lane);
+    }
+  }
+  __syncthreads();                                  // the stages are free for the next segment
+  if (!idle) wide_store<G, false>(p, st, g, q0, nq, row0, lane, whole, slot);
+}
+
+#ifndef PDA_WIDE_PIPE
+#define PDA_WIDE_PIPE 1               // fp16: the software-pipelined fold
+#endif
 
 template <int G, bool kFp8>
 __global__ __launch_bounds__(kWave * kMqWaves) __attribute__((amdgpu_waves_per_eu(2)))
@@ -1602,7 +1849,10 @@ void mq_wide_kernel(MqParams p) {
   const int g = blockIdx.x % p.Hkv;                 // KV head
   for_each_segment<PDA_WIDE_REVERSE != 0>(p, w, [&](int i, int tok_lo, int tok_hi, bool whole,
                                                      int slot) {
-    mq_wide_segment<G, kFp8>(p, stage, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+    if constexpr (!kFp8 && PDA_WIDE_PIPE != 0)
+      mq_wide_segment_pipe<G>(p, stage, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
+    else
+      mq_wide_segment<G, kFp8>(p, stage, lane, wave, g, i, tok_lo, tok_hi, whole, slot);
   });
 }
 
@@ -2005,7 +2255,9 @@ int run_multi_query(bool out_f16, void* out, float* lse_out, const void* q,
   mp.hg = pl.hg;
   mp.causal = causal ? 1 : 0;
   const float score_scale = scale * k_scale;      // k = k_scale * decoded code for FP8
-  mp.qk_scale = std::fabs(score_scale) * kLog2e;
+  // at least the least normal float: the kernels take exp2 of -inf * qk_scale
+  // as 0 (a masked score); for scale 0 the softmax stays uniform
+  mp.qk_scale = std::max(std::fabs(score_scale) * kLog2e, FLT_MIN);
   mp.q_sign = std::signbit(score_scale) ? 0x80008000u : 0u;
   mp.v_scale = v_scale;
   mp.hdr = reinterpret_cast<int32_t*>(ws + pl.hdr_offset);
