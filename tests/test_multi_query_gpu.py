@@ -282,6 +282,25 @@ def test_scale_sign_and_zero():
         compare_lse(to_np(lse), ref_lse)
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_scale_sign_and_zero(kv_dtype, causal):
+    # 60 queries x G = 4 = 240 rows per sequence: the wide tile kernel, whose fold
+    # takes exp2 of a masked (-inf) score times the kernels' score scale as 0.
+    # Scale 0 gives the uniform softmax over each query's visible tokens, a
+    # negative scale flips every score; P = 48 also cuts tiles between runs.
+    case = W.build_mq_case([300, 70, 1100], [60, 60, 60], 8, 2, causal=causal, seed=47,
+                           device="cuda", name=f"mq_wide_scale_{kv_dtype}", kv_dtype=kv_dtype)
+    q, k, v, table, lens, qs = host_mq(case)
+    for scale in (-0.2, 0.0):
+        case.scale = scale
+        ref, ref_lse = MQ.multi_query_attention(q, k, v, table, lens, qs, scale, causal=causal)
+        for P in (0, 48):
+            out, lse = run_mq(case, P)
+            compare_out(to_np(out), ref)
+            compare_lse(to_np(lse), ref_lse)
+
+
 def test_graph_capture_replays_match_eager():
     case = W.build_mq_case(SMALL_LENS, SMALL_NQ, 32, 8, causal=True, seed=46, device="cuda",
                            name="mq_graph")
