@@ -1100,6 +1100,13 @@ constexpr int wide_step() { return 2 * kBS * wide_ns<kFp8>(); }   // tokens per 
 //    chunk swizzle to be a bijection over the row slots of either parity.
 template <bool kFp8>
 constexpr int wide_row_bytes() { return kD * KvFmt<kFp8>::kElemBytes; }
+// FP8 V operands by transposed byte reads (ds_read_b64_tr_b8), tile u at
+// dims 32u + n as over fp16; else by whole-row dword reads and a byte
+// transpose in registers, tile u at dims 4n + u
+#ifndef PDA_WIDE_FP8_TR
+#define PDA_WIDE_FP8_TR 1
+#endif
+constexpr bool kWideFp8Tr = PDA_WIDE_FP8_TR != 0;
 template <bool kFp8>
 __device__ __forceinline__ int wide_prow(int t) {       // an involution
   if constexpr (kFp8) return t ^ ((t >> 2) & 1);
@@ -1107,7 +1114,11 @@ __device__ __forceinline__ int wide_prow(int t) {       // an involution
 }
 template <bool kFp8>
 __device__ __forceinline__ int wide_swz(int pr) {
-  if constexpr (kFp8) return (pr >> 1) & 7;
+  if constexpr (kFp8) {
+    const int i = (pr >> 1) & 7;
+    if constexpr (kWideFp8Tr) return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1);
+    return i;
+  }
   return ((pr & 3) << 2) | ((pr >> 2) & 3);
 }
 template <bool kFp8>
@@ -1164,7 +1175,20 @@ __device__ __forceinline__ void wide_load_q(const MqParams& p, int g, int q0, in
 template <bool kFp8>
 __device__ __forceinline__ void wide_v_offsets(int lane, unsigned (&voff)[8]) {
   const int n = lane & 31, hf = lane >> 5;
-  if constexpr (kFp8) {
+  if constexpr (kFp8 && kWideFp8Tr) {
+    // entry u: the 8-byte piece this lane addresses for tile u's transposed
+    // read; in each 16-lane group lane 16q + 8h + e receives, as byte k, byte
+    // e of the piece lane 16q + h + 2k addresses (probed on the device), so
+    // lane 16q + a addresses dims 32u + 16(q & 1) + 8(a & 1) .. +7 of the
+    // token that byte a / 2 of the P operand stands for
+    const int q = lane >> 4, a = lane & 15, k = a >> 1;
+    const int t = 8 * (k >> 2) + 4 * (q >> 1) + (k & 3);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      voff[u] = (unsigned)(wide_at<true>(t, 2 * u + (q & 1)) + 8 * (a & 1));
+      voff[u + 4] = voff[u];
+    }
+  } else if constexpr (kFp8) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -1192,7 +1216,30 @@ __device__ __forceinline__ void wide_v_operands(const char* vstage, const unsign
                                                 int c, int hf, int valid, half8_t (&vb)[4]) {
   constexpr int kRow = wide_row_bytes<kFp8>();
   const char* vc = vstage + 16 * c * kRow;
-  if constexpr (kFp8) {
+  if constexpr (kFp8 && kWideFp8Tr) {
+    // byte k of a lane's read is token 16c + 8(k / 4) + 4hf + k % 4 of dim
+    // 32u + n: the P operand's order.  Bytes of tokens at or past `valid`
+    // become code 0 (+0).
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i LdsV2i;
+    unsigned m0 = ~0u, m1 = ~0u;
+    if (kMasked) {
+      auto keep = [](int nb) { return nb >= 4 ? ~0u : nb <= 0 ? 0u : (1u << (8 * nb)) - 1u; };
+      const int r0 = valid - 16 * c - 4 * hf;      // bytes 0..3: tokens 16c + 4hf + 0..3
+      m0 = keep(r0);
+      m1 = keep(r0 - 8);                           // bytes 4..7: 8 tokens later
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LdsV2i*)(vc + voff[u]));
+      const unsigned w0 = (unsigned)x[0] & m0, w1 = (unsigned)x[1] & m1;
+      const half2_t a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+      const half2_t a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+      const half2_t b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+      const half2_t b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+      vb[u] = half8_t{a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    }
+  } else if constexpr (kFp8) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       unsigned w[4];
@@ -1407,7 +1454,7 @@ __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g
     const f32x4 o = {st.acc[0][r] * inv, st.acc[1][r] * inv, st.acc[2][r] * inv,
                      st.acc[3][r] * inv};
     const int h = g * G + j;
-    if constexpr (!kFp8) {
+    if constexpr (!kFp8 || kWideFp8Tr) {          // tile u at dims 32u + n
       if (whole) {
         const long long dst = ((long long)(q0 + qi) * p.Hq + h) * kD + n;
 #pragma unroll
