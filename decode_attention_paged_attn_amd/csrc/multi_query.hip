@@ -1050,8 +1050,8 @@ void mq_shared_kernel(MqParams p) {
 //     token chunk c, whose contraction index 8hf + t maps to token
 //     16c + 8(t >> 2) + 4hf + (t & 3); B = V at those tokens.  Output tile u
 //     holds, in register r of lane l, row 8(r >> 2) + 4hf + (r & 3) at head dim
-//     4n + u, so lane l reads V's dims 4n .. 4n+3 (8 bytes fp16, 4 FP8) of its
-//     8 tokens and builds the operand of tile u from element u of each.
+//     32u + n: the transposed LDS reads (16-bit elements over fp16, bytes over
+//     FP8) hand lane l its 8 tokens of that dim (see wide_v_operands).
 
 constexpr int kWideRows = 32;         // query rows per wave
 // 32-token sub-steps per staged step (one barrier per step): four over FP8
@@ -1094,10 +1094,15 @@ constexpr int wide_step() { return 2 * kBS * wide_ns<kFp8>(); }   // tokens per 
 //    consecutive rows): the swizzle's bits 2-3 take 4 values over the 4 rows
 //    (swapping the row's 2-bit halves does both; row ^ chunk put the 4 rows on
 //    the same banks: chunked prefill 0.699 -> 0.672 ms);
-//  - FP8 V (ds_read_b32, 64 lanes: whole rows t and t + 4) needs the two rows
-//    in different 128-byte halves of the banks, so rows 4..7 of each 8 trade
-//    places in pairs; FP8 K (16 lanes: one chunk of 16 rows) then needs the
-//    chunk swizzle to be a bijection over the row slots of either parity.
+//  - FP8 K (16 lanes: one chunk of 16 rows): the swizzle is a bijection over
+//    the 8 row slots of either parity (bits 1-3 of the slot, bits 0 and 1 of
+//    that swapped);
+//  - FP8 V (ds_read_b64_tr_b8, 32 lanes: chunks 2u, 2u + 1 of tokens 4hf + 0..3
+//    and 8 + 4hf + 0..3 of a 16-token chunk): the swizzle's bits 1-2 differ
+//    over the 4 row slots of either parity among them.
+//    Rows 4..7 of each 8 trade places in pairs over FP8 (a layout made for
+//    whole-row dword reads of V; the transposed reads find distinct banks with
+//    it too).
 template <bool kFp8>
 constexpr int wide_row_bytes() { return kD * KvFmt<kFp8>::kElemBytes; }
 // FP8 V operands by transposed byte reads (ds_read_b64_tr_b8), tile u at
@@ -1167,11 +1172,12 @@ __device__ __forceinline__ void wide_load_q(const MqParams& p, int g, int q0, in
 // Per-lane byte offsets, within a stage and for token chunk c = 0, of the V
 // reads of wide_v_operands (chunk c adds 16 rows, a constant: the row swizzle
 // depends on a row's low 4 bits only).  fp16: entry 2u + r is the 8-byte
-// transposed-read piece of tile u, token row 8r + 4hf + b; FP8: entry 4jj + i
-// is the 4 bytes (dims 4n .. 4n+3) of token row 8jj + 4hf + i.  Computed once
-// per segment and kept opaque, so that every read is one of these registers
-// plus an immediate offset (the stage, the sub-step and c), with no address
-// arithmetic in the token loop.
+// transposed-read piece of tile u, token row 8r + 4hf + b; FP8 by transposed
+// byte reads: entry u (repeated at u + 4) is the 8-byte piece of tile u; FP8
+// by dword reads: entry 4jj + i is the 4 bytes (dims 4n .. 4n+3) of token row
+// 8jj + 4hf + i.  Computed once per segment and kept opaque, so that every
+// read is one of these registers plus an immediate offset (the stage, the
+// sub-step and c), with no address arithmetic in the token loop.
 template <bool kFp8>
 __device__ __forceinline__ void wide_v_offsets(int lane, unsigned (&voff)[8]) {
   const int n = lane & 31, hf = lane >> 5;
@@ -1428,8 +1434,9 @@ __device__ __forceinline__ void wide_tail(WideSeg& st, const f32x16 (&sc)[kNS],
 }
 
 // Normalise and store the wave's rows: register r of lane l holds row
-// row0 + wide_row(r, hf) at head dims 4n .. 4n+3 (tiles 0..3) over an FP8
-// cache, and at dims n, 32 + n, 64 + n, 96 + n over an fp16 one.
+// row0 + wide_row(r, hf) at head dims n, 32 + n, 64 + n, 96 + n (tiles 0..3),
+// or over an FP8 cache read without the transposed byte reads, at dims
+// 4n .. 4n+3.
 template <int G, bool kFp8>
 __device__ __forceinline__ void wide_store(const MqParams& p, WideSeg& st, int g, int q0, int nq,
                                            int row0, int lane, bool whole, int slot) {
