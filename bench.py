@@ -383,6 +383,32 @@ def stream_read_ceiling(gib=4, steps=10):
     return res
 
 
+LDS_PROBE_FORMS = (("ds_read_b128", 1024), ("ds_read_b64", 512), ("ds_read_b64_tr_b16", 512),
+                   ("ds_read_b32", 256))
+
+
+def bench_lds_probe(steps, iters=4096):
+    """The LDS read forms of the multi-query kernels (pda_lds_probe), one at a
+    time: two 256-thread work-groups per CU (their 64 KiB stages fill 128 of the
+    CU's 160 KiB), ``iters`` passes of 16 reads per wave; mean kernel time by
+    events, and per CU the time and bytes of one wave-wide read."""
+    import torch
+    import decode_attention_paged_attn_amd as pda
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs_per_cu = 2
+    out = torch.empty(wgs_per_cu * cus * 256, dtype=torch.int32, device="cuda")
+    reads_per_cu = wgs_per_cu * 4 * iters * 16            # 4 waves per work-group
+    forms = {}
+    for form, (name, nbytes) in enumerate(LDS_PROBE_FORMS):
+        _, ev_ms, _ = _time_events(lambda: pda.lds_probe(form, out, iters), steps, 2)
+        ns = ev_ms * 1e6 / reads_per_cu
+        forms[name] = {"form": form, "ms": round(ev_ms, 4), "ns_per_wave_read_per_cu": round(ns, 4),
+                       "bytes_per_ns_per_cu": round(nbytes / ns, 1)}
+    print(json.dumps({"op": "lds_probe", "work_groups": wgs_per_cu * cus, "iters": iters,
+                      "reads_per_wave": iters * 16, "steps": steps, "forms": forms,
+                      "device": platform_info()}), flush=True)
+
+
 def mq_work(case):
     """(unique K/V bytes, algorithmic FLOPs) of one multi-query call.
 
@@ -656,12 +682,14 @@ def main():
                     help="also time the headline with this many MiB of scratch read before "
                          "each call (event-timed; 0: skip)")
     ap.add_argument("--op", default="attention",
-                    choices=["attention", "append", "multi_query", "cascade", "partial_merge"],
+                    choices=["attention", "append", "multi_query", "cascade", "partial_merge",
+                             "lds_probe"],
                     help="attention (default): paged_decode_attn; append: paged_kv_append of "
                          "one token per sequence; multi_query: paged_multi_query_attn on "
                          "--config spec_verify or chunked_prefill; cascade: "
                          "cascade_decode_attn on --config shared_prefix; partial_merge: 4 range "
-                         "partials + merge_partials on disagg_merge, against single pass")
+                         "partials + merge_partials on disagg_merge, against single pass; "
+                         "lds_probe: the LDS read forms of the multi-query kernels, timed alone")
     ap.add_argument("--no-mq", action="store_true",
                     help="skip the multi-query (speculative verification, chunked prefill) "
                          "and cascade records of the default run")
@@ -693,6 +721,9 @@ def main():
         copy_calibration(args.copy_calibration, args.steps)
         return
     pda.load_library()
+    if args.op == "lds_probe":
+        bench_lds_probe(args.steps)
+        return
     if args.op == "multi_query":
         name = args.config if args.config in W.MQ_CONFIGS else "spec_verify"
         case = W.MQ_CONFIGS[name](device="cuda", kv_dtype=args.kv_dtype)

@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     PdaError,
     cascade_decode_attn,
     decode_workspace_size,
+    lds_probe,
     library_path,
     load_library,
     merge_partials,
@@ -29,6 +30,7 @@ __all__ = [
     "PdaError",
     "cascade_decode_attn",
     "decode_workspace_size",
+    "lds_probe",
     "library_path",
     "load_library",
     "merge_partials",

@@ -89,6 +89,7 @@ _SIGNATURES = {
                                               _c_int, _c_float, _c_float, _c_float, _c_int, _vp,
                                               _vp, _c_size, _vp]),
     "pda_stream_read": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
+    "pda_lds_probe": (_c_int, [_c_int, _vp, _c_int, _c_int, _vp]),
     "pda_last_error": (ctypes.c_char_p, []),
     "pda_version": (ctypes.c_char_p, []),
 }
@@ -344,6 +345,19 @@ def stream_read(buf, sink, nontemporal=True):
     _check(load_library().pda_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
                                           _ptr(sink), int(bool(nontemporal)),
                                           _stream(buf.device)))
+
+
+def lds_probe(form, out, iters):
+    """Diagnostic: enqueue ``out.numel() // 256`` work-groups of the LDS read
+    probe of ``form`` (0 ds_read_b128, 1 ds_read_b64, 2 ds_read_b64_tr_b16,
+    3 ds_read_b32) for ``iters`` passes; ``out`` is a contiguous int32 GPU
+    tensor of 256 per work-group, filled with each thread's sum."""
+    if out.device.type != "cuda" or not out.is_contiguous() or out.element_size() != 4:
+        raise ValueError("out must be a contiguous 4-byte GPU tensor")
+    if out.numel() % 256:
+        raise ValueError("out holds 256 values per work-group")
+    _check(load_library().pda_lds_probe(int(form), _ptr(out), out.numel() // 256, int(iters),
+                                        _stream(out.device)))
 
 
 def merge_partials(o_parts, lse_parts, out=None, lse_out=None, return_lse=True):

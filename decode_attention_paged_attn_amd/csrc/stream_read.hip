@@ -8,6 +8,13 @@
 // folds them into an xor.  The result is
 // stored only if it equals a value the buffer would have to be built for, so
 // in practice nothing is written, while the loads cannot be dropped.
+//
+// A second diagnostic times the LDS read forms of the multi-query kernels
+// (ds_read_b128, ds_read_b64, ds_read_b64_tr_b16, ds_read_b32): every wave of
+// a 256-thread work-group reads a 64 KiB stage over and over with
+// conflict-free addresses and sums what it gets, so that the SQ_LDS_IDX_ACTIVE
+// count of those kernels can be set against what each form costs and against
+// a kernel that does nothing else.
 
 #include <hip/hip_runtime.h>
 
@@ -48,6 +55,54 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* 
   if (acc == kNeverXor) sink[0] = acc;
 }
 
+constexpr int kLdsProbeThreads = 256;
+constexpr int kLdsProbeWords = 16384;          // 64 KiB of stage
+constexpr int kLdsProbeReads = 16;             // reads per wave and pass
+
+// Word i of the stage, the pattern the host recomputes to check the sums.
+__device__ __forceinline__ unsigned lds_probe_word(int i) { return (unsigned)i * 2654435761u; }
+
+// Form 0: ds_read_b128 (1 KiB per wave-wide read), 1: ds_read_b64 (512 B),
+// 2: ds_read_b64_tr_b16 (512 B), 3: ds_read_b32 (256 B).  Read r of a pass
+// covers a contiguous window of the stage at r times its size, lane l at l
+// times the lane's share: no bank conflicts.  Thread t of work-group b stores
+// the wrapping sum of the 32-bit words it received at out[256 b + t].
+template <int kForm>
+__global__ __launch_bounds__(kLdsProbeThreads) void lds_probe_kernel(unsigned* out, int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned stage[kLdsProbeWords];
+  typedef __attribute__((address_space(3))) char LdsChar;
+  typedef __fp16 fp16x4 __attribute__((vector_size(8)));      // the builtin's element type
+  typedef __attribute__((address_space(3))) fp16x4 LdsHalf4;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  for (int i = tid; i < kLdsProbeWords; i += kLdsProbeThreads) stage[i] = lds_probe_word(i);
+  __syncthreads();
+  const LdsChar* base = (const LdsChar*)stage;
+  unsigned acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < kLdsProbeReads; ++r) {
+      constexpr int kBytes = kForm == 0 ? 16 : kForm == 3 ? 4 : 8;
+      unsigned a = (unsigned)(r * kWave * kBytes + kBytes * lane);
+      // opaque per read: no hoisting out of the pass, no pairing into read2
+      asm volatile("" : "+v"(a));
+      if constexpr (kForm == 0) {
+        const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(base + a);
+        acc += (x.x + x.y) + (x.z + x.w);
+      } else if constexpr (kForm == 1) {
+        const u32x2 x = *(const __attribute__((address_space(3))) u32x2*)(base + a);
+        acc += x.x + x.y;
+      } else if constexpr (kForm == 2) {
+        const u32x2 x =
+            __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LdsHalf4*)(base + a)));
+        acc += x.x + x.y;
+      } else {
+        acc += *(const __attribute__((address_space(3))) unsigned*)(base + a);
+      }
+    }
+  }
+  out[(long long)blockIdx.x * kLdsProbeThreads + tid] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +134,24 @@ int pda_stream_read(const void* src, size_t bytes, unsigned* sink, int nontempor
                        n16, sink);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pda::fail(PDA_EHIP, "stream read launch: %s", hipGetErrorString(e));
+  return pda::ok();
+}
+
+int pda_lds_probe(int form, unsigned* out, int work_groups, int iters, void* stream_ptr) {
+  if (form < 0 || form > 3) return pda::fail(PDA_EINVAL, "form must be 0..3");
+  if (work_groups < 0 || iters < 0) return pda::fail(PDA_EINVAL, "negative size");
+  if (work_groups == 0) return pda::ok();
+  if (!out) return pda::fail(PDA_EINVAL, "out must not be null");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const dim3 grid((unsigned)work_groups), block(kLdsProbeThreads);
+  switch (form) {
+    case 0: hipLaunchKernelGGL(lds_probe_kernel<0>, grid, block, 0, stream, out, iters); break;
+    case 1: hipLaunchKernelGGL(lds_probe_kernel<1>, grid, block, 0, stream, out, iters); break;
+    case 2: hipLaunchKernelGGL(lds_probe_kernel<2>, grid, block, 0, stream, out, iters); break;
+    default: hipLaunchKernelGGL(lds_probe_kernel<3>, grid, block, 0, stream, out, iters); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pda::fail(PDA_EHIP, "LDS probe launch: %s", hipGetErrorString(e));
   return pda::ok();
 }
 

@@ -466,6 +466,23 @@ int paged_multi_query_attn_partial_fp8(float* o, float* lse, const void* q,
 int pda_stream_read(const void* src, size_t bytes, unsigned* sink, int nontemporal,
                     void* stream);
 
+/*
+ * Diagnostic, no part of the attention path: times one LDS read form of the
+ * multi-query kernels, form 0 = ds_read_b128, 1 = ds_read_b64, 2 =
+ * ds_read_b64_tr_b16, 3 = ds_read_b32.  Launches `work_groups` work-groups of
+ * 256 threads on `stream`; each fills a 64 KiB LDS stage with word i =
+ * i * 2654435761 (mod 2^32), then each wave issues 16 conflict-free reads of
+ * the form per pass, `iters` passes (read r covers bytes [r S, (r + 1) S) of
+ * the stage, S = 64 lanes times the form's width, lane l at l times the
+ * width), and thread t of work-group b writes the wrapping 32-bit sum of the
+ * words it received to out[256 b + t] (out: device memory of 256 x
+ * work_groups unsigned).  With a profiler's SQ_LDS_IDX_ACTIVE count it gives
+ * that counter's cost per instruction of each form and the count per clock
+ * of a kernel bound by nothing else.  Returns PDA_EINVAL for a form outside
+ * 0..3, negative sizes or a null `out` when work_groups > 0.
+ */
+int pda_lds_probe(int form, unsigned* out, int work_groups, int iters, void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pda_last_error(void);
 

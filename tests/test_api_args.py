@@ -341,3 +341,14 @@ def test_stream_read_rejects(lib):
     assert lib.pda_stream_read(vp(256), 60, vp(256), 0, None) == 1     # size not a multiple of 16
     assert b"16" in lib.pda_last_error()
     assert lib.pda_stream_read(None, 0, None, 1, None) == 0           # nothing to read
+
+
+def test_lds_probe_rejects(lib):
+    vp = ctypes.c_void_p
+    assert lib.pda_lds_probe(4, vp(256), 1, 1, None) == 1              # no such form
+    assert lib.pda_lds_probe(-1, vp(256), 1, 1, None) == 1
+    assert lib.pda_lds_probe(0, vp(256), -1, 1, None) == 1             # negative sizes
+    assert lib.pda_lds_probe(0, vp(256), 1, -1, None) == 1
+    assert lib.pda_lds_probe(0, None, 1, 1, None) == 1                 # null out
+    assert b"null" in lib.pda_last_error()
+    assert lib.pda_lds_probe(3, None, 0, 1, None) == 0                 # nothing to launch

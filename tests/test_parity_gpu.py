@@ -690,6 +690,48 @@ def test_stream_read_reads_without_writing(nbytes):
     assert int(sink.item()) == -5
 
 
+def _lds_probe_sums(form, iters):
+    """Host model of pda_lds_probe: the wrapping sum each lane of a wave gets.
+
+    Stage word i is i * 2654435761 mod 2^32; read r of a pass covers 64 lane
+    shares of the form's width from r times 64 shares.  The transposed form
+    (ds_read_b64_tr_b16) hands lane 4a + e of each 16-lane group, as its
+    16-bit element b, element e of the 8-byte piece addressed by lane a + 4b of
+    the group."""
+    words = (np.arange(16384, dtype=np.uint64) * 2654435761) & 0xFFFFFFFF
+    width = {0: 16, 1: 8, 2: 8, 3: 4}[form]
+    sums = np.zeros(64, dtype=np.uint64)
+    for r in range(16):
+        for lane in range(64):
+            if form == 2:
+                grp, a, e = lane // 16 * 16, (lane % 16) // 4, lane % 4
+                h = []
+                for b in range(4):
+                    addr = r * 64 * 8 + 8 * (grp + a + 4 * b) + 2 * e
+                    h.append((int(words[addr // 4]) >> (16 * ((addr % 4) // 2))) & 0xFFFF)
+                got = (h[0] | h[1] << 16) + (h[2] | h[3] << 16)
+            else:
+                first = (r * 64 * width + width * lane) // 4
+                got = int(words[first:first + width // 4].sum())
+            sums[lane] += got
+    return (sums * iters) & 0xFFFFFFFF
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("form", [0, 1, 2, 3])
+def test_lds_probe_sums_what_each_form_reads(form):
+    """The LDS read probe (the bench's calibration of the LDS counter) reads
+    what its description says: every thread's sum matches the host model, for
+    each of the 4 waves of each work-group."""
+    iters, wgs = 3, 5
+    out = torch.full((wgs * 256,), -1, dtype=torch.int32, device="cuda")
+    pda.lds_probe(form, out, iters)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    want = np.tile(_lds_probe_sums(form, iters).astype(np.int64), 4 * wgs)
+    np.testing.assert_array_equal(got, want)
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("G", [1, 2, 4, 6, 8])
